@@ -1,0 +1,123 @@
+"""Trellis format: MCG16 codebook and 16x16 tail-biting tiles (oracle side).
+
+The pages say expert weights are trellis bitstreams at K bits per weight,
+with K per expert (TensorFold #837, "What this changes"; sparkinfer #99,
+Description) and that residual stages use an "MCG" codebook (exllamav3 #284,
+API contract), but they define neither the codebook nor the bit layout. This
+library fixes its own format, restated here so the oracle can be read alone:
+
+  codebook   h = (s * 0x9E37) mod 2**16 ; a = h >> 6 ; b = h mod 2**10 ;
+             CB(s) = (a - b) / 1024, an exact fp16 value in [-1008, 1008]/1024
+  tile       16 (input k) x 16 (output n) weights, a stream of 256*K bits
+             stored as 16*K little-endian uint16 words; stream bit j is bit
+             (j mod 16) of word j // 16
+  state      s_i = sum_t bit((i*K + K - 16 + t) mod 256K) << t, t = 0..15:
+             the 16 stream bits ending at bit i*K + K - 1, wrapping around
+             (tail-biting: the state before weight 0 is the last 16 bits)
+  position   weight i of a tile is W[k = i mod 16][n = i // 16]
+  tensor     uint16 [out/16][in/16][16*K]; tile (kt, nt) starts at word
+             (nt * (in/16) + kt) * 16*K
+
+Two decoders are given on purpose: ``decode_tiles_window`` reads each state
+straight from its 16-bit window; ``decode_tiles_shift`` runs the shift
+register s_i = (s_{i-1} >> K) | (next K bits << (16 - K)). They share nothing
+but the codebook.
+"""
+
+import numpy as np
+
+MCG_MULT = 0x9E37
+TILE = 16
+STATE_BITS = 16
+
+
+def codebook(states):
+    """MCG16 codebook value of 16-bit trellis states, as float64.
+
+    Written from the integer definition above (not from any fp16 bit trick).
+    """
+    s = np.asarray(states, dtype=np.int64) & 0xFFFF
+    h = (s * MCG_MULT) & 0xFFFF
+    a = h >> 6
+    b = h & 0x3FF
+    return (a - b).astype(np.float64) / 1024.0
+
+
+def _stream_bits(words):
+    """[T, 16K] uint16 words -> [T, 256K] uint8 bits, LSB first."""
+    w = np.ascontiguousarray(np.asarray(words, dtype=np.uint16))
+    t = w.shape[0]
+    by = w.astype("<u2").view(np.uint8).reshape(t, -1)
+    return np.unpackbits(by, axis=1, bitorder="little")
+
+
+def tile_states_window(words, K):
+    """States s_0..s_255 of each tile, read from their 16-bit windows.
+
+    ``words``: [T, 16*K] uint16. Returns [T, 256] int64.
+    """
+    bits = _stream_bits(words).astype(np.int64)
+    L = 256 * K
+    i = np.arange(256)[:, None]
+    t = np.arange(STATE_BITS)[None, :]
+    pos = (i * K + K - STATE_BITS + t) % L          # [256, 16]
+    return (bits[:, pos] << t[None]).sum(axis=2)
+
+
+def tile_states_shift(words, K):
+    """States s_0..s_255 of each tile, produced by the shift register.
+
+    s_{-1} is the last 16 stream bits (tail-biting); each step shifts the
+    register right by K and inserts the next K stream bits at the top.
+    """
+    bits = _stream_bits(words).astype(np.int64)
+    T = bits.shape[0]
+    L = 256 * K
+    state = np.zeros(T, dtype=np.int64)
+    for t in range(STATE_BITS):
+        state |= bits[:, L - STATE_BITS + t] << t
+    out = np.empty((T, 256), dtype=np.int64)
+    for i in range(256):
+        new = np.zeros(T, dtype=np.int64)
+        for u in range(K):
+            new |= bits[:, i * K + u] << u
+        state = (state >> K) | (new << (STATE_BITS - K))
+        out[:, i] = state
+    return out
+
+
+def decode_tiles_window(words, K):
+    """[T, 16K] uint16 -> [T, 16(k), 16(n)] float64 via the window decoder."""
+    v = codebook(tile_states_window(words, K))
+    return v.reshape(-1, TILE, TILE).transpose(0, 2, 1)  # i = 16n + k
+
+
+def decode_tiles_shift(words, K):
+    """[T, 16K] uint16 -> [T, 16(k), 16(n)] float64 via the shift register."""
+    v = codebook(tile_states_shift(words, K))
+    out = np.empty((v.shape[0], TILE, TILE))
+    for i in range(256):
+        out[:, i % TILE, i // TILE] = v[:, i]
+    return out
+
+
+def tensor_words(in_features, out_features, K):
+    """Number of uint16 words of one (in x out) trellis tensor at K bits."""
+    return (in_features // TILE) * (out_features // TILE) * TILE * K
+
+
+def dequantize(words, in_features, out_features, K, decoder="window",
+               chunk_tiles=8192):
+    """Dense W [in][out] (float64) of one trellis tensor.
+
+    ``words`` is the flat uint16 tensor in [out/16][in/16][16K] order.
+    """
+    kt_n, nt_n = in_features // TILE, out_features // TILE
+    w = np.asarray(words, dtype=np.uint16).reshape(nt_n * kt_n, TILE * K)
+    dec = decode_tiles_window if decoder == "window" else decode_tiles_shift
+    tiles = np.empty((nt_n * kt_n, TILE, TILE))
+    for c0 in range(0, w.shape[0], chunk_tiles):
+        tiles[c0:c0 + chunk_tiles] = dec(w[c0:c0 + chunk_tiles], K)
+    # tiles[nt * kt_n + kt][k][n] -> W[16 kt + k][16 nt + n]
+    t = tiles.reshape(nt_n, kt_n, TILE, TILE)
+    return t.transpose(1, 2, 0, 3).reshape(in_features, out_features)
