@@ -29,7 +29,7 @@ def stage_sum(proj, e):
         if s != 0.0:
             W += s * dequantize(proj.words[t][e], proj.in_features,
                                 proj.out_features, int(proj.bits[t][e]),
-                                decoder="shift")
+                                decoder="window")
     return W
 
 

@@ -36,11 +36,11 @@ def codebook(states):
 
     Written from the integer definition above (not from any fp16 bit trick).
     """
-    s = np.asarray(states, dtype=np.int64) & 0xFFFF
+    s = np.asarray(states).astype(np.int32) & 0xFFFF
     h = (s * MCG_MULT) & 0xFFFF
     a = h >> 6
     b = h & 0x3FF
-    return (a - b).astype(np.float64) / 1024.0
+    return (a - b) / 1024.0
 
 
 def _stream_bits(words):
@@ -70,20 +70,33 @@ def tile_states_shift(words, K):
     s_{-1} is the last 16 stream bits (tail-biting); each step shifts the
     register right by K and inserts the next K stream bits at the top.
     """
-    bits = _stream_bits(words).astype(np.int64)
-    T = bits.shape[0]
+    w = np.ascontiguousarray(np.asarray(words, dtype=np.uint16))
+    by = np.ascontiguousarray(w.astype("<u2").view(np.uint8).reshape(w.shape[0], -1).T)
+    bits = np.unpackbits(by, axis=0, bitorder="little")   # [256K, T], bit-major
+    T = bits.shape[1]
     L = 256 * K
-    state = np.zeros(T, dtype=np.int64)
+    state = np.zeros(T, dtype=np.uint32)
     for t in range(STATE_BITS):
-        state |= bits[:, L - STATE_BITS + t] << t
-    out = np.empty((T, 256), dtype=np.int64)
+        state |= bits[L - STATE_BITS + t].astype(np.uint32) << t
+    out = np.empty((256, T), dtype=np.uint32)
     for i in range(256):
-        new = np.zeros(T, dtype=np.int64)
+        new = np.zeros(T, dtype=np.uint32)
         for u in range(K):
-            new |= bits[:, i * K + u] << u
+            new |= bits[i * K + u].astype(np.uint32) << u
         state = (state >> K) | (new << (STATE_BITS - K))
-        out[:, i] = state
-    return out
+        out[i] = state
+    return np.ascontiguousarray(out.T)
+
+
+_TABLE = None
+
+
+def codebook_lookup(states):
+    """codebook() of every 16-bit state, tabulated once and gathered."""
+    global _TABLE
+    if _TABLE is None:
+        _TABLE = codebook(np.arange(65536))
+    return _TABLE[np.asarray(states)]
 
 
 def decode_tiles_window(words, K):
@@ -94,11 +107,9 @@ def decode_tiles_window(words, K):
 
 def decode_tiles_shift(words, K):
     """[T, 16K] uint16 -> [T, 16(k), 16(n)] float64 via the shift register."""
-    v = codebook(tile_states_shift(words, K))
-    out = np.empty((v.shape[0], TILE, TILE))
-    for i in range(256):
-        out[:, i % TILE, i // TILE] = v[:, i]
-    return out
+    v = codebook_lookup(tile_states_shift(words, K))
+    # v[:, i] with i = 16 n + k; swap to [k][n] (a view, no copy)
+    return v.reshape(-1, TILE, TILE).swapaxes(1, 2)
 
 
 def tensor_words(in_features, out_features, K):
@@ -106,18 +117,19 @@ def tensor_words(in_features, out_features, K):
     return (in_features // TILE) * (out_features // TILE) * TILE * K
 
 
-def dequantize(words, in_features, out_features, K, decoder="window",
+def dequantize(words, in_features, out_features, K, decoder="shift",
                chunk_tiles=8192):
     """Dense W [in][out] (float64) of one trellis tensor.
 
     ``words`` is the flat uint16 tensor in [out/16][in/16][16K] order.
     """
     kt_n, nt_n = in_features // TILE, out_features // TILE
-    w = np.asarray(words, dtype=np.uint16).reshape(nt_n * kt_n, TILE * K)
+    w = np.asarray(words, dtype=np.uint16).reshape(nt_n, kt_n, TILE * K)
     dec = decode_tiles_window if decoder == "window" else decode_tiles_shift
-    tiles = np.empty((nt_n * kt_n, TILE, TILE))
-    for c0 in range(0, w.shape[0], chunk_tiles):
-        tiles[c0:c0 + chunk_tiles] = dec(w[c0:c0 + chunk_tiles], K)
-    # tiles[nt * kt_n + kt][k][n] -> W[16 kt + k][16 nt + n]
-    t = tiles.reshape(nt_n, kt_n, TILE, TILE)
-    return t.transpose(1, 2, 0, 3).reshape(in_features, out_features)
+    W = np.empty((kt_n, TILE, nt_n, TILE))      # W[16 kt + k][16 nt + n]
+    step = max(1, chunk_tiles // kt_n)
+    for n0 in range(0, nt_n, step):
+        n1 = min(nt_n, n0 + step)
+        tiles = dec(w[n0:n1].reshape(-1, TILE * K), K)      # [(nt, kt)][k][n]
+        W[:, :, n0:n1, :] = tiles.reshape(n1 - n0, kt_n, TILE, TILE).transpose(1, 2, 0, 3)
+    return W.reshape(in_features, out_features)

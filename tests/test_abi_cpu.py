@@ -1,0 +1,98 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+the header declares, reports its ABI version, and rejects bad arguments on
+the host before any device work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from trellis_quantized_moe_amd import exl3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "exl3moe.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(exl3_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = exl3.lib()
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert exl3.abi_version() == 1
+    L = exl3.lib()
+    for s in range(0, -9, -1):
+        msg = L.exl3_status_string(s).decode()
+        assert msg and msg != "unknown status"
+    assert L.exl3_status_string(123).decode() == "unknown status"
+
+
+def test_workspace_sizes():
+    L = exl3.lib()
+    a = L.exl3_moe_workspace_size(3072, 8, 192, 6144, 2048, 2048)
+    b = L.exl3_moe_workspace_size(3072, 8, 192, 6144, 2048, 4096)
+    c = L.exl3_moe_workspace_size(3072, 8, 192, 6144, 2048, 10 ** 6)
+    assert 0 < a < b <= c
+    # capacity beyond rows*topk does not grow the workspace
+    assert c == L.exl3_moe_workspace_size(3072, 8, 192, 6144, 2048, 24576)
+    assert L.exl3_moe_workspace_size(4, 2, 8, 200, 512, 8) == 0  # not a multiple of 128
+    lay = exl3.moe_layout(3072, 8, 192, 6144, 2048, 2048)
+    assert lay.passes == 12
+    offs = [lay.ctrl, lay.meta, lay.expert_of_pos, lay.plan, lay.xt, lay.at, lay.d, lay.yacc]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.total == a
+    assert L.exl3_linear_workspace_size(7, 4096, 4096) >= 7 * 4096 * 2
+
+
+def _proj(**kw):
+    d = dict(in_features=256, out_features=512, num_experts=8, num_stages=1,
+             trellis=256, scale=512, bits=768, suh=1024, svh=1280, chscale=1536)
+    d.update(kw)
+    return exl3.ProjC(**d)
+
+
+def _fwd(gate=None, up=None, down=None, rows=4, topk=2, capacity=8, out_dtype=exl3.F32,
+         ids=4096, ids_dtype=exl3.I32, w=8192, w_dtype=exl3.F32, x=16384, out=32768,
+         ws=65536, ws_bytes=1 << 40):
+    gate = gate or _proj()
+    up = up or _proj()
+    down = down or _proj(in_features=512, out_features=256)
+    return exl3.lib().exl3_moe_forward(
+        ctypes.c_void_p(x), rows, ctypes.c_void_p(ids), ids_dtype, ctypes.c_void_p(w),
+        w_dtype, topk, ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down),
+        ctypes.c_void_p(out), out_dtype, capacity, -1, ctypes.c_void_p(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=0), -1), (dict(ids=0), -1), (dict(ws=0), -1),
+    (dict(ids_dtype=exl3.F16), -2), (dict(w_dtype=exl3.I32), -2), (dict(out_dtype=exl3.BF16), -2),
+    (dict(gate=_proj(in_features=200)), -3), (dict(up=_proj(out_features=384)), -3),
+    (dict(down=_proj(in_features=512, out_features=128)), -3),
+    (dict(up=_proj(num_experts=7)), -3),
+    (dict(x=16385), -4), (dict(out=32770), -4),
+    (dict(topk=0), -7), (dict(topk=33), -7), (dict(capacity=0), -7), (dict(rows=-1), -7),
+    (dict(gate=_proj(num_stages=9)), -7), (dict(gate=_proj(num_experts=2000)), -7),
+    (dict(ws_bytes=10), -6),
+])
+def test_forward_rejects_bad_arguments_before_device_work(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_rows_zero_is_a_noop():
+    assert _fwd(rows=0, x=0, ws=0) == 0
+
+
+def test_host_pointers_are_rejected_as_not_device():
+    # everything valid on the host side; the device check must fail (no GPU
+    # here, or host memory on a GPU machine) without launching anything
+    assert _fwd() == -5

@@ -1,0 +1,259 @@
+"""GPU parity of the HIP path against the float64 oracle (MI355X only).
+
+Bars: bit-exact for the route pack and decoded weights; floating-point
+outputs within max|gpu - oracle_R| <= 2e-3 * RMS(oracle_R) (fp32 output);
+fp16 output equal to RNE of the fp32 output; invariances bit-exact.
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import linear as olinear  # noqa: E402
+from oracle import moe as omoe  # noqa: E402
+from oracle import route as oroute  # noqa: E402
+from oracle import trellis as otrellis  # noqa: E402
+from trellis_quantized_moe_amd import exl3, synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _rel_err(got, ref):
+    rms = float(np.sqrt(np.mean(np.square(ref))))
+    return float(np.max(np.abs(got - ref))) / rms
+
+
+def _fp16_of(t):
+    return t.float().cpu().numpy().astype(np.float16)
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("K", range(2, 9))
+def test_decode_tiles_bit_exact(K):
+    _say("decode K=%d" % K)
+    rng = np.random.default_rng(100 + K)
+    ntiles = 4096
+    words = rng.integers(0, 65536, size=(ntiles, 16 * K), dtype=np.uint16)
+    words[0] = 0
+    words[1] = 0xFFFF
+    d = torch.from_numpy(words.reshape(-1).view(np.int16)).to(DEV)
+    got = exl3.exl3_decode_tiles(d, K).cpu().numpy()
+    ref = otrellis.decode_tiles_shift(words, K).astype(np.float16)
+    assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
+
+
+# ------------------------------------------------------------------- route
+@pytest.mark.parametrize("rows,topk,E,idt,wdt,seed", [
+    (16, 2, 8, "i32", "f32", 0), (32, 8, 128, "i64", "bf16", 1),
+    (1, 8, 128, "i64", "f16", 2), (3072, 8, 192, "i32", "f16", 3),
+    (700, 6, 1024, "i64", "f32", 4), (5, 32, 3, "i32", "bf16", 5)])
+def test_route_pack_bit_exact(rows, topk, E, idt, wdt, seed):
+    _say("route", rows, topk, E, idt, wdt)
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(-2, E + 2, size=(rows, topk))  # some dropped
+    w = rng.random((rows, topk)).astype(np.float32)
+    if wdt == "bf16":
+        wb = synth.f32_to_bf16_bits(w)
+        wt = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16)
+        wexact = synth.bf16_bits_to_f64(wb)
+    elif wdt == "f16":
+        wt = torch.from_numpy(w.astype(np.float16))
+        wexact = w.astype(np.float16).astype(np.float64)
+    else:
+        wt = torch.from_numpy(w)
+        wexact = w.astype(np.float64)
+    it = torch.from_numpy(ids.astype(np.int64 if idt == "i64" else np.int32))
+    meta = exl3.exl3_route_pack(it.to(DEV), wt.to(DEV), E)
+    torch.cuda.synchronize()
+    ref = oroute.route_pack(ids, wexact, E)
+    P = rows * topk
+    assert np.array_equal(meta["expert_count"].cpu().numpy(), ref["count"])
+    assert np.array_equal(meta["expert_offset"].cpu().numpy(), ref["offset"])
+    assert np.array_equal(meta["pair_of_pos"].cpu().numpy()[:P], ref["pair_of_pos"])
+    assert np.array_equal(meta["pos_of_pair"].cpu().numpy()[:P], ref["pos_of_pair"])
+    assert np.array_equal(meta["weight_of_pos"].cpu().numpy()[:P].astype(np.float64),
+                          ref["weight_of_pos"])
+    assert int(meta["num_active"][0]) == ref["num_active"]
+    assert int(meta["status"][0]) == ref["dropped"]
+
+
+# ------------------------------------------------------------------ linear
+def _linear_case(fin, fout, stages, rows, seed):
+    bits = np.array([[k] for k, _ in stages], dtype=np.int32)
+    scale = np.array([[s] for _, s in stages], dtype=np.float32)
+    p = synth.make_proj(seed, "linear", 1, fin, fout, bits, scale)
+    x = np.random.default_rng(seed).standard_normal((rows, fin)).astype(np.float16)
+    return p, x
+
+
+@pytest.mark.parametrize("fin,fout,stages,rows", [
+    (256, 384, ((4, 1.0),), 1), (256, 384, ((3, 1.0), (2, 0.37)), 33),
+    (512, 256, ((8, 1.0), (5, -0.25)), 7), (384, 128, ((2, 1.0), (7, 0.5), (6, 0.0)), 17),
+    (128, 256, ((6, 1.0),), 40)])
+def test_linear_parity(fin, fout, stages, rows):
+    _say("linear", fin, fout, stages, rows)
+    p, x = _linear_case(fin, fout, stages, rows, seed=fin + fout + rows)
+    dp = exl3.DeviceProj(p, DEV)
+    xd = exl3.f16_tensor(x)
+    y32 = exl3.exl3_linear(xd, dp, torch.float32)
+    y16 = exl3.exl3_linear(xd, dp, torch.float16)
+    torch.cuda.synchronize()
+    ref = olinear.linear(x, p, "R")
+    got = y32.cpu().double().numpy()
+    assert _rel_err(got, ref) <= TOL
+    assert np.array_equal(_fp16_of(y32).view(np.uint16),
+                          y16.cpu().numpy().view(np.uint16))
+
+
+@pytest.mark.parametrize("K", [2, 3, 4, 8])
+def test_linear_4096_parity_and_row_invariance(K):
+    """The linear workload: rows 1/7/32/128 and 2048 (also as 16 chunks of
+    128); a row's output bytes are identical in every call."""
+    _say("linear4096 K=%d" % K)
+    p, x = synth.linear_workload(K, 2048)
+    dp = exl3.DeviceProj(p, DEV)
+    xd = exl3.f16_tensor(x)
+    full = exl3.exl3_linear(xd, dp, torch.float16)
+    chunks = torch.cat([exl3.exl3_linear(xd[i:i + 128], dp, torch.float16)
+                        for i in range(0, 2048, 128)])
+    torch.cuda.synchronize()
+    fb = full.cpu().numpy().view(np.uint16)
+    assert np.array_equal(chunks.cpu().numpy().view(np.uint16), fb)
+    for rows in (1, 7, 32, 128):
+        y = exl3.exl3_linear(xd[:rows], dp, torch.float16)
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), fb[:rows]), rows
+    # parity on sampled rows (fp32 output)
+    sample = [0, 1, 777, 2047]
+    y32 = exl3.exl3_linear(xd, dp, torch.float32).cpu().double().numpy()
+    ref = olinear.linear(x[sample], p, "R")
+    assert _rel_err(y32[sample], ref) <= TOL
+
+
+# --------------------------------------------------------------------- moe
+def _moe_inputs(wl):
+    gate, up, down = (exl3.DeviceProj(p, DEV) for p in (wl.gate, wl.up, wl.down))
+    x, ids, w = exl3.device_inputs(wl, DEV)
+    return gate, up, down, x, ids, w
+
+
+def _tiny(**over):
+    return synth.moe_workload("tiny", **over)
+
+
+@pytest.mark.parametrize("over", [
+    {}, dict(K=(2, 3, 5, 8)), dict(rows=37, topk=3, E=5, K=(4, 6)),
+    dict(rows=1, topk=8, E=16, K=(3, 4))])
+def test_moe_tiny_parity(over):
+    _say("moe tiny", over)
+    wl = _tiny(**over)
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    y32 = exl3.exl3_moe_forward(x, ids, w, gate, up, down, wl.capacity, torch.float32)
+    y16 = exl3.exl3_moe_forward(x, ids, w, gate, up, down, wl.capacity, torch.float16)
+    torch.cuda.synchronize()
+    ref = omoe.moe_forward(wl.x, wl.ids, wl.weights_f64, wl.gate, wl.up, wl.down, "R")
+    assert _rel_err(y32.cpu().double().numpy(), ref) <= TOL
+    assert np.array_equal(_fp16_of(y32).view(np.uint16), y16.cpu().numpy().view(np.uint16))
+
+
+def test_moe_capacity_invariance():
+    """capacity in {1, 7, span, span+1, 32, inf}: identical bytes."""
+    wl = _tiny()
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    span = int(np.bincount(wl.ids.reshape(-1), minlength=8).max())
+    base = exl3.exl3_moe_forward(x, ids, w, gate, up, down, 10 ** 6, torch.float32)
+    for cap in (1, 7, span, span + 1, 32):
+        _say("capacity", cap)
+        y = exl3.exl3_moe_forward(x, ids, w, gate, up, down, cap, torch.float32)
+        assert torch.equal(y.view(torch.int32), base.view(torch.int32)), cap
+
+
+def test_moe_additive_equals_forward_and_ignores_hint():
+    wl = _tiny(rows=29)
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    fwd = exl3.exl3_moe_forward(x, ids, w, gate, up, down, 16, torch.float32)
+    meta = exl3.exl3_route_pack(ids, w, wl.num_experts)
+    for hint in (-1, 0, 3, 1000):
+        add = exl3.exl3_moe_additive(x, wl.topk, meta, gate, up, down, 16, torch.float32,
+                                     num_active_hint=hint)
+        assert torch.equal(add.view(torch.int32), fwd.view(torch.int32)), hint
+
+
+def test_moe_row_invariance_member_counts():
+    """A row's bytes do not change with the other rows (member counts)."""
+    wl = _tiny(rows=64)
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    full = exl3.exl3_moe_forward(x, ids, w, gate, up, down, 10 ** 6, torch.float32)
+    for r0, r1 in ((0, 1), (5, 6), (0, 17), (40, 64)):
+        part = exl3.exl3_moe_forward(x[r0:r1], ids[r0:r1], w[r0:r1], gate, up, down,
+                                     10 ** 6, torch.float32)
+        assert torch.equal(part.view(torch.int32), full[r0:r1].view(torch.int32)), (r0, r1)
+
+
+def test_zero_scale_equals_absent_stage():
+    wl = _tiny(rows=16)
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    base = exl3.exl3_moe_forward(x, ids, w, gate, up, down, 64, torch.float32)
+
+    def with_zero_stage(p, null):
+        n3 = synth.words_per_tensor(p.in_features, p.out_features, 3)
+        words = p.words + [[None if null else np.full(n3, 0x1234, np.uint16)
+                            for e in range(p.num_experts)]]
+        return synth.Proj(p.in_features, p.out_features, p.num_experts, words,
+                          np.concatenate([p.scale, np.zeros((1, p.num_experts), np.float32)]),
+                          np.concatenate([p.bits, np.full((1, p.num_experts), 3, np.int32)]),
+                          p.suh, p.svh, p.chscale)
+
+    for null in (False, True):
+        g2, u2, d2 = (exl3.DeviceProj(with_zero_stage(p, null), DEV)
+                      for p in (wl.gate, wl.up, wl.down))
+        y = exl3.exl3_moe_forward(x, ids, w, g2, u2, d2, 64, torch.float32)
+        assert torch.equal(y.view(torch.int32), base.view(torch.int32)), null
+
+
+def test_dropped_ids_and_unrouted_rows():
+    wl = _tiny(rows=8)
+    ids_np = wl.ids.copy()
+    ids_np[3, :] = [99, -1]        # row 3 fully dropped -> zeros
+    ids_np[5, 1] = 8               # one dropped pair
+    wl.ids = ids_np
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    for dt in (torch.float32, torch.float16):
+        out = torch.full((8, wl.hidden), 7.0, dtype=dt, device=DEV)
+        y = exl3.exl3_moe_forward(x, ids, w, gate, up, down, 5, dt, out=out)
+        torch.cuda.synchronize()
+        ref = omoe.moe_forward(wl.x, ids_np, wl.weights_f64, wl.gate, wl.up, wl.down, "R")
+        assert torch.all(y[3] == 0)
+        assert _rel_err(y.cpu().double().numpy(), ref) <= (TOL if dt == torch.float32 else 5e-3)
+
+
+# ---------------------------------------------------- full-size workloads
+def _sampled_parity(wl, rows_sample, capacity):
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    y = exl3.exl3_moe_forward(x, ids, w, gate, up, down, capacity, torch.float32)
+    torch.cuda.synchronize()
+    got = y.cpu().double().numpy()[rows_sample]
+    ref = omoe.moe_forward(wl.x, wl.ids, wl.weights_f64, wl.gate, wl.up, wl.down, "R",
+                           rows=rows_sample)
+    err = _rel_err(got, ref)
+    _say("  sampled rows", rows_sample, "err %.3e" % err)
+    return err
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_decode_workload_sampled(M):
+    _say("decode workload M=%d" % M)
+    wl = synth.moe_workload("decode", rows=M)
+    assert _sampled_parity(wl, [0] if M == 1 else [0, M - 1], M * 8) <= TOL
+
+
+def test_additive_workload_sampled():
+    _say("additive workload")
+    wl = synth.moe_workload("additive")
+    assert _sampled_parity(wl, [3], 1024) <= TOL

@@ -1,0 +1,190 @@
+// Device building blocks for gfx950: trellis decode into MFMA B operands,
+// the MCG16 codebook on packed 16-bit lanes, a 128-point FWHT on 16-lane
+// groups, and the v_mfma_f32_16x16x32_f16 wrapper.
+//
+// Format (this library's definition; the pages name trellis widths and the
+// MCG codebook but define neither — exllamav3 PR #284 "MoE: Add fused
+// additive EXL3 kernels", API contract; TensorFold PR #837, What this
+// changes):
+//   CB(s)  = ((h >> 6) - (h & 1023)) / 1024,  h = s * 0x9E37 mod 2^16
+//   tile   16 (k) x 16 (n) weights, 256*K-bit tail-biting stream; the state of
+//          weight i is the 16 stream bits ending at bit i*K + K - 1; weight i
+//          sits at (k = i mod 16, n = i / 16)
+//   tensor uint16 [out/16][in/16][16K], tile (kt, nt) at (nt*in/16 + kt)*16K
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace exl3 {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Global-address-space views (keeps loads on the global_load path).
+typedef const uint32_t __attribute__((address_space(1))) *gu32p;
+typedef const u32x4 __attribute__((address_space(1))) *gu32x4p;
+
+constexpr float kRsqrt128 = 0.08838834764831845f;  // 1/sqrt(128), fp32
+
+// GPU-internal k order of rotated activations: inside every aligned group of
+// 16 entries, stored slot p holds entry kSigma[p] =
+// {0,4,1,5,2,6,3,7, 8,12,9,13,10,14,11,15}. It matches the order in which one
+// lane's decoded B values reach the MFMA (see decode_column).
+// Entry k (0..15) of a 16-group -> stored slot.
+__device__ __forceinline__ int sigma_inv(int k) {
+  // inverse of kSigma: k -> 2*(k&3) + ((k>>2)&1) + (k&8)
+  return ((k & 3) << 1) | ((k >> 2) & 1) | (k & 8);
+}
+
+// ---------------------------------------------------------------- codebook
+// Two MCG16 states in the 16-bit halves of s2 -> two fp16 codebook values.
+// (1 + a/1024) - (1 + b/1024) is exact in fp16, so the packed add returns
+// (a - b)/1024 exactly: v_pk_mul_lo_u16, v_pk_lshrrev_b16, v_or_b32,
+// v_and_or_b32, v_pk_add_f16.
+__device__ __forceinline__ uint32_t codebook2(uint32_t s2, uint32_t mask_lo10) {
+  u16x2 s = __builtin_bit_cast(u16x2, s2);
+  u16x2 h = s * (u16x2){(unsigned short)0x9E37, (unsigned short)0x9E37};
+  u16x2 a = h >> (u16x2){6, 6};
+  const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+  uint32_t A = __builtin_bit_cast(uint32_t, a) | 0x3C003C00u;
+  // (h & 0x03FF03FF) | 0xBC00BC00 in one VOP3 op: gfx9 VOP3 takes no literal,
+  // so the mask comes in a VGPR and the OR constant in an SGPR.
+  uint32_t B;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(B) : "v"(hb), "v"(mask_lo10), "s"(0xBC00BC00u));
+  f16x2 r = __builtin_bit_cast(f16x2, A) + __builtin_bit_cast(f16x2, B);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// A VGPR holding 0x03FF03FF that the compiler cannot fold back into a literal.
+__device__ __forceinline__ uint32_t codebook_mask() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x3ff03ff" : "=v"(m));
+  return m;
+}
+
+// ------------------------------------------------------------ tile geometry
+template <int K>
+struct Geom {
+  static constexpr int kTileDw = 8 * K;  // dwords per tile
+  // dwords covering one column's window (15K + 16 bits) at the worst offset
+  static constexpr int kLoadDw = (K == 2) ? 2 : (K <= 4) ? 3 : (K <= 6) ? 4 : 5;
+  // dwords of the window once shifted to bit 0
+  static constexpr int kNormDw = (15 * K + 16 + 31) / 32;
+};
+
+// Dword indices (within a tile) and bit shift of the window of column n.
+// The window of states 16n..16n+15 starts at bit 16nK + K - 16; for n = 0 it
+// wraps to the end of the tile (tail-biting).
+template <int K>
+struct ColumnWindow {
+  int idx[Geom<K>::kLoadDw];
+  uint32_t shift;
+  __device__ __forceinline__ explicit ColumnWindow(int n) {
+    const int b = 16 * n * K + K - 16;
+    const int d0 = b >> 5;  // floor
+    shift = (uint32_t)(b & 31);
+#pragma unroll
+    for (int j = 0; j < Geom<K>::kLoadDw; ++j) {
+      int d = d0 + j;
+      d += (d < 0) ? Geom<K>::kTileDw : 0;
+      d -= (d >= Geom<K>::kTileDw) ? Geom<K>::kTileDw : 0;
+      idx[j] = d;
+    }
+  }
+};
+
+// 32 bits of the normalised window starting at bit OFF (bits < 0 read 0).
+template <int K, int OFF>
+__device__ __forceinline__ uint32_t window32(const uint32_t (&N)[Geom<K>::kNormDw]) {
+  constexpr int NN = Geom<K>::kNormDw;
+  if constexpr (OFF < 0) {
+    return N[0] << (-OFF);
+  } else {
+    constexpr int w = OFF >> 5, s = OFF & 31;
+    const uint32_t lo = N[w];
+    if constexpr (s == 0) {
+      return lo;
+    } else {
+      const uint32_t hi = (w + 1 < NN) ? N[(w + 1 < NN) ? w + 1 : w] : 0u;
+      return __builtin_amdgcn_alignbit(hi, lo, s);
+    }
+  }
+}
+
+// Decode one tile column (16 states) from its raw dwords into 8 packed fp16
+// pairs. Register v holds states (j, j+4) with j = (v & 3) + 8 * (v >> 2),
+// so registers 0..3 feed k = {0,4,1,5,2,6,3,7} and 4..7 feed
+// k = {8,12,9,13,10,14,11,15} of the tile column: the kSigma order.
+template <int K>
+__device__ __forceinline__ void decode_column(const uint32_t (&raw)[Geom<K>::kLoadDw],
+                                              uint32_t shift, uint32_t mask,
+                                              uint32_t (&out)[8]) {
+  constexpr int ND = Geom<K>::kLoadDw, NN = Geom<K>::kNormDw;
+  uint32_t N[NN];
+#pragma unroll
+  for (int j = 0; j < NN; ++j) {
+    const uint32_t hi = (j + 1 < ND) ? raw[(j + 1 < ND) ? j + 1 : j] : 0u;
+    N[j] = __builtin_amdgcn_alignbit(hi, raw[j], shift);
+  }
+#define EXL3_DECODE_REG(v)                                                   \
+  {                                                                          \
+    constexpr int j = ((v) & 3) + 8 * ((v) >> 2);                            \
+    const uint32_t lo = window32<K, j * K>(N);                               \
+    const uint32_t hi = window32<K, (j + 4) * K - 16>(N);                    \
+    out[v] = codebook2((lo & 0x0000FFFFu) | (hi & 0xFFFF0000u), mask);        \
+  }
+  EXL3_DECODE_REG(0) EXL3_DECODE_REG(1) EXL3_DECODE_REG(2) EXL3_DECODE_REG(3)
+  EXL3_DECODE_REG(4) EXL3_DECODE_REG(5) EXL3_DECODE_REG(6) EXL3_DECODE_REG(7)
+#undef EXL3_DECODE_REG
+}
+
+// -------------------------------------------------------------------- MFMA
+// D[16x16] += A[16x32] * B[32x16], fp16 inputs, fp32 accumulate. Lane l
+// supplies A row (l & 15) and B column (l & 15), 8 k-entries each for the
+// k-group l >> 4; it receives D rows 4*(l>>4) + r (r = 0..3), column l & 15.
+__device__ __forceinline__ f32x4 mfma16x16x32(const f16x8 &a, const f16x8 &b,
+                                              const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// --------------------------------------------------------------------- FWHT
+// Unnormalised 128-point Walsh-Hadamard transform (Sylvester order) on a
+// group of 16 consecutive lanes; lane i of the group holds entries
+// i + 16*j in v[j]. Butterflies (lo, hi) -> (lo + hi, lo - hi), distances
+// 1, 2, 4, 8 across lanes then 16, 32, 64 in registers. The fixed order makes
+// the fp32 result a pure function of the inputs.
+__device__ __forceinline__ void fwht128_group16(float (&v)[8]) {
+  const int i = threadIdx.x & 15;
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) {
+    const bool upper = (i & d) != 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float o = __shfl_xor(v[j], d, 64);
+      v[j] = upper ? (o - v[j]) : (v[j] + o);
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < 8; d <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if ((j & d) == 0) {
+        const float lo = v[j], hi = v[j + d];
+        v[j] = lo + hi;
+        v[j + d] = lo - hi;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);  // RNE
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+}  // namespace exl3

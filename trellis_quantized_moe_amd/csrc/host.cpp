@@ -1,0 +1,500 @@
+// C ABI of the fused EXL3 routed-experts layer: host-side validation,
+// workspace layout and stream-ordered launch orchestration. No call
+// synchronises, allocates or frees; every argument is checked before the
+// first launch (exllamav3 PR #284 "MoE: Add fused additive EXL3 kernels",
+// Summary: validate device, contiguity, dtype, shape, workspace and routing
+// contracts before device-side mutation; API contract: exact ABI version).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/exl3moe.h"
+#include "kernels.hpp"
+
+using namespace exl3;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Device residency: the pointer must be device (or managed) memory of the
+// current device. Called only after every host-side check passed.
+int32_t check_device(const void *p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return EXL3_E_DEVICE;
+  hipPointerAttribute_t a;
+  std::memset(&a, 0, sizeof(a));
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return EXL3_E_DEVICE;
+  }
+  if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged) return EXL3_E_DEVICE;
+  if (a.device != dev) return EXL3_E_DEVICE;
+  return EXL3_OK;
+}
+
+int32_t check_features(int32_t f) {
+  return (f > 0 && f <= EXL3_MAX_FEATURES && f % 128 == 0) ? EXL3_OK : EXL3_E_SHAPE;
+}
+
+int32_t check_proj_host(const exl3_proj *p) {
+  if (!p) return EXL3_E_NULL;
+  if (!p->trellis || !p->scale || !p->bits || !p->suh || !p->svh || !p->chscale)
+    return EXL3_E_NULL;
+  if (check_features(p->in_features) || check_features(p->out_features)) return EXL3_E_SHAPE;
+  if (p->num_experts < 1 || p->num_experts > EXL3_MAX_EXPERTS) return EXL3_E_ARG;
+  if (p->num_stages < 1 || p->num_stages > EXL3_MAX_STAGES) return EXL3_E_ARG;
+  const void *ptrs[] = {p->trellis, p->scale, p->bits, p->suh, p->svh, p->chscale};
+  for (const void *q : ptrs)
+    if (!aligned16(q)) return EXL3_E_ALIGN;
+  return EXL3_OK;
+}
+
+int32_t check_proj_device(const exl3_proj *p) {
+  const void *ptrs[] = {p->trellis, p->scale, p->bits, p->suh, p->svh, p->chscale};
+  for (const void *q : ptrs)
+    if (int32_t s = check_device(q)) return s;
+  return EXL3_OK;
+}
+
+ProjDev to_dev(const exl3_proj *p) {
+  ProjDev d;
+  d.trellis = p->trellis;
+  d.scale = p->scale;
+  d.bits = p->bits;
+  d.svh = p->svh;
+  d.cs = p->chscale;
+  d.num_stages = p->num_stages;
+  return d;
+}
+
+bool out_dtype_ok(int32_t t) { return t == EXL3_F16 || t == EXL3_F32; }
+
+struct MoeLayout {
+  size_t ctrl, count, offset, pair_of_pos, weight_of_pos, pos_of_pair, num_active, status;
+  size_t expert_of_pos, plan, xt, at, d, yacc, total;
+  int passes, slots, cap;
+};
+
+MoeLayout moe_layout(int32_t rows, int32_t topk, int32_t E, int32_t H, int32_t I,
+                     int32_t capacity) {
+  MoeLayout L{};
+  const int64_t P = (int64_t)rows * topk;
+  const int64_t C = std::max<int64_t>(1, std::min<int64_t>(capacity, std::max<int64_t>(P, 1)));
+  L.cap = (int)C;
+  L.passes = P > 0 ? (int)((P + C - 1) / C) : 0;
+  L.slots = (int)(std::min<int64_t>(E, C) + (C + kBM - 1) / kBM);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.ctrl = take(256);
+  L.count = take(4 * (size_t)E);
+  L.offset = take(4 * (size_t)(E + 1));
+  L.pair_of_pos = take(4 * (size_t)P);
+  L.weight_of_pos = take(4 * (size_t)P);
+  L.pos_of_pair = take(4 * (size_t)P);
+  L.num_active = take(4);
+  L.status = take(4);
+  L.expert_of_pos = take(4 * (size_t)P);
+  L.plan = take(4 * (size_t)L.passes * (1 + 3 * (size_t)L.slots));
+  L.xt = take(2 * (size_t)C * 2 * H);
+  L.at = take(2 * (size_t)C * I);
+  L.d = take(4 * (size_t)C * H);
+  L.yacc = take(4 * (size_t)rows * H);
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+  return (T *)((char *)ws + off);
+}
+
+int32_t validate_moe_common(const uint16_t *x, int32_t rows, int32_t topk,
+                            const exl3_proj *gate, const exl3_proj *up,
+                            const exl3_proj *down, void *out, int32_t out_dtype,
+                            int32_t capacity, void *ws) {
+  if (rows < 0) return EXL3_E_ARG;
+  if (!x || !out || !ws) return EXL3_E_NULL;
+  for (const exl3_proj *p : {gate, up, down})
+    if (int32_t s = check_proj_host(p)) return s;
+  if (!out_dtype_ok(out_dtype)) return EXL3_E_DTYPE;
+  if (topk < 1 || topk > EXL3_MAX_TOPK) return EXL3_E_ARG;
+  if (capacity < 1) return EXL3_E_ARG;
+  const int H = gate->in_features, I = gate->out_features, E = gate->num_experts;
+  if (up->in_features != H || up->out_features != I || down->in_features != I ||
+      down->out_features != H)
+    return EXL3_E_SHAPE;
+  if (up->num_experts != E || down->num_experts != E) return EXL3_E_SHAPE;
+  if ((int64_t)rows * topk > (int64_t)1 << 30) return EXL3_E_ARG;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return EXL3_E_ALIGN;
+  return EXL3_OK;
+}
+
+int32_t validate_moe_device(const uint16_t *x, const exl3_proj *gate,
+                            const exl3_proj *up, const exl3_proj *down, void *out,
+                            void *ws) {
+  for (const void *q : {(const void *)x, (const void *)out, (const void *)ws})
+    if (int32_t s = check_device(q)) return s;
+  for (const exl3_proj *p : {gate, up, down})
+    if (int32_t s = check_proj_device(p)) return s;
+  return EXL3_OK;
+}
+
+// Passes over the packed positions: rotate, gate/up, down, combine.
+int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
+                    const exl3_proj *gate, const exl3_proj *up,
+                    const exl3_proj *down, void *out, int32_t out_dtype,
+                    const MoeLayout &L, void *ws, const int32_t *pair_of_pos,
+                    const int32_t *pos_of_pair, const float *weight_of_pos,
+                    const int32_t *offset, hipStream_t st) {
+  const int H = gate->in_features, I = gate->out_features, E = gate->num_experts;
+  const int64_t P = (int64_t)rows * topk;
+  const int32_t *total_valid = offset + E;
+  int32_t *ctrl = at<int32_t>(ws, L.ctrl);
+  for (int pass = 0; pass < L.passes; ++pass) {
+    const int pb = pass * L.cap;
+    const int npos = (int)std::min<int64_t>(L.cap, P - pb);
+    const int tiles = std::min(E, npos) + (npos + kBM - 1) / kBM;
+    const int32_t *plan = at<int32_t>(ws, L.plan) + (size_t)pass * (1 + 3 * (size_t)L.slots);
+
+    RotParams rp{};
+    rp.x = x;
+    rp.H = H;
+    rp.topk = topk;
+    rp.suh[0] = gate->suh;
+    rp.suh[1] = up->suh;
+    rp.nproj = 2;
+    rp.pair_of_pos = pair_of_pos;
+    rp.expert_of_pos = at<int32_t>(ws, L.expert_of_pos);
+    rp.total_valid = total_valid;
+    rp.pass_base = pb;
+    rp.pairs = (int)P;
+    rp.nitems = npos;
+    rp.xt = at<uint16_t>(ws, L.xt);
+    rp.ctrl_clear = nullptr;
+    if (launch_rotate(rp, st) != hipSuccess) return EXL3_E_LAUNCH;
+
+    GemmParams g{};
+    g.proj[0] = to_dev(gate);
+    g.proj[1] = to_dev(up);
+    g.E = E;
+    g.in_f = H;
+    g.out_f = I;
+    g.A = at<uint16_t>(ws, L.xt);
+    g.lda = 2 * (int64_t)H;
+    g.a_proj_stride = H;
+    g.plan_ntiles = plan;
+    g.plan_tiles = plan + 1;
+    g.suh_down = down->suh;
+    g.out_h = at<uint16_t>(ws, L.at);
+    g.ldo = I;
+    g.ctrl = ctrl;
+    if (launch_gemm(EPI_GATEUP, g, tiles, I / 128, st) != hipSuccess) return EXL3_E_LAUNCH;
+
+    GemmParams dn{};
+    dn.proj[0] = to_dev(down);
+    dn.E = E;
+    dn.in_f = I;
+    dn.out_f = H;
+    dn.A = at<uint16_t>(ws, L.at);
+    dn.lda = I;
+    dn.plan_ntiles = plan;
+    dn.plan_tiles = plan + 1;
+    dn.out_f32 = at<float>(ws, L.d);
+    dn.ldo = H;
+    dn.weight_of_pos = weight_of_pos;
+    dn.pass_base = pb;
+    dn.ctrl = ctrl;
+    if (launch_gemm(EPI_DOWN, dn, tiles, H / 128, st) != hipSuccess) return EXL3_E_LAUNCH;
+
+    CombineParams cp{};
+    cp.rows = rows;
+    cp.topk = topk;
+    cp.H = H;
+    cp.pairs = (int)P;
+    cp.pair_of_pos = pair_of_pos;
+    cp.pos_of_pair = pos_of_pair;
+    cp.total_valid = total_valid;
+    cp.pass_base = pb;
+    cp.pass_end = pb + L.cap;
+    cp.d = at<float>(ws, L.d);
+    cp.yacc = at<float>(ws, L.yacc);
+    cp.out = out;
+    cp.out_f32 = out_dtype == EXL3_F32;
+    if (launch_combine(cp, npos, st) != hipSuccess) return EXL3_E_LAUNCH;
+  }
+  return EXL3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t exl3_abi_version(void) { return EXL3_ABI_VERSION; }
+
+const char *exl3_status_string(int32_t s) {
+  switch (s) {
+    case EXL3_OK: return "ok";
+    case EXL3_E_NULL: return "null pointer";
+    case EXL3_E_DTYPE: return "unsupported dtype";
+    case EXL3_E_SHAPE: return "bad or inconsistent shape (features must be positive multiples of 128)";
+    case EXL3_E_ALIGN: return "pointer not 16-byte aligned";
+    case EXL3_E_DEVICE: return "pointer not on the current HIP device (or no device)";
+    case EXL3_E_WORKSPACE: return "workspace missing or too small";
+    case EXL3_E_ARG: return "argument out of range";
+    case EXL3_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t exl3_linear_workspace_size(int32_t rows, int32_t in_features, int32_t out_features) {
+  (void)out_features;
+  if (rows < 0 || in_features < 0) return 0;
+  return 256 + align_up(2 * (size_t)rows * in_features);
+}
+
+int32_t exl3_linear(const uint16_t *x, int32_t rows, const exl3_proj *proj, void *out,
+                    int32_t out_dtype, void *ws, size_t ws_bytes, void *stream) {
+  if (rows < 0) return EXL3_E_ARG;
+  if (rows == 0) return EXL3_OK;
+  if (!x || !out || !ws) return EXL3_E_NULL;
+  if (int32_t s = check_proj_host(proj)) return s;
+  if (proj->num_experts != 1) return EXL3_E_ARG;
+  if (!out_dtype_ok(out_dtype)) return EXL3_E_DTYPE;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return EXL3_E_ALIGN;
+  if (ws_bytes < exl3_linear_workspace_size(rows, proj->in_features, proj->out_features))
+    return EXL3_E_WORKSPACE;
+  for (const void *q : {(const void *)x, (const void *)out, (const void *)ws})
+    if (int32_t s = check_device(q)) return s;
+  if (int32_t s = check_proj_device(proj)) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  int32_t *ctrl = (int32_t *)ws;
+  uint16_t *xt = at<uint16_t>(ws, 256);
+  RotParams rp{};
+  rp.x = x;
+  rp.H = proj->in_features;
+  rp.suh[0] = proj->suh;
+  rp.nproj = 1;
+  rp.nitems = rows;
+  rp.xt = xt;
+  rp.ctrl_clear = ctrl;
+  if (launch_rotate(rp, st) != hipSuccess) return EXL3_E_LAUNCH;
+
+  GemmParams g{};
+  g.proj[0] = to_dev(proj);
+  g.E = 1;
+  g.in_f = proj->in_features;
+  g.out_f = proj->out_features;
+  g.A = xt;
+  g.lda = proj->in_features;
+  g.rows = rows;
+  g.ldo = proj->out_features;
+  if (out_dtype == EXL3_F32) g.out_f32 = (float *)out;
+  else g.out_h = (uint16_t *)out;
+  g.ctrl = ctrl;
+  if (launch_gemm(EPI_LINEAR, g, (rows + kBM - 1) / kBM, proj->out_features / 128, st) !=
+      hipSuccess)
+    return EXL3_E_LAUNCH;
+  return EXL3_OK;
+}
+
+int32_t exl3_moe_layout(int32_t rows, int32_t topk, int32_t num_experts, int32_t hidden,
+                        int32_t intermediate, int32_t capacity, exl3_moe_layout_t *out) {
+  if (!out) return EXL3_E_NULL;
+  if (rows < 0 || topk < 1 || topk > EXL3_MAX_TOPK || capacity < 1 || num_experts < 1 ||
+      num_experts > EXL3_MAX_EXPERTS)
+    return EXL3_E_ARG;
+  if (check_features(hidden) || check_features(intermediate)) return EXL3_E_SHAPE;
+  const MoeLayout L = moe_layout(rows, topk, num_experts, hidden, intermediate, capacity);
+  out->ctrl = L.ctrl;
+  out->meta = L.count;
+  out->expert_of_pos = L.expert_of_pos;
+  out->plan = L.plan;
+  out->xt = L.xt;
+  out->at = L.at;
+  out->d = L.d;
+  out->yacc = L.yacc;
+  out->total = L.total;
+  out->passes = L.passes;
+  out->plan_slots = L.slots;
+  return EXL3_OK;
+}
+
+size_t exl3_moe_workspace_size(int32_t rows, int32_t topk, int32_t num_experts, int32_t hidden,
+                               int32_t intermediate, int32_t capacity) {
+  exl3_moe_layout_t l;
+  if (exl3_moe_layout(rows, topk, num_experts, hidden, intermediate, capacity, &l) != EXL3_OK)
+    return 0;
+  return l.total;
+}
+
+int32_t exl3_route_pack(const void *ids, int32_t ids_dtype, const void *w, int32_t w_dtype,
+                        int32_t rows, int32_t topk, int32_t num_experts,
+                        const exl3_route_meta *meta, void *stream) {
+  if (rows < 0) return EXL3_E_ARG;
+  if (!meta) return EXL3_E_NULL;
+  if (topk < 1 || topk > EXL3_MAX_TOPK || num_experts < 1 || num_experts > EXL3_MAX_EXPERTS)
+    return EXL3_E_ARG;
+  if ((int64_t)rows * topk > (int64_t)1 << 30) return EXL3_E_ARG;
+  if (rows == 0) return EXL3_OK;
+  if (!ids || !w) return EXL3_E_NULL;
+  if (ids_dtype != EXL3_I32 && ids_dtype != EXL3_I64) return EXL3_E_DTYPE;
+  if (w_dtype != EXL3_F16 && w_dtype != EXL3_BF16 && w_dtype != EXL3_F32) return EXL3_E_DTYPE;
+  void *mp[] = {meta->expert_count, meta->expert_offset, meta->pair_of_pos,
+                meta->weight_of_pos, meta->pos_of_pair, meta->num_active, meta->status};
+  for (void *q : mp)
+    if (!q) return EXL3_E_NULL;
+  for (const void *q : {ids, w})
+    if (!aligned16(q)) return EXL3_E_ALIGN;
+  for (void *q : mp)
+    if (!aligned16(q)) return EXL3_E_ALIGN;
+  for (const void *q : {ids, w})
+    if (int32_t s = check_device(q)) return s;
+  for (void *q : mp)
+    if (int32_t s = check_device(q)) return s;
+
+  PackParams p{};
+  p.ids = ids;
+  p.ids_i64 = ids_dtype == EXL3_I64;
+  p.w = w;
+  p.w_dtype = w_dtype == EXL3_F16 ? 1 : w_dtype == EXL3_BF16 ? 2 : 3;
+  p.rows = rows;
+  p.topk = topk;
+  p.E = num_experts;
+  p.count = meta->expert_count;
+  p.offset = meta->expert_offset;
+  p.pair_of_pos = meta->pair_of_pos;
+  p.weight_of_pos = meta->weight_of_pos;
+  p.pos_of_pair = meta->pos_of_pair;
+  p.num_active = meta->num_active;
+  p.status = meta->status;
+  p.do_pack = 1;
+  p.do_plan = 0;
+  return launch_pack(p, (hipStream_t)stream) == hipSuccess ? EXL3_OK : EXL3_E_LAUNCH;
+}
+
+int32_t exl3_moe_forward(const uint16_t *x, int32_t rows, const void *ids, int32_t ids_dtype,
+                         const void *w, int32_t w_dtype, int32_t topk, const exl3_proj *gate,
+                         const exl3_proj *up, const exl3_proj *down, void *out,
+                         int32_t out_dtype, int32_t capacity, int32_t num_active_hint,
+                         void *ws, size_t ws_bytes, void *stream) {
+  (void)num_active_hint;
+  if (rows < 0) return EXL3_E_ARG;
+  if (rows == 0) return EXL3_OK;
+  if (int32_t s = validate_moe_common(x, rows, topk, gate, up, down, out, out_dtype, capacity, ws))
+    return s;
+  if (!ids || !w) return EXL3_E_NULL;
+  if (ids_dtype != EXL3_I32 && ids_dtype != EXL3_I64) return EXL3_E_DTYPE;
+  if (w_dtype != EXL3_F16 && w_dtype != EXL3_BF16 && w_dtype != EXL3_F32) return EXL3_E_DTYPE;
+  if (!aligned16(ids) || !aligned16(w)) return EXL3_E_ALIGN;
+  const int H = gate->in_features, I = gate->out_features, E = gate->num_experts;
+  const MoeLayout L = moe_layout(rows, topk, E, H, I, capacity);
+  if (ws_bytes < L.total) return EXL3_E_WORKSPACE;
+  if (int32_t s = validate_moe_device(x, gate, up, down, out, ws)) return s;
+  for (const void *q : {ids, w})
+    if (int32_t s = check_device(q)) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  PackParams p{};
+  p.ids = ids;
+  p.ids_i64 = ids_dtype == EXL3_I64;
+  p.w = w;
+  p.w_dtype = w_dtype == EXL3_F16 ? 1 : w_dtype == EXL3_BF16 ? 2 : 3;
+  p.rows = rows;
+  p.topk = topk;
+  p.E = E;
+  p.count = at<int32_t>(ws, L.count);
+  p.offset = at<int32_t>(ws, L.offset);
+  p.pair_of_pos = at<int32_t>(ws, L.pair_of_pos);
+  p.weight_of_pos = at<float>(ws, L.weight_of_pos);
+  p.pos_of_pair = at<int32_t>(ws, L.pos_of_pair);
+  p.num_active = at<int32_t>(ws, L.num_active);
+  p.status = at<int32_t>(ws, L.status);
+  p.do_pack = 1;
+  p.do_plan = 1;
+  p.expert_of_pos = at<int32_t>(ws, L.expert_of_pos);
+  p.plan = at<int32_t>(ws, L.plan);
+  p.passes = L.passes;
+  p.capacity = L.cap;
+  p.slots = L.slots;
+  p.bm = kBM;
+  p.out = out;
+  p.out_f32 = out_dtype == EXL3_F32;
+  p.H = H;
+  p.ctrl = at<int32_t>(ws, L.ctrl);
+  if (launch_pack(p, st) != hipSuccess) return EXL3_E_LAUNCH;
+  return run_experts(x, rows, topk, gate, up, down, out, out_dtype, L, ws, p.pair_of_pos,
+                     p.pos_of_pair, p.weight_of_pos, p.offset, st);
+}
+
+int32_t exl3_moe_additive(const uint16_t *x, int32_t rows, int32_t topk,
+                          const exl3_route_meta *meta, const exl3_proj *gate,
+                          const exl3_proj *up, const exl3_proj *down, void *out,
+                          int32_t out_dtype, int32_t capacity, int32_t num_active_hint,
+                          void *ws, size_t ws_bytes, void *stream) {
+  (void)num_active_hint;
+  if (rows < 0) return EXL3_E_ARG;
+  if (rows == 0) return EXL3_OK;
+  if (int32_t s = validate_moe_common(x, rows, topk, gate, up, down, out, out_dtype, capacity, ws))
+    return s;
+  if (!meta) return EXL3_E_NULL;
+  void *mp[] = {meta->expert_offset, meta->pair_of_pos, meta->weight_of_pos, meta->pos_of_pair};
+  for (void *q : mp)
+    if (!q) return EXL3_E_NULL;
+  for (void *q : mp)
+    if (!aligned16(q)) return EXL3_E_ALIGN;
+  const int H = gate->in_features, I = gate->out_features, E = gate->num_experts;
+  const MoeLayout L = moe_layout(rows, topk, E, H, I, capacity);
+  if (ws_bytes < L.total) return EXL3_E_WORKSPACE;
+  if (int32_t s = validate_moe_device(x, gate, up, down, out, ws)) return s;
+  for (void *q : mp)
+    if (int32_t s = check_device(q)) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  PackParams p{};
+  p.rows = rows;
+  p.topk = topk;
+  p.E = E;
+  p.offset = meta->expert_offset;
+  p.pos_of_pair = meta->pos_of_pair;
+  p.do_pack = 0;
+  p.do_plan = 1;
+  p.expert_of_pos = at<int32_t>(ws, L.expert_of_pos);
+  p.plan = at<int32_t>(ws, L.plan);
+  p.passes = L.passes;
+  p.capacity = L.cap;
+  p.slots = L.slots;
+  p.bm = kBM;
+  p.out = out;
+  p.out_f32 = out_dtype == EXL3_F32;
+  p.H = H;
+  p.ctrl = at<int32_t>(ws, L.ctrl);
+  if (launch_pack(p, st) != hipSuccess) return EXL3_E_LAUNCH;
+  return run_experts(x, rows, topk, gate, up, down, out, out_dtype, L, ws, meta->pair_of_pos,
+                     meta->pos_of_pair, meta->weight_of_pos, meta->expert_offset, st);
+}
+
+int32_t exl3_decode_tiles(const uint16_t *words, int32_t ntiles, int32_t K, uint16_t *out,
+                          void *stream) {
+  if (ntiles < 0 || K < 2 || K > 8) return EXL3_E_ARG;
+  if (ntiles == 0) return EXL3_OK;
+  if (!words || !out) return EXL3_E_NULL;
+  if (!aligned16(words) || !aligned16(out)) return EXL3_E_ALIGN;
+  for (const void *q : {(const void *)words, (const void *)out})
+    if (int32_t s = check_device(q)) return s;
+  return launch_decode_tiles(words, ntiles, K, out, (hipStream_t)stream) == hipSuccess
+             ? EXL3_OK
+             : EXL3_E_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Internal launch interface between the C ABI (host.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace exl3 {
+
+enum Epilogue { EPI_LINEAR = 0, EPI_GATEUP = 1, EPI_DOWN = 2 };
+
+struct ProjDev {
+  const int64_t *trellis;  // [S][E] device addresses
+  const float *scale;      // [S][E]
+  const int32_t *bits;     // [S][E]
+  const uint16_t *svh;     // [E][out]
+  const uint16_t *cs;      // [E][out]
+  int num_stages;
+};
+
+struct GemmParams {
+  ProjDev proj[2];  // GATEUP: gate, up; otherwise proj[0]
+  int E, in_f, out_f;
+  // A operand: rotated fp16 rows in kSigma order; row r of projection pj at
+  // A + r * lda + pj * a_proj_stride (elements).
+  const uint16_t *A;
+  int64_t lda, a_proj_stride;
+  // Work tiles. Implicit (linear): tile t = rows [t*BM, min(rows, t*BM+BM)),
+  // expert 0. Plan (MoE): plan_tiles[3*t] = {expert, first row, rows}.
+  int rows;
+  const int32_t *plan_ntiles;
+  const int32_t *plan_tiles;
+  // Epilogue.
+  const uint16_t *suh_down;  // GATEUP: [E][I] (down input signs)
+  uint16_t *out_h;           // GATEUP: a~ [C][I]; LINEAR fp16 output
+  float *out_f32;            // DOWN: d [C][H]; LINEAR fp32 output
+  int64_t ldo;
+  const float *weight_of_pos;  // DOWN
+  int pass_base;               // DOWN: packed position of tile row 0
+  int32_t *ctrl;               // [1] counts bad stage entries
+};
+
+struct RotParams {
+  const uint16_t *x;  // [rows][H] fp16
+  int H, topk;
+  const uint16_t *suh[2];  // [E][H] per projection (suh[1] may be null)
+  int nproj;
+  // MoE mode: item position -> pair/expert via the pack; linear: row = item.
+  const int32_t *pair_of_pos;
+  const int32_t *expert_of_pos;
+  const int32_t *total_valid;  // device: kept pairs
+  int pass_base;
+  int pairs;   // rows * topk (bound for caller-supplied metadata)
+  int nitems;  // positions of this pass (upper bound) or rows
+  uint16_t *xt;  // [nitems][nproj][H]
+  int32_t *ctrl_clear;  // if set, block 0 zeroes ctrl[1] (bad stage entries)
+};
+
+struct CombineParams {
+  int rows, topk, H, pairs;
+  const int32_t *pair_of_pos, *pos_of_pair, *total_valid;
+  int pass_base, pass_end;
+  const float *d;  // [C][H]
+  float *yacc;     // [rows][H]
+  void *out;
+  int out_f32;     // 1: fp32 out, 0: fp16
+};
+
+struct PackParams {
+  // pack inputs (do_pack)
+  const void *ids;
+  int ids_i64;
+  const void *w;
+  int w_dtype;  // 1 f16, 2 bf16, 3 f32
+  int rows, topk, E;
+  // meta (written when do_pack, read otherwise)
+  int32_t *count, *offset, *pair_of_pos, *pos_of_pair, *num_active, *status;
+  float *weight_of_pos;
+  int do_pack, do_plan;
+  // plan outputs
+  int32_t *expert_of_pos;
+  int32_t *plan;  // per pass: [1 + 3 * slots]
+  int passes, capacity, slots, bm;
+  // unrouted rows get zero output
+  void *out;
+  int out_f32, H;
+  int32_t *ctrl;  // [0] dropped pairs, [1] bad stage entries (cleared)
+};
+
+hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks,
+                       hipStream_t s);
+hipError_t launch_rotate(const RotParams &p, hipStream_t s);
+hipError_t launch_combine(const CombineParams &p, int npos, hipStream_t s);
+hipError_t launch_pack(const PackParams &p, hipStream_t s);
+hipError_t launch_decode_tiles(const uint16_t *words, int ntiles, int K,
+                               uint16_t *out, hipStream_t s);
+
+constexpr int kBM = 16;  // rows per GEMM work tile
+
+}  // namespace exl3

@@ -1,0 +1,55 @@
+// Input rotation x~ = fp16_rne(H128(x * suh) / sqrt(128)) for the GEMM A
+// operands, stored in the kSigma k-order the decoded B operands use.
+// exllamav3 PR #284 "MoE: Add fused additive EXL3 kernels" (API contract:
+// each projection's suh/svh rotations, reused by residual stages) and
+// TensorFold PR #837 (What this changes: the input rotation, each expert's
+// rotation for gate and up).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace exl3 {
+
+// One 16-lane group per (item, projection, 128-block); 16 groups per block.
+__global__ void __launch_bounds__(256) rotate_kernel(RotParams p) {
+  const int nblk = p.H >> 7;
+  const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int i = threadIdx.x & 15;
+  if (p.ctrl_clear && blockIdx.x == 0 && threadIdx.x == 0) p.ctrl_clear[1] = 0;
+  const int64_t per_item = (int64_t)p.nproj * nblk;
+  if (gid >= (int64_t)p.nitems * per_item) return;
+  const int item = (int)(gid / per_item);
+  const int rem = (int)(gid - (int64_t)item * per_item);
+  const int pj = rem / nblk, blk = rem - pj * nblk;
+
+  int row, e;
+  if (p.pair_of_pos != nullptr) {
+    const int pos = p.pass_base + item;
+    if (pos >= min(*p.total_valid, p.pairs)) return;  // uniform per group
+    const int q = p.pair_of_pos[pos];
+    if (q < 0 || q >= p.pairs) return;  // inconsistent metadata: drop
+    row = q / p.topk;
+    e = p.expert_of_pos[pos];
+  } else {
+    row = item;
+    e = 0;
+  }
+  const uint16_t *xr = p.x + (int64_t)row * p.H + blk * 128;
+  const uint16_t *sg = p.suh[pj] + (int64_t)e * p.H + blk * 128;
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    v[j] = f16_bits_to_f32(xr[i + 16 * j]) * f16_bits_to_f32(sg[i + 16 * j]);
+  fwht128_group16(v);
+  uint16_t *o = p.xt + ((int64_t)item * p.nproj + pj) * p.H + blk * 128;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[16 * j + sigma_inv(i)] = f32_to_f16_bits(v[j] * kRsqrt128);
+}
+
+hipError_t launch_rotate(const RotParams &p, hipStream_t s) {
+  const int64_t groups = (int64_t)p.nitems * p.nproj * (p.H >> 7);
+  if (groups <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rotate_kernel, dim3((unsigned)((groups + 15) / 16)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace exl3
