@@ -1,0 +1,283 @@
+"""Benchmark of the fused EXL3 routed-experts layer on one MI355X.
+
+A step is one full layer forward (route pack, rotations, gate/up GEMM +
+SwiGLU, down GEMM, ordered combine) over one batch of synthetic input that is
+already resident in HBM. The headline workload is the mixed-width prefill
+layer (192 experts, top-8, hidden 6144, intermediate 2048, K per expert in
+{3,4,5,6,8}, 3072 rows, Zipf(1.2) routing, capacity 2048 pairs). The decode
+layer (128 experts, top-8, hidden 4096, intermediate 1536, K=4) at 1 and 32
+rows is reported alongside, timed by hipGraph replay over rotating routings.
+
+Prints one JSON line. ``--gpus N`` with N > 1 is refused: this build runs on
+one GPU.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("MoE layer µs and tokens/sec at M=1/32/3072; % HBM peak (decode), "
+          "% MFMA (prefill)")
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _kernel_stats(records):
+    st = {}
+    for name, ms in records:
+        s = st.setdefault(name, [0, 0.0])
+        s[0] += 1
+        s[1] += ms
+    return {k: {"launches": n, "total_ms": t, "avg_us": 1000.0 * t / n}
+            for k, (n, t) in st.items()}
+
+
+def prefill_step_flops(wl):
+    P = int(np.sum((wl.ids >= 0) & (wl.ids < wl.num_experts)))
+    H, I = wl.hidden, wl.intermediate
+    return {"gemm_gateup": 2.0 * P * H * 2 * I, "gemm_down": 2.0 * P * I * H}
+
+
+def run_prefill(args, torch, exl3, synth):
+    _log("prefill: drawing inputs")
+    t0 = time.time()
+    wl = synth.moe_workload("prefill", materialize=False)
+    gate, up, down = (exl3.DeviceProj(p, "cuda", words_fn=synth.realize_words)
+                      for p in (wl.gate, wl.up, wl.down))
+    x, ids, w = exl3.device_inputs(wl, "cuda")
+    out = torch.empty(wl.rows, wl.hidden, dtype=torch.float16, device="cuda")
+    need = exl3.moe_workspace_size(wl.rows, wl.topk, wl.num_experts, wl.hidden,
+                                   wl.intermediate, wl.capacity)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    _log("prefill: inputs resident in %.1f s (trellis %.2f GB)" % (
+        time.time() - t0, sum(p.buffer.numel() for p in (gate, up, down)) / 1e9))
+
+    def step():
+        exl3.exl3_moe_forward(x, ids, w, gate, up, down, wl.capacity, out=out, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _log("prefill: warmup done")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    # per-kernel durations measured live over the timed steps (events on the
+    # stream the library launches on)
+    with exl3.Profile(max_launches=64 * args.steps) as prof:
+        torch.cuda.synchronize()
+        t_start.record()
+        for _ in range(args.steps):
+            step()
+        t_stop.record()
+        torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_stop) / args.steps
+    _log("prefill: %.1f us per layer" % (1000 * ms))
+    kstats = _kernel_stats(prof.records)
+    flops = prefill_step_flops(wl)
+    dom = max(("gemm_gateup", "gemm_down"), key=lambda k: kstats[k]["total_ms"])
+    per_launch_flops = flops[dom] / (kstats[dom]["launches"] / args.steps)
+    achieved = per_launch_flops / (kstats[dom]["avg_us"] * 1e-6) / 1e12
+    layer_tflops = (flops["gemm_gateup"] + flops["gemm_down"]) / (ms * 1e-3) / 1e12
+    # algorithmic trellis bytes of one step: every expert with pairs is read
+    # once per row tile of 16 (gate/up) -> report both
+    res = {
+        "ms": ms, "tokens_per_s": wl.rows / (ms * 1e-3), "kernels": kstats,
+        "dominant": dom, "per_launch_flops": per_launch_flops,
+        "achieved_tflops": achieved, "layer_tflops": layer_tflops,
+        "layer_mfma_frac": layer_tflops / MFMA_F16_PEAK_TFLOPS,
+        "passes": exl3.moe_layout(wl.rows, wl.topk, wl.num_experts, wl.hidden,
+                                  wl.intermediate, wl.capacity).passes,
+    }
+    return wl, res
+
+
+def run_decode(args, torch, exl3, synth, M, groups=16):
+    wl = synth.moe_workload("decode", rows=M)
+    gate, up, down = (exl3.DeviceProj(p, "cuda") for p in (wl.gate, wl.up, wl.down))
+    x, _, _ = exl3.device_inputs(wl, "cuda")
+    routings = []
+    for gi in range(groups):
+        ids, wb = synth.routes("uniform", 1000 + gi, M, wl.num_experts, wl.topk, "bf16")
+        it = torch.from_numpy(ids.astype(np.int64)).cuda()
+        wt = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).cuda()
+        routings.append((ids, it, wt))
+    out = torch.empty(M, wl.hidden, dtype=torch.float16, device="cuda")
+    need = exl3.moe_workspace_size(M, wl.topk, wl.num_experts, wl.hidden, wl.intermediate,
+                                   M * wl.topk)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def call(r):
+        exl3.exl3_moe_forward(x, r[1], r[2], gate, up, down, M * wl.topk, out=out, ws=ws)
+
+    for r in routings:
+        call(r)
+    torch.cuda.synchronize()
+    # one captured graph per routing: replays stream different experts
+    graphs = []
+    side = torch.cuda.Stream()
+    for r in routings:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side, capture_error_mode="relaxed"):
+            call(r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    steps = max(args.steps, 4 * groups)
+    for i in range(groups):
+        graphs[i].replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        graphs[i % groups].replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    # per-kernel durations from eager launches over the same routings
+    with exl3.Profile(max_launches=16 * groups * 4) as prof:
+        for _ in range(4):
+            for r in routings:
+                call(r)
+        torch.cuda.synchronize()
+    kst = _kernel_stats(prof.records)
+    # algorithmic HBM bytes of the gate/up GEMM: the trellis of every active
+    # expert's gate and up projection (read once: <= 16 pairs per expert),
+    # plus its rotated inputs and a~ outputs
+    per_tensor = wl.hidden * wl.intermediate * 4 // 8
+    act = [len(np.unique(r[0])) for r in routings]
+    gu_bytes = np.mean([2 * per_tensor * n for n in act]) + M * wl.topk * (
+        2 * wl.hidden * 2 + wl.intermediate * 2)
+    dn_bytes = np.mean([per_tensor * n for n in act]) + M * wl.topk * (
+        wl.intermediate * 2 + wl.hidden * 4)
+    layer_bytes = gu_bytes + dn_bytes
+    return {
+        "rows": M, "us": 1000 * ms, "tokens_per_s": M / (ms * 1e-3), "graph_replays": steps,
+        "kernels": kst,
+        "gemm_gateup_GBps": gu_bytes / (kst["gemm_gateup"]["avg_us"] * 1e-6) / 1e9,
+        "gemm_down_GBps": dn_bytes / (kst["gemm_down"]["avg_us"] * 1e-6) / 1e9,
+        "layer_GBps": layer_bytes / (ms * 1e-3) / 1e9,
+        "layer_hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes": {"gemm_gateup": gu_bytes, "gemm_down": dn_bytes},
+    }
+
+
+def cpu_baseline(wl, synth):
+    """The float64 oracle on a bounded sample of the prefill workload: the
+    first two routed pairs of row 0 through the whole layer (expert
+    dequantisation included), scaled to one token (top-8)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import moe as omoe
+    from oracle.linear import WeightCache
+
+    r = 0
+    pairs = [(r, j, int(wl.ids[r, j])) for j in range(2)]
+    experts = {e for _, _, e in pairs}
+    views = [synth.materialized_view(p, experts) for p in (wl.gate, wl.up, wl.down)]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        cache = WeightCache()
+        for _, j, e in pairs:
+            at = omoe.stage1(wl.x[r:r + 1].astype(np.float64), e, *views, "R", cache)
+            omoe.down_output(at, e, views[2], cache)
+        dt = time.perf_counter() - t0
+    per_token = dt * wl.topk / len(pairs)
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "prefill workload, row 0, its first 2 of 8 routed pairs through the "
+                      "float64 oracle (dequantisation included): %.1f s, scaled x4 to one "
+                      "token" % dt}
+
+
+def copy_probe(torch, gib=1.0, reps=5):
+    """Plain device copy of known size, used to calibrate HBM counters."""
+    n = int(gib * (1 << 30))
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode extras")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="JSON with measured HBM bytes per launch of the dominant kernel")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d refused)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from trellis_quantized_moe_amd import exl3, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    exl3.lib()
+    if args.copy_probe:
+        copy_probe(torch)
+        return
+
+    wl, pre = run_prefill(args, torch, exl3, synth)
+    extra = {"prefill": pre}
+    if not args.no_decode:
+        for M in (1, 32):
+            _log("decode M=%d" % M)
+            extra["decode_M%d" % M] = run_decode(args, torch, exl3, synth, M)
+
+    dom = pre["dominant"]
+    traffic = None
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            t = json.load(f)
+        if t.get("kernel") == dom and t.get("workload") == "prefill":
+            traffic = t.get("bytes_per_launch")
+    roof = {"bound": "mfma", "kernel": dom, "achieved": pre["achieved_tflops"],
+            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": pre["achieved_tflops"] / MFMA_F16_PEAK_TFLOPS, "traffic": traffic,
+            "per_launch": "%.4g flops (2 x pairs_in_pass x in x out summed over the "
+                          "projections of the launch)" % pre["per_launch_flops"]}
+    cpu = None
+    if not args.no_cpu:
+        _log("cpu baseline (oracle)")
+        cpu = cpu_baseline(wl, synth)
+
+    line = {
+        "metric": METRIC, "value": pre["tokens_per_s"], "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": pre["ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "prefill MoE layer: 192 experts, top-8, hidden 6144, "
+                               "intermediate 2048, K per expert in {3,4,5,6,8}, 3072 rows, "
+                               "Zipf(1.2) routing, capacity 2048 pairs",
+                   "global_batch": wl.rows, "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

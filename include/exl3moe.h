@@ -60,7 +60,10 @@ enum exl3_status {
   EXL3_E_DTYPE = -2,     /* unsupported dtype enum for that argument */
   EXL3_E_SHAPE = -3,     /* dimension not a positive multiple of 128, or
                             gate/up/down shapes inconsistent */
-  EXL3_E_ALIGN = -4,     /* a pointer is not 16-byte aligned */
+  EXL3_E_ALIGN = -4,     /* x, out, ws, trellis tensors and projection
+                            tables must be 16-byte aligned; ids, route
+                            weights and route metadata need the natural
+                            alignment of their element type */
   EXL3_E_DEVICE = -5,    /* a pointer is not device memory of the current
                             device, or no HIP device is usable */
   EXL3_E_WORKSPACE = -6, /* workspace NULL or smaller than *_workspace_size */
@@ -229,6 +232,24 @@ int32_t exl3_moe_layout(int32_t rows, int32_t topk, int32_t num_experts,
  */
 int32_t exl3_decode_tiles(const uint16_t *words, int32_t ntiles, int32_t K,
                           uint16_t *out, void *stream);
+
+/*
+ * Diagnostic per-launch timing (host). exl3_profile_begin() creates
+ * 2 * max_launches hipEvents (so it allocates: call it outside timed or
+ * captured regions); while active, every kernel the library launches is
+ * bracketed by an event pair on its stream (the first max_launches
+ * launches). exl3_profile_end() waits for those events, writes up to `cap`
+ * (kernel id, milliseconds) pairs to the host arrays, frees the events and
+ * returns the number of recorded launches (or a negative status). Not for
+ * use during graph capture; not thread-safe.
+ */
+enum exl3_kernel_id {
+  EXL3_K_PACK = 1, EXL3_K_ROTATE = 2, EXL3_K_GATEUP = 3, EXL3_K_DOWN = 4,
+  EXL3_K_COMBINE = 5, EXL3_K_LINEAR = 6, EXL3_K_DECODE = 7
+};
+int32_t exl3_profile_begin(int32_t max_launches);
+int32_t exl3_profile_end(int32_t *kernel_ids /* host */, float *ms /* host */,
+                         int32_t cap);
 
 #ifdef __cplusplus
 }

@@ -257,3 +257,53 @@ def test_additive_workload_sampled():
     _say("additive workload")
     wl = synth.moe_workload("additive")
     assert _sampled_parity(wl, [3], 1024) <= TOL
+
+
+# ------------------------------------------------ wide (128-row) MoE tiles
+def _wide_wl(rows=300):
+    # pairs >= 64 * experts selects 128-row tiles
+    return synth.moe_workload("tiny", rows=rows, topk=2, E=4, H=256, I=384, K=(3, 5, 8))
+
+
+def test_moe_wide_tiles_parity():
+    wl = _wide_wl()
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    y = exl3.exl3_moe_forward(x, ids, w, gate, up, down, 10 ** 6, torch.float32)
+    torch.cuda.synchronize()
+    ref = omoe.moe_forward(wl.x, wl.ids, wl.weights_f64, wl.gate, wl.up, wl.down, "R")
+    assert _rel_err(y.cpu().double().numpy(), ref) <= TOL
+
+
+def test_moe_wide_equals_narrow_rows():
+    """The same rows through 128-row tiles (many rows) and 16-row tiles (few
+    rows): identical bytes."""
+    wl = _wide_wl()
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    full = exl3.exl3_moe_forward(x, ids, w, gate, up, down, 10 ** 6, torch.float32)
+    for r0, r1 in ((0, 3), (100, 117), (290, 300)):
+        part = exl3.exl3_moe_forward(x[r0:r1], ids[r0:r1], w[r0:r1], gate, up, down,
+                                     10 ** 6, torch.float32)
+        assert torch.equal(part.view(torch.int32), full[r0:r1].view(torch.int32)), (r0, r1)
+
+
+def test_moe_wide_capacity_invariance():
+    wl = _wide_wl()
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    base = exl3.exl3_moe_forward(x, ids, w, gate, up, down, 10 ** 6, torch.float32)
+    for cap in (1, 100, 128, 129, 257, 599):
+        _say("wide capacity", cap)
+        y = exl3.exl3_moe_forward(x, ids, w, gate, up, down, cap, torch.float32)
+        assert torch.equal(y.view(torch.int32), base.view(torch.int32)), cap
+
+
+def test_linear_wide_multistage_parity():
+    # 1024 rows x 8192 out selects 128-row tiles; three stages, one zero
+    p, x = _linear_case(256, 8192, ((3, 1.0), (2, 0.25), (4, 0.0)), 1024, seed=9)
+    dp = exl3.DeviceProj(p, DEV)
+    xd = exl3.f16_tensor(x)
+    y = exl3.exl3_linear(xd, dp, torch.float32)
+    y_small = exl3.exl3_linear(xd[:5], dp, torch.float32)
+    torch.cuda.synchronize()
+    ref = olinear.linear(x[[0, 4, 1023]], p, "R")
+    assert _rel_err(y.cpu().double().numpy()[[0, 4, 1023]], ref) <= TOL
+    assert torch.equal(y_small.view(torch.int32), y[:5].view(torch.int32))

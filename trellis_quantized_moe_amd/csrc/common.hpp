@@ -141,6 +141,26 @@ __device__ __forceinline__ void decode_column(const uint32_t (&raw)[Geom<K>::kLo
 #undef EXL3_DECODE_REG
 }
 
+// Wave index as a scalar: lets the compiler keep every per-wave value (and
+// the buffer resources built from them) in SGPRs.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// Loads of per-workgroup / per-wave table entries, forced into SGPRs.
+__device__ __forceinline__ int uload_i32(const int32_t *a) {
+  return __builtin_amdgcn_readfirstlane(*a);
+}
+__device__ __forceinline__ float uload_f32(const float *a) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, *a)));
+}
+__device__ __forceinline__ const uint32_t *uload_ptr(const int64_t *a) {
+  const int64_t v = *a;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (const uint32_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // -------------------------------------------------------------------- MFMA
 // D[16x16] += A[16x32] * B[32x16], fp16 inputs, fp32 accumulate. Lane l
 // supplies A row (l & 15) and B column (l & 15), 8 k-entries each for the

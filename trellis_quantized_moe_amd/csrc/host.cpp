@@ -17,10 +17,42 @@ using namespace exl3;
 
 namespace {
 
+// ------------------------------------------------------------- profiling
+// Optional per-launch timing: when active, every kernel launch is bracketed
+// by two hipEvents on its stream. Off by default; begin/end allocate and free
+// the events (never inside a product call).
+struct Profiler {
+  bool on = false;
+  int cap = 0, n = 0;
+  hipEvent_t *ev = nullptr;
+  int32_t *kid = nullptr;
+} g_prof;
+
+struct ProfScope {
+  hipStream_t s;
+  int slot = -1;
+  int32_t id;
+  ProfScope(hipStream_t st, int32_t kernel_id) : s(st), id(kernel_id) {
+    if (g_prof.on && g_prof.n < g_prof.cap) {
+      slot = g_prof.n++;
+      g_prof.kid[slot] = id;
+      (void)hipEventRecord(g_prof.ev[2 * slot], s);
+    }
+  }
+  ~ProfScope() {
+    if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
+  }
+};
+
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned_to(const void *p, unsigned a) { return ((uintptr_t)p & (a - 1)) == 0; }
+// ids / route weights / metadata arrays are read element by element: their
+// natural alignment is enough.
+unsigned ids_align(int32_t t) { return t == EXL3_I64 ? 8u : 4u; }
+unsigned w_align(int32_t t) { return t == EXL3_F32 ? 4u : 2u; }
 
 // Device residency: the pointer must be device (or managed) memory of the
 // current device. Called only after every host-side check passed.
@@ -113,6 +145,15 @@ MoeLayout moe_layout(int32_t rows, int32_t topk, int32_t E, int32_t H, int32_t I
   return L;
 }
 
+// Tile shape choice (never changes results: both tile shapes run the same
+// per-element MFMA chain and the same epilogue code). Wide 128-row tiles pay
+// off once expert spans average 64+ rows; otherwise 16-row tiles keep the
+// machine full at decode sizes.
+bool moe_wide(int64_t pairs, int E) { return pairs >= 64 * (int64_t)E; }
+bool linear_wide(int rows, int out) {
+  return (int64_t)((rows + kBMWide - 1) / kBMWide) * ((out + 255) / 256) >= 256;
+}
+
 template <typename T>
 T *at(void *ws, size_t off) {
   return (T *)((char *)ws + off);
@@ -160,10 +201,12 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
   const int64_t P = (int64_t)rows * topk;
   const int32_t *total_valid = offset + E;
   int32_t *ctrl = at<int32_t>(ws, L.ctrl);
+  const bool wide = moe_wide(P, E);
+  const int bm = wide ? kBMWide : kBM;
   for (int pass = 0; pass < L.passes; ++pass) {
     const int pb = pass * L.cap;
     const int npos = (int)std::min<int64_t>(L.cap, P - pb);
-    const int tiles = std::min(E, npos) + (npos + kBM - 1) / kBM;
+    const int tiles = std::min(E, npos) + (npos + bm - 1) / bm;
     const int32_t *plan = at<int32_t>(ws, L.plan) + (size_t)pass * (1 + 3 * (size_t)L.slots);
 
     RotParams rp{};
@@ -181,7 +224,10 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     rp.nitems = npos;
     rp.xt = at<uint16_t>(ws, L.xt);
     rp.ctrl_clear = nullptr;
-    if (launch_rotate(rp, st) != hipSuccess) return EXL3_E_LAUNCH;
+    {
+      ProfScope ps(st, EXL3_K_ROTATE);
+      if (launch_rotate(rp, st) != hipSuccess) return EXL3_E_LAUNCH;
+    }
 
     GemmParams g{};
     g.proj[0] = to_dev(gate);
@@ -198,7 +244,10 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     g.out_h = at<uint16_t>(ws, L.at);
     g.ldo = I;
     g.ctrl = ctrl;
-    if (launch_gemm(EPI_GATEUP, g, tiles, I / 128, st) != hipSuccess) return EXL3_E_LAUNCH;
+    {
+      ProfScope ps(st, EXL3_K_GATEUP);
+      if (launch_gemm(EPI_GATEUP, g, tiles, I / 128, st, wide) != hipSuccess) return EXL3_E_LAUNCH;
+    }
 
     GemmParams dn{};
     dn.proj[0] = to_dev(down);
@@ -214,7 +263,11 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     dn.weight_of_pos = weight_of_pos;
     dn.pass_base = pb;
     dn.ctrl = ctrl;
-    if (launch_gemm(EPI_DOWN, dn, tiles, H / 128, st) != hipSuccess) return EXL3_E_LAUNCH;
+    {
+      ProfScope ps(st, EXL3_K_DOWN);
+      const int nbd = wide ? (H + 255) / 256 : H / 128;
+      if (launch_gemm(EPI_DOWN, dn, tiles, nbd, st, wide) != hipSuccess) return EXL3_E_LAUNCH;
+    }
 
     CombineParams cp{};
     cp.rows = rows;
@@ -230,7 +283,10 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     cp.yacc = at<float>(ws, L.yacc);
     cp.out = out;
     cp.out_f32 = out_dtype == EXL3_F32;
-    if (launch_combine(cp, npos, st) != hipSuccess) return EXL3_E_LAUNCH;
+    {
+      ProfScope ps(st, EXL3_K_COMBINE);
+      if (launch_combine(cp, npos, st) != hipSuccess) return EXL3_E_LAUNCH;
+    }
   }
   return EXL3_OK;
 }
@@ -288,7 +344,10 @@ int32_t exl3_linear(const uint16_t *x, int32_t rows, const exl3_proj *proj, void
   rp.nitems = rows;
   rp.xt = xt;
   rp.ctrl_clear = ctrl;
-  if (launch_rotate(rp, st) != hipSuccess) return EXL3_E_LAUNCH;
+  {
+    ProfScope ps(st, EXL3_K_ROTATE);
+    if (launch_rotate(rp, st) != hipSuccess) return EXL3_E_LAUNCH;
+  }
 
   GemmParams g{};
   g.proj[0] = to_dev(proj);
@@ -302,9 +361,13 @@ int32_t exl3_linear(const uint16_t *x, int32_t rows, const exl3_proj *proj, void
   if (out_dtype == EXL3_F32) g.out_f32 = (float *)out;
   else g.out_h = (uint16_t *)out;
   g.ctrl = ctrl;
-  if (launch_gemm(EPI_LINEAR, g, (rows + kBM - 1) / kBM, proj->out_features / 128, st) !=
-      hipSuccess)
-    return EXL3_E_LAUNCH;
+  ProfScope ps(st, EXL3_K_LINEAR);
+  const int fo = proj->out_features;
+  const bool wide = linear_wide(rows, fo);
+  const hipError_t le =
+      wide ? launch_gemm(EPI_LINEAR, g, (rows + kBMWide - 1) / kBMWide, (fo + 255) / 256, st, true)
+           : launch_gemm(EPI_LINEAR, g, (rows + kBM - 1) / kBM, fo / 128, st, false);
+  if (le != hipSuccess) return EXL3_E_LAUNCH;
   return EXL3_OK;
 }
 
@@ -354,10 +417,10 @@ int32_t exl3_route_pack(const void *ids, int32_t ids_dtype, const void *w, int32
                 meta->weight_of_pos, meta->pos_of_pair, meta->num_active, meta->status};
   for (void *q : mp)
     if (!q) return EXL3_E_NULL;
-  for (const void *q : {ids, w})
-    if (!aligned16(q)) return EXL3_E_ALIGN;
+  if (!aligned_to(ids, ids_align(ids_dtype)) || !aligned_to(w, w_align(w_dtype)))
+    return EXL3_E_ALIGN;
   for (void *q : mp)
-    if (!aligned16(q)) return EXL3_E_ALIGN;
+    if (!aligned_to(q, 4)) return EXL3_E_ALIGN;
   for (const void *q : {ids, w})
     if (int32_t s = check_device(q)) return s;
   for (void *q : mp)
@@ -380,6 +443,7 @@ int32_t exl3_route_pack(const void *ids, int32_t ids_dtype, const void *w, int32
   p.status = meta->status;
   p.do_pack = 1;
   p.do_plan = 0;
+  ProfScope ps((hipStream_t)stream, EXL3_K_PACK);
   return launch_pack(p, (hipStream_t)stream) == hipSuccess ? EXL3_OK : EXL3_E_LAUNCH;
 }
 
@@ -396,7 +460,8 @@ int32_t exl3_moe_forward(const uint16_t *x, int32_t rows, const void *ids, int32
   if (!ids || !w) return EXL3_E_NULL;
   if (ids_dtype != EXL3_I32 && ids_dtype != EXL3_I64) return EXL3_E_DTYPE;
   if (w_dtype != EXL3_F16 && w_dtype != EXL3_BF16 && w_dtype != EXL3_F32) return EXL3_E_DTYPE;
-  if (!aligned16(ids) || !aligned16(w)) return EXL3_E_ALIGN;
+  if (!aligned_to(ids, ids_align(ids_dtype)) || !aligned_to(w, w_align(w_dtype)))
+    return EXL3_E_ALIGN;
   const int H = gate->in_features, I = gate->out_features, E = gate->num_experts;
   const MoeLayout L = moe_layout(rows, topk, E, H, I, capacity);
   if (ws_bytes < L.total) return EXL3_E_WORKSPACE;
@@ -427,12 +492,15 @@ int32_t exl3_moe_forward(const uint16_t *x, int32_t rows, const void *ids, int32
   p.passes = L.passes;
   p.capacity = L.cap;
   p.slots = L.slots;
-  p.bm = kBM;
+  p.bm = moe_wide((int64_t)rows * topk, E) ? kBMWide : kBM;
   p.out = out;
   p.out_f32 = out_dtype == EXL3_F32;
   p.H = H;
   p.ctrl = at<int32_t>(ws, L.ctrl);
-  if (launch_pack(p, st) != hipSuccess) return EXL3_E_LAUNCH;
+  {
+    ProfScope ps(st, EXL3_K_PACK);
+    if (launch_pack(p, st) != hipSuccess) return EXL3_E_LAUNCH;
+  }
   return run_experts(x, rows, topk, gate, up, down, out, out_dtype, L, ws, p.pair_of_pos,
                      p.pos_of_pair, p.weight_of_pos, p.offset, st);
 }
@@ -452,7 +520,7 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t rows, int32_t topk,
   for (void *q : mp)
     if (!q) return EXL3_E_NULL;
   for (void *q : mp)
-    if (!aligned16(q)) return EXL3_E_ALIGN;
+    if (!aligned_to(q, 4)) return EXL3_E_ALIGN;
   const int H = gate->in_features, I = gate->out_features, E = gate->num_experts;
   const MoeLayout L = moe_layout(rows, topk, E, H, I, capacity);
   if (ws_bytes < L.total) return EXL3_E_WORKSPACE;
@@ -474,12 +542,15 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t rows, int32_t topk,
   p.passes = L.passes;
   p.capacity = L.cap;
   p.slots = L.slots;
-  p.bm = kBM;
+  p.bm = moe_wide((int64_t)rows * topk, E) ? kBMWide : kBM;
   p.out = out;
   p.out_f32 = out_dtype == EXL3_F32;
   p.H = H;
   p.ctrl = at<int32_t>(ws, L.ctrl);
-  if (launch_pack(p, st) != hipSuccess) return EXL3_E_LAUNCH;
+  {
+    ProfScope ps(st, EXL3_K_PACK);
+    if (launch_pack(p, st) != hipSuccess) return EXL3_E_LAUNCH;
+  }
   return run_experts(x, rows, topk, gate, up, down, out, out_dtype, L, ws, meta->pair_of_pos,
                      meta->pos_of_pair, meta->weight_of_pos, meta->expert_offset, st);
 }
@@ -492,9 +563,50 @@ int32_t exl3_decode_tiles(const uint16_t *words, int32_t ntiles, int32_t K, uint
   if (!aligned16(words) || !aligned16(out)) return EXL3_E_ALIGN;
   for (const void *q : {(const void *)words, (const void *)out})
     if (int32_t s = check_device(q)) return s;
+  ProfScope ps((hipStream_t)stream, EXL3_K_DECODE);
   return launch_decode_tiles(words, ntiles, K, out, (hipStream_t)stream) == hipSuccess
              ? EXL3_OK
              : EXL3_E_LAUNCH;
+}
+
+int32_t exl3_profile_begin(int32_t max_launches) {
+  if (g_prof.on || max_launches < 1 || max_launches > (1 << 20)) return EXL3_E_ARG;
+  g_prof.ev = new hipEvent_t[2 * (size_t)max_launches];
+  g_prof.kid = new int32_t[max_launches];
+  for (int i = 0; i < 2 * max_launches; ++i) {
+    if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_prof.ev[j]);
+      delete[] g_prof.ev;
+      delete[] g_prof.kid;
+      g_prof = Profiler{};
+      return EXL3_E_DEVICE;
+    }
+  }
+  g_prof.cap = max_launches;
+  g_prof.n = 0;
+  g_prof.on = true;
+  return EXL3_OK;
+}
+
+int32_t exl3_profile_end(int32_t *kernel_ids, float *ms, int32_t cap) {
+  if (!g_prof.on) return EXL3_E_ARG;
+  const int n = g_prof.n;
+  int32_t status = n;
+  for (int i = 0; i < n; ++i) {
+    float t = -1.0f;
+    if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&t, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess)
+      status = EXL3_E_DEVICE;
+    if (i < cap) {
+      if (kernel_ids) kernel_ids[i] = g_prof.kid[i];
+      if (ms) ms[i] = t;
+    }
+  }
+  for (int i = 0; i < 2 * g_prof.cap; ++i) (void)hipEventDestroy(g_prof.ev[i]);
+  delete[] g_prof.ev;
+  delete[] g_prof.kid;
+  g_prof = Profiler{};
+  return status;
 }
 
 }  // extern "C"

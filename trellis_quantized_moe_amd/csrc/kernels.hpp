@@ -87,13 +87,14 @@ struct PackParams {
 };
 
 hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks,
-                       hipStream_t s);
+                       hipStream_t s, bool wide);
 hipError_t launch_rotate(const RotParams &p, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int npos, hipStream_t s);
 hipError_t launch_pack(const PackParams &p, hipStream_t s);
 hipError_t launch_decode_tiles(const uint16_t *words, int ntiles, int K,
                                uint16_t *out, hipStream_t s);
 
-constexpr int kBM = 16;  // rows per GEMM work tile
+constexpr int kBM = 16;       // rows per narrow GEMM work tile
+constexpr int kBMWide = 128;  // rows per wide GEMM work tile
 
 }  // namespace exl3

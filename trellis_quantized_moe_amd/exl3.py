@@ -64,7 +64,12 @@ _SIGS = {
                                  _vp]),
     "exl3_moe_layout": (_i32, [_i32] * 6 + [ctypes.POINTER(LayoutC)]),
     "exl3_decode_tiles": (_i32, [_vp, _i32, _i32, _vp, _vp]),
+    "exl3_profile_begin": (_i32, [_i32]),
+    "exl3_profile_end": (_i32, [ctypes.POINTER(ctypes.c_int32),
+                                ctypes.POINTER(ctypes.c_float), _i32]),
 }
+KERNEL_NAMES = {1: "route_pack", 2: "rotate", 3: "gemm_gateup", 4: "gemm_down",
+                5: "combine", 6: "gemm_linear", 7: "decode_tiles"}
 
 
 def lib():
@@ -268,6 +273,29 @@ def unpermute_rotated(t):
     out = torch.empty_like(g)
     out[..., sigma] = g
     return out.reshape(shape)
+
+
+class Profile:
+    """Per-launch kernel timing through the library's event hooks:
+    ``with Profile(n) as p: ...`` then ``p.records`` = [(name, ms), ...]."""
+
+    def __init__(self, max_launches=4096):
+        self.max = max_launches
+        self.records = []
+
+    def __enter__(self):
+        _check(lib().exl3_profile_begin(self.max))
+        return self
+
+    def __exit__(self, *exc):
+        ids = (ctypes.c_int32 * self.max)()
+        ms = (ctypes.c_float * self.max)()
+        n = lib().exl3_profile_end(ids, ms, self.max)
+        if n < 0:
+            _check(n)
+        self.records = [(KERNEL_NAMES.get(ids[i], str(ids[i])), float(ms[i]))
+                        for i in range(min(n, self.max))]
+        return False
 
 
 def device_inputs(wl, device="cuda"):

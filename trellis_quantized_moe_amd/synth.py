@@ -197,6 +197,14 @@ def _cast_weights(w, dtype):
     return w.astype(np.float32)
 
 
+def routes(kind, seed, rows, E, topk, wdtype, idtype=np.int64):
+    """Only the routing of a workload: (ids, raw weights) for a fresh seed."""
+    router = {"uniform": _uniform_routes, "logit": _logit_routes,
+              "zipf": _zipf_routes}[kind]
+    ids, w = router(seed, rows, E, topk)
+    return ids.astype(idtype), _cast_weights(w, wdtype)
+
+
 def moe_workload(name, rows=None, seed=None, capacity=None, materialize=True,
                  **over):
     """Build one of the MoE workloads (tiny, decode, prefill, additive),
