@@ -32,36 +32,44 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineParams p) {
   }
   if (owner != pos) return;
 
-  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
-  if (c >= p.H) return;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (!first) acc = *(const f32x4 *)(p.yacc + (int64_t)r * p.H + c);
-  int prev = -1;
-  for (;;) {  // ascending positions of this row inside the pass
-    int nxt = 0x7fffffff;
-    for (int j = 0; j < p.topk; ++j) {
-      const int q = spos[j];
-      if (q > prev && q >= p.pass_base && q < end) nxt = min(nxt, q);
+  // this row's positions inside the pass, ascending (at most topk <= 32)
+  __shared__ int order[32];
+  __shared__ int s_cnt;
+  if (threadIdx.x == 0) {
+    int cnt = 0;
+    for (int prev = -1;;) {
+      int nxt = 0x7fffffff;
+      for (int j = 0; j < p.topk; ++j) {
+        const int q = spos[j];
+        if (q > prev && q >= p.pass_base && q < end) nxt = min(nxt, q);
+      }
+      if (nxt == 0x7fffffff) break;
+      order[cnt++] = nxt - p.pass_base;
+      prev = nxt;
     }
-    if (nxt == 0x7fffffff) break;
-    const f32x4 d = *(const f32x4 *)(p.d + (int64_t)(nxt - p.pass_base) * p.H + c);
-    acc += d;
-    prev = nxt;
+    s_cnt = cnt;
   }
-  if (!last) {
-    *(f32x4 *)(p.yacc + (int64_t)r * p.H + c) = acc;
-  } else if (p.out_f32) {
-    *(f32x4 *)((float *)p.out + (int64_t)r * p.H + c) = acc;
-  } else {
-    uint16_t *o = (uint16_t *)p.out + (int64_t)r * p.H + c;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = f32_to_f16_bits(acc[k]);
+  __syncthreads();
+  const int cnt = s_cnt;
+  for (int c = threadIdx.x * 4; c < p.H; c += 256 * 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (!first) acc = *(const f32x4 *)(p.yacc + (int64_t)r * p.H + c);
+    for (int k = 0; k < cnt; ++k) acc += *(const f32x4 *)(p.d + (int64_t)order[k] * p.H + c);
+    if (!last) {
+      *(f32x4 *)(p.yacc + (int64_t)r * p.H + c) = acc;
+    } else if (p.out_f32) {
+      *(f32x4 *)((float *)p.out + (int64_t)r * p.H + c) = acc;
+    } else {
+      const uint32_t lo = (uint32_t)f32_to_f16_bits(acc[0]) | ((uint32_t)f32_to_f16_bits(acc[1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_f16_bits(acc[2]) | ((uint32_t)f32_to_f16_bits(acc[3]) << 16);
+      *(uint2 *)((uint16_t *)p.out + (int64_t)r * p.H + c) = make_uint2(lo, hi);
+    }
   }
 }
 
 hipError_t launch_combine(const CombineParams &p, int npos, hipStream_t s) {
   if (npos <= 0) return hipSuccess;
-  const dim3 grid(npos, (p.H + 1023) / 1024);
+  const dim3 grid(npos);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }

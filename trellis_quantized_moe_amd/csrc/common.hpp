@@ -200,6 +200,33 @@ __device__ __forceinline__ void fwht128_group16(float (&v)[8]) {
   }
 }
 
+// Unnormalised 128-point FWHT with 8 consecutive entries per lane: lane i of
+// the 16-lane group holds entries 8i..8i+7. Distances 1, 2, 4 in registers,
+// then 8..64 across lanes (xor 1..8). Used for the input rotation only.
+__device__ __forceinline__ void fwht128_lane8(float (&v)[8]) {
+  const int i = threadIdx.x & 15;
+#pragma unroll
+  for (int d = 1; d < 8; d <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if ((j & d) == 0) {
+        const float lo = v[j], hi = v[j + d];
+        v[j] = lo + hi;
+        v[j + d] = lo - hi;
+      }
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) {
+    const bool upper = (i & d) != 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float o = __shfl_xor(v[j], d, 64);
+      v[j] = upper ? (o - v[j]) : (v[j] + o);
+    }
+  }
+}
+
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);  // RNE
 }

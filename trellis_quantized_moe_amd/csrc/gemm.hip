@@ -281,12 +281,14 @@ __global__ void __launch_bounds__(EPI == EPI_GATEUP ? 1024 : 512)
 // (4 strips) over all 128 rows (8 MFMA row blocks). GATEUP: waves 0-1 gate,
 // 2-3 up (128 columns each); otherwise 256 consecutive output columns.
 //
-// Pipeline: the A rows and the trellis words of a 64-input k-block are
-// copied global->LDS by the DMA form of the global loads into a ring of
-// kRing buffers, kRing-1 k-blocks ahead of the k-block being decoded and
-// multiplied. The wait for a k-block is an exact vmcnt (every wave issues the
-// same number of DMAs per k-block; tails re-issue the last k-block), followed
-// by a barrier, so loads stay in flight across iterations.
+// Software pipeline over 64-input k-blocks. A rows and trellis words are
+// copied global->LDS by DMA (SGPR base + per-lane offset) into rings of
+// three buffers: at k-block kb a wave issues A[kb+2] and T[kb+3], multiplies
+// A[kb] by the B operands decoded one iteration earlier, and meanwhile
+// decodes T[kb+1] into the other B register set. Every wave issues the same
+// number of DMAs per iteration (tails re-copy the last k-block), so the wait
+// for the data of iteration kb is an exact vmcnt with one iteration of DMAs
+// still in flight, followed by one barrier.
 constexpr int kWBM = 128;
 constexpr int kRing = 3;
 constexpr int kAbuf = 128 * 128;        // bytes: one projection's A k-block
@@ -303,22 +305,27 @@ struct WideLds {
   static constexpr int kTOff = kRing * NPROJ * kAbuf;
   static constexpr int kRingBytes = kTOff + kRing * kTbuf;
   static constexpr int kBytes = kTileBytes > kRingBytes ? kTileBytes : kRingBytes;
-  static constexpr int kDmaPerKb = NPROJ * 16 / 4 + 4;  // per wave: A chunks + strips
+  static constexpr int kAChunks = NPROJ * 16 / 4;  // 1 KB A chunks per wave per k-block
+  static constexpr int kDmaPerIter = kAChunks + 4;
 };
 
-// One 16-byte-per-lane global->LDS DMA: lane L writes lds_base + 16 L.
-// m0 is saved and restored around the copy.
-__device__ __forceinline__ void dma16(const void *gaddr, uint32_t lds_base) {
-  uint32_t saved;
+// 16-byte-per-lane global->LDS copy: lane L reads sbase + voff and writes
+// LDS byte m0 + 16 L. The wave's LDS destination goes through m0.
+__device__ __forceinline__ void dma16(uint32_t voff, const void *sbase, uint32_t lds_base) {
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gaddr), "s"(lds_base)
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_base)
       : "memory");
+}
+
+__device__ __forceinline__ const char *uniform_ptr(const char *ptr) {
+  const uint64_t b = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  return (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 template <int N>
@@ -327,89 +334,230 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Column window of lane column n for width K: dword indices and bit shift.
 template <int K>
-__device__ __forceinline__ void decode_lds(const char *tbase, const int (&idx)[5], uint32_t shift,
-                                           uint32_t mask, uint32_t (&w)[8]) {
-  uint32_t r[Geom<K>::kLoadDw];
-#pragma unroll
-  for (int j = 0; j < Geom<K>::kLoadDw; ++j) r[j] = *(const uint32_t *)(tbase + 4 * idx[j]);
-  decode_column<K>(r, shift, mask, w);
-}
-
-__device__ __forceinline__ void decode_lds_k(int K, const char *tbase, const int (&idx)[5],
-                                             uint32_t shift, uint32_t mask, uint32_t (&w)[8]) {
-  switch (K) {
-    case 2: decode_lds<2>(tbase, idx, shift, mask, w); break;
-    case 3: decode_lds<3>(tbase, idx, shift, mask, w); break;
-    case 4: decode_lds<4>(tbase, idx, shift, mask, w); break;
-    case 5: decode_lds<5>(tbase, idx, shift, mask, w); break;
-    case 6: decode_lds<6>(tbase, idx, shift, mask, w); break;
-    case 7: decode_lds<7>(tbase, idx, shift, mask, w); break;
-    default: decode_lds<8>(tbase, idx, shift, mask, w); break;
-  }
-}
-
-// Column window of lane column n for width K (runtime K): 5 dword indices
-// (extra ones wrap inside the tile and are never used) and the bit shift.
-__device__ __forceinline__ void column_window(int K, int n, int (&idx)[5], uint32_t &shift) {
-  const int td = 8 * K;
+__device__ __forceinline__ void column_window_k(int n, int (&idx)[Geom<K>::kLoadDw],
+                                                uint32_t &shift) {
+  constexpr int td = 8 * K;
   const int b = 16 * n * K + K - 16;
   const int d0 = b >> 5;
   shift = (uint32_t)(b & 31);
 #pragma unroll
-  for (int j = 0; j < 5; ++j) {
+  for (int j = 0; j < Geom<K>::kLoadDw; ++j) {
     int d = d0 + j;
     d += (d < 0) ? td : 0;
     d -= (d >= td) ? td : 0;
-    d -= (d >= td) ? td : 0;
     idx[j] = d;
   }
+}
+
+struct WideArgs {
+  int e, row0, nrows, nb, w, pj, lane, nkb, colbase;
+  const char *abase;     // A rows of the tile (uniform)
+  uint32_t avoff[8];     // per A chunk: lane's byte offset from abase
+  uint32_t adst[8];      // per A chunk: LDS byte offset inside an A buffer
+  uint32_t lds0;         // LDS address of smem
+};
+
+// One projection stage over all k-blocks for one wave: pacc += A x W_t.
+// MS = number of 16-row blocks multiplied (the tile's valid rows rounded up).
+template <int EPI, int K, int MS>
+__device__ __forceinline__ void wide_stage(const WideArgs &c, char *smem, const char *tens,
+                                           int nt0, int ktiles, f32x4 (&pacc)[8][4]) {
+  using L = WideLds<EPI>;
+  constexpr int NPROJ = L::NPROJ;
+  constexpr int ND = Geom<K>::kLoadDw;
+  constexpr int TD = Geom<K>::kTileDw;
+  constexpr int SEG = 128 * K;               // bytes of a strip's k-block (4 tiles)
+  const int lane = c.lane, g = lane >> 4, n = lane & 15;
+  const int nkb = c.nkb;
+
+  // trellis DMA: lane L copies 16 bytes at 16 min(L, SEG/16 - 1) of each
+  // strip's k-block segment (lanes past the segment repeat its last chunk
+  // into the unused tail of the 1 KB slot)
+  uint32_t tvoff[4];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns)
+    tvoff[ns] = (uint32_t)((nt0 + ns) * ktiles * 32 * K + 16 * min(lane, SEG / 16 - 1));
+  const uint32_t tdst = (uint32_t)(L::kTOff + c.w * 4 * kTslot);
+
+  // decode reads: dword idx of the lane's column inside tile g of a strip slot
+  int idx[ND];
+  uint32_t shift;
+  column_window_k<K>(n, idx, shift);
+  uint32_t traddr[ND];
+#pragma unroll
+  for (int j = 0; j < ND; ++j)
+    traddr[j] = (uint32_t)(L::kTOff + c.w * 4 * kTslot + g * 32 * K + 4 * idx[j]);
+  // A fragment reads: row 16 ms + n, 16-byte chunk (2g + s) ^ (n & 7)
+  uint32_t afrag[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    afrag[s] = (uint32_t)(L::kAOff + c.pj * kAbuf + n * 128 + (((2 * g + s) ^ (n & 7)) * 16));
+  const uint32_t mask = codebook_mask();
+
+  auto issue = [&](int ka, int kt, int abuf, int tbuf) {
+    const char *ab = uniform_ptr(c.abase + (size_t)ka * 128);
+#pragma unroll
+    for (int ch = 0; ch < L::kAChunks; ++ch)
+      dma16(c.avoff[ch], ab, c.lds0 + c.adst[ch] + abuf * NPROJ * kAbuf);
+    const char *tb = uniform_ptr(tens + (size_t)kt * 4 * 32 * K);
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns)
+      dma16(tvoff[ns], tb, c.lds0 + tdst + tbuf * kTbuf + ns * kTslot);
+  };
+  auto decode = [&](int tbuf, uint32_t (&bw)[4][8]) {
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+      uint32_t r[ND];
+#pragma unroll
+      for (int j = 0; j < ND; ++j)
+        r[j] = *(const uint32_t *)(smem + traddr[j] + tbuf * kTbuf + ns * kTslot);
+      decode_column<K>(r, shift, mask, bw[ns]);
+    }
+  };
+  auto multiply = [&](int abuf, const uint32_t (&bw)[4][8]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      f16x8 bf[4];
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns)
+        bf[ns] = __builtin_bit_cast(f16x8, (u32x4){bw[ns][4 * s], bw[ns][4 * s + 1],
+                                                    bw[ns][4 * s + 2], bw[ns][4 * s + 3]});
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) {
+        const f16x8 a = *(const f16x8 *)(smem + afrag[s] + abuf * NPROJ * kAbuf + ms * 2048);
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) pacc[ms][ns] = mfma16x16x32(a, bf[ns], pacc[ms][ns]);
+      }
+    }
+  };
+
+  uint32_t bA[4][8], bB[4][8];
+  const int last = nkb - 1;
+  __syncthreads();  // the LDS rings are free
+  // prologue: T[0]; A[0] + T[1]; A[1] + T[2]
+  const char *t0 = uniform_ptr(tens);
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns)
+    dma16(tvoff[ns], t0, c.lds0 + tdst + 0 * kTbuf + ns * kTslot);
+  issue(0, min(1, last), 0, 1);
+  issue(min(1, last), min(2, last), 1, 2);
+  wait_vmcnt<2 * L::kDmaPerIter>();
+  __syncthreads();
+  decode(0, bA);
+
+  // iteration kb: A[kb] in abuf kb%3, T[kb+1] in tbuf (kb+1)%3; issue
+  // A[kb+2] -> abuf (kb+2)%3 and T[kb+3] -> tbuf kb%3
+#define EXL3_WIDE_ITER(KB, AB, TB_NEXT, CUR, NXT)                                       \
+  {                                                                                     \
+    wait_vmcnt<L::kDmaPerIter>();                                                       \
+    __syncthreads();                                                                    \
+    issue(min((KB) + 2, last), min((KB) + 3, last), ((AB) + 2) % 3, (AB));               \
+    decode((TB_NEXT), NXT);                                                             \
+    multiply((AB), CUR);                                                                \
+  }
+  int kb = 0;
+  for (; kb + 6 <= nkb; kb += 6) {
+    EXL3_WIDE_ITER(kb + 0, 0, 1, bA, bB)
+    EXL3_WIDE_ITER(kb + 1, 1, 2, bB, bA)
+    EXL3_WIDE_ITER(kb + 2, 2, 0, bA, bB)
+    EXL3_WIDE_ITER(kb + 3, 0, 1, bB, bA)
+    EXL3_WIDE_ITER(kb + 4, 1, 2, bA, bB)
+    EXL3_WIDE_ITER(kb + 5, 2, 0, bB, bA)
+  }
+  // remainder (nkb is even): 0, 2 or 4 k-blocks, buffers continue from 0
+  if (kb + 2 <= nkb) {
+    EXL3_WIDE_ITER(kb + 0, 0, 1, bA, bB)
+    EXL3_WIDE_ITER(kb + 1, 1, 2, bB, bA)
+    kb += 2;
+    if (kb + 2 <= nkb) {
+      EXL3_WIDE_ITER(kb + 0, 2, 0, bA, bB)
+      EXL3_WIDE_ITER(kb + 1, 0, 1, bB, bA)
+    }
+  }
+#undef EXL3_WIDE_ITER
+  wait_vmcnt<0>();  // drain tail DMAs before the LDS is reused
+}
+
+// A wave with no work for this stage still takes part in the DMA/barrier
+// cadence of its workgroup (same counts, data never read).
+template <int EPI>
+__device__ __forceinline__ void wide_idle_stage(const WideArgs &c) {
+  using L = WideLds<EPI>;
+  const int nkb = c.nkb;
+  const uint32_t tdst = (uint32_t)(L::kTOff + c.w * 4 * kTslot);
+  auto issue = [&](int ka, int abuf, int tbuf) {
+    const char *ab = uniform_ptr(c.abase + (size_t)ka * 128);
+#pragma unroll
+    for (int ch = 0; ch < L::kAChunks; ++ch)
+      dma16(c.avoff[ch], ab, c.lds0 + c.adst[ch] + abuf * L::NPROJ * kAbuf);
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) dma16(c.avoff[0], ab, c.lds0 + tdst + tbuf * kTbuf + ns * kTslot);
+  };
+  const int last = nkb - 1;
+  __syncthreads();
+  const char *a0 = uniform_ptr(c.abase);
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) dma16(c.avoff[0], a0, c.lds0 + tdst + ns * kTslot);
+  issue(0, 0, 1);
+  issue(min(1, last), 1, 2);
+  wait_vmcnt<2 * L::kDmaPerIter>();
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    wait_vmcnt<L::kDmaPerIter>();
+    __syncthreads();
+    const int ab = kb % 3;
+    issue(min(kb + 2, last), (ab + 2) % 3, ab);
+  }
+  wait_vmcnt<0>();
+}
+
+template <int EPI, int K>
+__device__ __forceinline__ void wide_stage_rows(const WideArgs &c, char *smem, const char *tens,
+                                                int nt0, int ktiles, int msub,
+                                                f32x4 (&pacc)[8][4]) {
+  if (msub <= 2) wide_stage<EPI, K, 2>(c, smem, tens, nt0, ktiles, pacc);
+  else if (msub <= 4) wide_stage<EPI, K, 4>(c, smem, tens, nt0, ktiles, pacc);
+  else wide_stage<EPI, K, 8>(c, smem, tens, nt0, ktiles, pacc);
 }
 
 template <int EPI, bool MULTI>
 __global__ void __launch_bounds__(256, 1) gemm_wide_kernel(GemmParams p) {
   using L = WideLds<EPI>;
   constexpr int NPROJ = L::NPROJ;
-  constexpr int kAChunks = NPROJ * 16 / 4;  // 1 KB A chunks per wave per k-block
   __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
 
-  int e, row0, nrows;
-  if (!tile_of_block(p, kWBM, blockIdx.x, e, row0, nrows)) return;
-  const int nb = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
-  const int pj = (EPI == EPI_GATEUP) ? (w >> 1) : 0;
-  const int colbase = (EPI == EPI_GATEUP) ? nb * 128 : nb * 256;
-  const int colw = colbase + ((EPI == EPI_GATEUP) ? 64 * (w & 1) : 64 * w);
+  WideArgs c;
+  if (!tile_of_block(p, kWBM, blockIdx.x, c.e, c.row0, c.nrows)) return;
+  c.nb = blockIdx.y;
+  c.lane = threadIdx.x & 63;
+  c.w = wave_id();
+  c.pj = (EPI == EPI_GATEUP) ? (c.w >> 1) : 0;
+  c.colbase = (EPI == EPI_GATEUP) ? c.nb * 128 : c.nb * 256;
+  c.nkb = p.in_f >> 6;
+  c.lds0 = (uint32_t)(uintptr_t)smem;
+  const int w = c.w, lane = c.lane, g = lane >> 4, n = lane & 15;
+  const int colw = c.colbase + ((EPI == EPI_GATEUP) ? 64 * (w & 1) : 64 * w);
   const bool col_ok = colw < p.out_f;
   const int nt0 = colw >> 4;
-  const int g = lane >> 4, n = lane & 15;
-  const int msub_act = (nrows + 15) >> 4;
-  const int nkb = p.in_f >> 6;
   const int ktiles = p.in_f >> 4;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const int msub = (c.nrows + 15) >> 4;
 
-  // A chunk c of this wave: 8 rows x 128 B; lane L -> row 8 rg + L/8, slot
-  // L%8 holding global 16-byte chunk (L%8) ^ (row & 7) (bank swizzle).
-  const uint16_t *asrc[kAChunks];
-  uint32_t adst[kAChunks];
+  // A chunk ch of this wave: 8 rows x 128 B; lane L -> row 8 rg + L/8, LDS
+  // slot L%8 holding the global 16-byte chunk (L%8) ^ (row & 7) (swizzle).
+  c.abase = (const char *)(p.A + (int64_t)c.row0 * p.lda);
 #pragma unroll
-  for (int c = 0; c < kAChunks; ++c) {
-    const int f = w * kAChunks + c;
+  for (int ch = 0; ch < L::kAChunks; ++ch) {
+    const int f = w * L::kAChunks + ch;
     const int q = f >> 4, rg = f & 15;
     const int r = 8 * rg + (lane >> 3);
-    const int rs = min(r, nrows - 1);
+    const int rs = min(r, c.nrows - 1);
     const int gc = (lane & 7) ^ (r & 7);
-    asrc[c] = p.A + (int64_t)(row0 + rs) * p.lda + q * p.a_proj_stride + gc * 8;
-    adst[c] = (uint32_t)(L::kAOff + q * kAbuf + rg * 1024);
+    c.avoff[ch] = (uint32_t)(2 * ((int64_t)rs * p.lda + q * p.a_proj_stride + gc * 8));
+    c.adst[ch] = (uint32_t)(L::kAOff + q * kAbuf + rg * 1024);
   }
-  auto a_frag = [&](int buf, int ms, int s) -> f16x8 {
-    const int r = 16 * ms + n;
-    const int c = (2 * g + s) ^ (r & 7);
-    return *(const f16x8 *)(smem + L::kAOff + (buf * NPROJ + pj) * kAbuf + r * 128 + c * 16);
-  };
 
-  const uint32_t mask = codebook_mask();
-  // acc: running stage sum (only with several stages); pacc: one stage's chain
   f32x4 acc[MULTI ? 8 : 1][4];
   f32x4 pacc[8][4];
 #pragma unroll
@@ -417,103 +565,39 @@ __global__ void __launch_bounds__(256, 1) gemm_wide_kernel(GemmParams p) {
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const ProjDev pd = (pj == 0) ? p.proj[0] : p.proj[NPROJ - 1];
+  const ProjDev pd = (c.pj == 0) ? p.proj[0] : p.proj[NPROJ - 1];
   const int nst = MULTI ? max(p.proj[0].num_stages, p.proj[NPROJ - 1].num_stages) : 1;
   for (int t = 0; t < nst; ++t) {
     float sc = 0.0f;
-    int K = 4;
-    const uint32_t *tens = nullptr;
+    int K = 0;
+    const char *tens = nullptr;
     if (t < pd.num_stages && col_ok) {
-      sc = uload_f32(pd.scale + t * p.E + e);
-      K = uload_i32(pd.bits + t * p.E + e);
-      tens = uload_ptr(pd.trellis + t * p.E + e);
+      sc = uload_f32(pd.scale + t * p.E + c.e);
+      K = uload_i32(pd.bits + t * p.E + c.e);
+      tens = (const char *)uload_ptr(pd.trellis + t * p.E + c.e);
       if (sc != 0.0f && (tens == nullptr || K < 2 || K > 8)) {
-        if (nb == 0 && (w & 1) == 0 && lane == 0) atomicAdd(p.ctrl + 1, 1);
+        if (c.nb == 0 && (w & 1) == 0 && lane == 0) atomicAdd(p.ctrl + 1, 1);
         sc = 0.0f;
       }
     }
     const bool active = __builtin_amdgcn_readfirstlane(sc != 0.0f ? 1 : 0) != 0;
-    if (!active) K = 4;
-    int idx[5];
-    uint32_t shift;
-    column_window(K, n, idx, shift);
-    const int seg = 128 * K;  // bytes of one strip's 4 tiles of a k-block
-    // trellis DMA source of this lane for strip ns: 16 bytes at 16*min(L, seg/16-1)
-    // of the strip's k-block segment (lanes past the segment repeat its last
-    // chunk into the unused tail of the 1 KB slot). Inactive waves copy from
-    // their A rows instead (never decoded).
-    const char *tsrc[4];
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
-      const int ch = min(lane, seg / 16 - 1);
-      tsrc[ns] = active ? (const char *)tens + (size_t)(nt0 + ns) * ktiles * 32 * K + 16 * ch
-                        : (const char *)asrc[0];
-    }
-    const uint32_t tdst = (uint32_t)(L::kTOff + w * 4 * kTslot);
-    const int kstride = active ? 4 * 32 * K : 0;  // bytes per k-block in a strip
-
-    auto issue = [&](int kb, int buf) {
-#pragma unroll
-      for (int c = 0; c < kAChunks; ++c)
-        dma16(asrc[c] + kb * 64, lds0 + adst[c] + buf * NPROJ * kAbuf);
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns)
-        dma16(tsrc[ns] + (size_t)kb * kstride, lds0 + tdst + buf * kTbuf + ns * kTslot);
-    };
-
 #pragma unroll
     for (int ms = 0; ms < 8; ++ms)
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns) pacc[ms][ns] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    __syncthreads();  // previous users of the ring are done
-#pragma unroll
-    for (int d = 0; d < kRing - 1; ++d) issue(min(d, nkb - 1), d);
-    int buf = 0;
-    for (int kb = 0; kb < nkb; ++kb) {
-      // DMAs of k-block kb are done once at most (kRing-2) later k-blocks'
-      // worth of DMAs are still outstanding
-      wait_vmcnt<(kRing - 2) * L::kDmaPerKb>();
-      __syncthreads();
-      const int nbuf = (buf + kRing - 1) % kRing;
-      issue(min(kb + kRing - 1, nkb - 1), nbuf);
-      if (active) {
-        uint32_t bw[4][8];
-        const char *tb = smem + L::kTOff + buf * kTbuf + w * 4 * kTslot + g * 32 * K;
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns)
-          decode_lds_k(K, tb + ns * kTslot, idx, shift, mask, bw[ns]);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          f16x8 bf[4];
-#pragma unroll
-          for (int ns = 0; ns < 4; ++ns)
-            bf[ns] = __builtin_bit_cast(f16x8, (u32x4){bw[ns][4 * s], bw[ns][4 * s + 1],
-                                                        bw[ns][4 * s + 2], bw[ns][4 * s + 3]});
-          f16x8 af[8];
-#pragma unroll
-          for (int ms = 0; ms < 8; ++ms) af[ms] = a_frag(buf, ms, s);
-          if (msub_act == 8) {
-#pragma unroll
-            for (int ms = 0; ms < 8; ++ms)
-#pragma unroll
-              for (int ns = 0; ns < 4; ++ns)
-                pacc[ms][ns] = mfma16x16x32(af[ms], bf[ns], pacc[ms][ns]);
-          } else {
-#pragma unroll
-            for (int ms = 0; ms < 8; ++ms) {
-              if (ms < msub_act) {
-#pragma unroll
-                for (int ns = 0; ns < 4; ++ns)
-                  pacc[ms][ns] = mfma16x16x32(af[ms], bf[ns], pacc[ms][ns]);
-              }
-            }
-          }
-        }
+    if (!active) {
+      wide_idle_stage<EPI>(c);
+    } else {
+      switch (K) {
+        case 2: wide_stage_rows<EPI, 2>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 3: wide_stage_rows<EPI, 3>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 4: wide_stage_rows<EPI, 4>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 5: wide_stage_rows<EPI, 5>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 6: wide_stage_rows<EPI, 6>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 7: wide_stage_rows<EPI, 7>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        default: wide_stage_rows<EPI, 8>(c, smem, tens, nt0, ktiles, msub, pacc); break;
       }
-      buf = (buf + 1 == kRing) ? 0 : buf + 1;
     }
-    wait_vmcnt<0>();  // drain the tail DMAs before the ring is reused
     // acc = fmaf(s_t, P_t, acc) from acc = 0; a skipped stage leaves acc alone
 #pragma unroll
     for (int ms = 0; ms < 8; ++ms)
@@ -528,7 +612,8 @@ __global__ void __launch_bounds__(256, 1) gemm_wide_kernel(GemmParams p) {
           }
         }
   }
-  const f32x4(&fin)[8][4] = *reinterpret_cast<const f32x4(*)[8][4]>(MULTI ? &acc[0][0] : &pacc[0][0]);
+  const f32x4(&fin)[8][4] =
+      *reinterpret_cast<const f32x4(*)[8][4]>(MULTI ? &acc[0][0] : &pacc[0][0]);
 
   // ---- epilogue: accumulators -> LDS tile -> shared epilogue
   __syncthreads();
@@ -540,11 +625,11 @@ __global__ void __launch_bounds__(256, 1) gemm_wide_kernel(GemmParams p) {
     for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        T[pj * (kWBM * L::kLd) + (16 * ms + 4 * g + r) * L::kLd + cw + 16 * ns + n] =
+        T[c.pj * (kWBM * L::kLd) + (16 * ms + 4 * g + r) * L::kLd + cw + 16 * ns + n] =
             fin[ms][ns][r];
   __syncthreads();
-  const int nblk = (EPI == EPI_GATEUP) ? 1 : min(2, (p.out_f - colbase) / 128);
-  epilogue<EPI>(p, T, L::kLd, kWBM * L::kLd, e, row0, nrows, colbase, nblk);
+  const int nblk = (EPI == EPI_GATEUP) ? 1 : min(2, (p.out_f - c.colbase) / 128);
+  epilogue<EPI>(p, T, L::kLd, kWBM * L::kLd, c.e, c.row0, c.nrows, c.colbase, nblk);
 }
 
 hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks, hipStream_t s,

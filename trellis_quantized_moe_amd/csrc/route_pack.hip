@@ -200,14 +200,15 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
     if (tid == 0) plan[0] = total;
   }
 
-  // rows whose pairs were all dropped produce zeros
+  // rows whose pairs were all dropped produce zeros: one row per thread to
+  // find them (rare), then the row is cleared by that thread
   __syncthreads();
   if (p.out) {
-    for (int r = w; r < p.rows; r += kPackWaves) {
+    for (int r = tid; r < p.rows; r += kPackThreads) {
       bool any = false;
       for (int j = 0; j < p.topk; ++j) any |= p.pos_of_pair[r * p.topk + j] >= 0;
       if (!any) {
-        for (int c = lane; c < p.H; c += 64) {
+        for (int c = 0; c < p.H; ++c) {
           if (p.out_f32) ((float *)p.out)[(int64_t)r * p.H + c] = 0.0f;
           else ((uint16_t *)p.out)[(int64_t)r * p.H + c] = 0;
         }
