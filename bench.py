@@ -249,11 +249,18 @@ def main():
             extra["decode_M%d" % M] = run_decode(args, torch, exl3, synth, M)
 
     dom = pre["dominant"]
+    # HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    # counter summary, only while the kernel source is the one measured
     traffic = None
     if os.path.exists(args.traffic):
+        import hashlib
         with open(args.traffic) as f:
             t = json.load(f)
-        if t.get("kernel") == dom and t.get("workload") == "prefill":
+        src = os.path.join(ROOT, "trellis_quantized_moe_amd", "csrc", "gemm.hip")
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if (t.get("kernel") == dom and t.get("workload") == "prefill"
+                and t.get("source_sha256") == sha):
             traffic = t.get("bytes_per_launch")
     roof = {"bound": "mfma", "kernel": dom, "achieved": pre["achieved_tflops"],
             "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
