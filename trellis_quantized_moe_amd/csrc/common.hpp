@@ -50,10 +50,9 @@ __device__ __forceinline__ uint32_t codebook2(uint32_t s2, uint32_t mask_lo10) {
   u16x2 a = h >> (u16x2){6, 6};
   const uint32_t hb = __builtin_bit_cast(uint32_t, h);
   uint32_t A = __builtin_bit_cast(uint32_t, a) | 0x3C003C00u;
-  // (h & 0x03FF03FF) | 0xBC00BC00 in one VOP3 op: gfx9 VOP3 takes no literal,
-  // so the mask comes in a VGPR and the OR constant in an SGPR.
-  uint32_t B;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(B) : "v"(hb), "v"(mask_lo10), "s"(0xBC00BC00u));
+  // (h & 0x03FF03FF) | 0xBC00BC00 is one v_and_or_b32 when the mask sits in a
+  // VGPR (gfx9 VOP3 takes no literal; the OR constant goes to an SGPR)
+  const uint32_t B = (hb & mask_lo10) | 0xBC00BC00u;
   f16x2 r = __builtin_bit_cast(f16x2, A) + __builtin_bit_cast(f16x2, B);
   return __builtin_bit_cast(uint32_t, r);
 }
@@ -118,27 +117,47 @@ __device__ __forceinline__ uint32_t window32(const uint32_t (&N)[Geom<K>::kNormD
 // pairs. Register v holds states (j, j+4) with j = (v & 3) + 8 * (v >> 2),
 // so registers 0..3 feed k = {0,4,1,5,2,6,3,7} and 4..7 feed
 // k = {8,12,9,13,10,14,11,15} of the tile column: the kSigma order.
+// The window of one tile column shifted to bit 0 (kNormDw dwords).
 template <int K>
-__device__ __forceinline__ void decode_column(const uint32_t (&raw)[Geom<K>::kLoadDw],
-                                              uint32_t shift, uint32_t mask,
-                                              uint32_t (&out)[8]) {
+__device__ __forceinline__ void column_normalize(const uint32_t (&raw)[Geom<K>::kLoadDw],
+                                                 uint32_t shift,
+                                                 uint32_t (&N)[Geom<K>::kNormDw]) {
   constexpr int ND = Geom<K>::kLoadDw, NN = Geom<K>::kNormDw;
-  uint32_t N[NN];
 #pragma unroll
   for (int j = 0; j < NN; ++j) {
     const uint32_t hi = (j + 1 < ND) ? raw[(j + 1 < ND) ? j + 1 : j] : 0u;
     N[j] = __builtin_amdgcn_alignbit(hi, raw[j], shift);
   }
-#define EXL3_DECODE_REG(v)                                                   \
-  {                                                                          \
-    constexpr int j = ((v) & 3) + 8 * ((v) >> 2);                            \
-    const uint32_t lo = window32<K, j * K>(N);                               \
-    const uint32_t hi = window32<K, (j + 4) * K - 16>(N);                    \
-    out[v] = codebook2((lo & 0x0000FFFFu) | (hi & 0xFFFF0000u), mask);        \
-  }
-  EXL3_DECODE_REG(0) EXL3_DECODE_REG(1) EXL3_DECODE_REG(2) EXL3_DECODE_REG(3)
-  EXL3_DECODE_REG(4) EXL3_DECODE_REG(5) EXL3_DECODE_REG(6) EXL3_DECODE_REG(7)
-#undef EXL3_DECODE_REG
+}
+
+// Packed fp16 register V (0..7) of a decoded tile column: states (j, j+4)
+// with j = (V & 3) + 8 * (V >> 2), so registers 0..3 feed k = {0,4,1,5,2,6,3,7}
+// and 4..7 feed k = {8,12,9,13,10,14,11,15} of the column: the kSigma order.
+template <int K, int V>
+__device__ __forceinline__ uint32_t column_reg(const uint32_t (&N)[Geom<K>::kNormDw],
+                                               uint32_t mask) {
+  constexpr int j = (V & 3) + 8 * (V >> 2);
+  const uint32_t lo = window32<K, j * K>(N);
+  const uint32_t hi = window32<K, (j + 4) * K - 16>(N);
+  return codebook2((lo & 0x0000FFFFu) | (hi & 0xFFFF0000u), mask);
+}
+
+// Decode one tile column (16 states) from its raw dwords into 8 packed fp16
+// pairs (register order as in column_reg).
+template <int K>
+__device__ __forceinline__ void decode_column(const uint32_t (&raw)[Geom<K>::kLoadDw],
+                                              uint32_t shift, uint32_t mask,
+                                              uint32_t (&out)[8]) {
+  uint32_t N[Geom<K>::kNormDw];
+  column_normalize<K>(raw, shift, N);
+  out[0] = column_reg<K, 0>(N, mask);
+  out[1] = column_reg<K, 1>(N, mask);
+  out[2] = column_reg<K, 2>(N, mask);
+  out[3] = column_reg<K, 3>(N, mask);
+  out[4] = column_reg<K, 4>(N, mask);
+  out[5] = column_reg<K, 5>(N, mask);
+  out[6] = column_reg<K, 6>(N, mask);
+  out[7] = column_reg<K, 7>(N, mask);
 }
 
 // Wave index as a scalar: lets the compiler keep every per-wave value (and

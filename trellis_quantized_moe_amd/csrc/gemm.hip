@@ -18,6 +18,9 @@
 //                 stages with s_t == 0 skipped
 //   epilogue    = fixed-order fp32 FWHT per 128-block, then per-element
 //                 scalings, identical code for every tile shape.
+#include <algorithm>
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -351,6 +354,36 @@ __device__ __forceinline__ void column_window_k(int n, int (&idx)[Geom<K>::kLoad
   }
 }
 
+// One scheduling unit of a pipelined wide iteration: decode register V of
+// strip NS of the next k-block and issue this unit's share of the current
+// k-block's MFMAs (MFMA m: step m / (4 MS), row block (m / 4) % MS, strip
+// m % 4). Units are separated by scheduling barriers so that the in-order
+// issue alternates MFMAs with decode VALU work.
+template <int K, int MS, int U>
+__device__ __forceinline__ void wide_unit(const uint32_t (&N)[4][Geom<K>::kNormDw],
+                                          uint32_t mask, const f16x8 (&af)[2][MS],
+                                          const f16x8 (&bf)[2][4], f32x4 (&pacc)[8][4],
+                                          uint32_t (&nxt)[4][8]) {
+  constexpr int NS = U / 8, V = U % 8;
+  nxt[NS][V] = column_reg<K, V>(N[NS], mask);
+  constexpr int M = 8 * MS, m0 = U * M / 32, m1 = (U + 1) * M / 32;
+#pragma unroll
+  for (int m = m0; m < m1; ++m) {
+    const int s = m / (4 * MS), ms = (m / 4) % MS, ns = m % 4;
+    pacc[ms][ns] = mfma16x16x32(af[s][ms], bf[s][ns], pacc[ms][ns]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int K, int MS, int... Us>
+__device__ __forceinline__ void wide_units(const uint32_t (&N)[4][Geom<K>::kNormDw],
+                                           uint32_t mask, const f16x8 (&af)[2][MS],
+                                           const f16x8 (&bf)[2][4], f32x4 (&pacc)[8][4],
+                                           uint32_t (&nxt)[4][8],
+                                           std::integer_sequence<int, Us...>) {
+  (wide_unit<K, MS, Us>(N, mask, af, bf, pacc, nxt), ...);
+}
+
 struct WideArgs {
   int e, row0, nrows, nb, w, pj, lane, nkb, colbase;
   const char *abase;     // A rows of the tile (uniform)
@@ -416,21 +449,33 @@ __device__ __forceinline__ void wide_stage(const WideArgs &c, char *smem, const 
       decode_column<K>(r, shift, mask, bw[ns]);
     }
   };
-  auto multiply = [&](int abuf, const uint32_t (&bw)[4][8]) {
+  // multiply A[abuf] by the current B registers while decoding the next
+  // k-block from T[tbuf] into nxt, interleaved unit by unit
+  auto step = [&](int abuf, int tbuf, const uint32_t (&cur)[4][8], uint32_t (&nxt)[4][8]) {
+    uint32_t r[4][ND];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      f16x8 bf[4];
+    for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+      for (int j = 0; j < ND; ++j)
+        r[ns][j] = *(const uint32_t *)(smem + traddr[j] + tbuf * kTbuf + ns * kTslot);
+    f16x8 af[2][MS];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms)
+        af[st][ms] = *(const f16x8 *)(smem + afrag[st] + abuf * NPROJ * kAbuf + ms * 2048);
+    f16x8 bf[2][4];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns)
-        bf[ns] = __builtin_bit_cast(f16x8, (u32x4){bw[ns][4 * s], bw[ns][4 * s + 1],
-                                                    bw[ns][4 * s + 2], bw[ns][4 * s + 3]});
+        bf[st][ns] = __builtin_bit_cast(f16x8, (u32x4){cur[ns][4 * st], cur[ns][4 * st + 1],
+                                                        cur[ns][4 * st + 2], cur[ns][4 * st + 3]});
+    uint32_t N[4][Geom<K>::kNormDw];
 #pragma unroll
-      for (int ms = 0; ms < MS; ++ms) {
-        const f16x8 a = *(const f16x8 *)(smem + afrag[s] + abuf * NPROJ * kAbuf + ms * 2048);
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns) pacc[ms][ns] = mfma16x16x32(a, bf[ns], pacc[ms][ns]);
-      }
-    }
+    for (int ns = 0; ns < 4; ++ns) column_normalize<K>(r[ns], shift, N[ns]);
+    __builtin_amdgcn_sched_barrier(0);
+    wide_units<K, MS>(N, mask, af, bf, pacc, nxt, std::make_integer_sequence<int, 32>{});
   };
 
   uint32_t bA[4][8], bB[4][8];
@@ -454,8 +499,7 @@ __device__ __forceinline__ void wide_stage(const WideArgs &c, char *smem, const 
     wait_vmcnt<L::kDmaPerIter>();                                                       \
     __syncthreads();                                                                    \
     issue(min((KB) + 2, last), min((KB) + 3, last), ((AB) + 2) % 3, (AB));               \
-    decode((TB_NEXT), NXT);                                                             \
-    multiply((AB), CUR);                                                                \
+    step((AB), (TB_NEXT), CUR, NXT);                                                    \
   }
   int kb = 0;
   for (; kb + 6 <= nkb; kb += 6) {
@@ -522,15 +566,15 @@ __device__ __forceinline__ void wide_stage_rows(const WideArgs &c, char *smem, c
   else wide_stage<EPI, K, 8>(c, smem, tens, nt0, ktiles, pacc);
 }
 
+// One work item: rows of tile `bx` times 256-column block `by`.
 template <int EPI, bool MULTI>
-__global__ void __launch_bounds__(256, 1) gemm_wide_kernel(GemmParams p) {
+__device__ __forceinline__ void wide_item(const GemmParams &p, char *smem, int bx, int by) {
   using L = WideLds<EPI>;
   constexpr int NPROJ = L::NPROJ;
-  __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
 
   WideArgs c;
-  if (!tile_of_block(p, kWBM, blockIdx.x, c.e, c.row0, c.nrows)) return;
-  c.nb = blockIdx.y;
+  if (!tile_of_block(p, kWBM, bx, c.e, c.row0, c.nrows)) return;
+  c.nb = by;
   c.lane = threadIdx.x & 63;
   c.w = wave_id();
   c.pj = (EPI == EPI_GATEUP) ? (c.w >> 1) : 0;
@@ -632,13 +676,24 @@ __global__ void __launch_bounds__(256, 1) gemm_wide_kernel(GemmParams p) {
   epilogue<EPI>(p, T, L::kLd, kWBM * L::kLd, c.e, c.row0, c.nrows, c.colbase, nblk);
 }
 
+// One workgroup per (tile, 256-column block). The host rounds the tile
+// count up to a multiple of 8: workgroups are dealt to the 8 XCDs
+// round-robin by linear id (x fastest), so every column block of a tile runs
+// on the same XCD and shares its L2 copy of the tile's A rows.
+template <int EPI, bool MULTI>
+__global__ void __launch_bounds__(256, 1) gemm_wide_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[WideLds<EPI>::kBytes];
+  wide_item<EPI, MULTI>(p, smem, blockIdx.x, blockIdx.y);
+}
+
 hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks, hipStream_t s,
                        bool wide) {
   if (tiles <= 0 || nblocks <= 0) return hipSuccess;
   const dim3 grid(tiles, nblocks);
   const bool multi = p.proj[0].num_stages > 1 || (epi == EPI_GATEUP && p.proj[1].num_stages > 1);
   if (wide) {
-#define EXL3_WIDE(E, M) hipLaunchKernelGGL((gemm_wide_kernel<E, M>), grid, dim3(256), 0, s, p)
+    const dim3 wgrid((tiles + 7) / 8 * 8, nblocks);
+#define EXL3_WIDE(E, M) hipLaunchKernelGGL((gemm_wide_kernel<E, M>), wgrid, dim3(256), 0, s, p)
     switch (epi) {
       case EPI_GATEUP: if (multi) EXL3_WIDE(EPI_GATEUP, true); else EXL3_WIDE(EPI_GATEUP, false); break;
       case EPI_DOWN: if (multi) EXL3_WIDE(EPI_DOWN, true); else EXL3_WIDE(EPI_DOWN, false); break;

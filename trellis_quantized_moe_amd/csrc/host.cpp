@@ -206,12 +206,7 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
   for (int pass = 0; pass < L.passes; ++pass) {
     const int pb = pass * L.cap;
     const int npos = (int)std::min<int64_t>(L.cap, P - pb);
-    // Wide launches round the tile count up to a multiple of 8: workgroups
-    // are dealt to the 8 XCDs round-robin by linear id, so every column
-    // block of a tile then lands on the same XCD and shares its L2 copy of
-    // the tile's A rows (surplus workgroups exit at once).
-    int tiles = std::min(E, npos) + (npos + bm - 1) / bm;
-    if (wide) tiles = (tiles + 7) / 8 * 8;
+    const int tiles = std::min(E, npos) + (npos + bm - 1) / bm;
     const int32_t *plan = at<int32_t>(ws, L.plan) + (size_t)pass * (1 + 3 * (size_t)L.slots);
 
     RotParams rp{};
@@ -370,8 +365,7 @@ int32_t exl3_linear(const uint16_t *x, int32_t rows, const exl3_proj *proj, void
   const int fo = proj->out_features;
   const bool wide = linear_wide(rows, fo);
   const hipError_t le =
-      wide ? launch_gemm(EPI_LINEAR, g, ((rows + kBMWide - 1) / kBMWide + 7) / 8 * 8,
-                         (fo + 255) / 256, st, true)
+      wide ? launch_gemm(EPI_LINEAR, g, (rows + kBMWide - 1) / kBMWide, (fo + 255) / 256, st, true)
            : launch_gemm(EPI_LINEAR, g, (rows + kBM - 1) / kBM, fo / 128, st, false);
   if (le != hipSuccess) return EXL3_E_LAUNCH;
   return EXL3_OK;

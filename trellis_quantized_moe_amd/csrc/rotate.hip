@@ -17,7 +17,9 @@ __global__ void __launch_bounds__(256) rotate_kernel(RotParams p) {
   const int nblk = p.H >> 7;
   const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int i = threadIdx.x & 15;
-  if (p.ctrl_clear && blockIdx.x == 0 && threadIdx.x == 0) p.ctrl_clear[1] = 0;
+  if (p.ctrl_clear && blockIdx.x == 0 && threadIdx.x == 0) {
+    p.ctrl_clear[1] = 0;  // bad stage entries
+  }
   const int64_t per_item = (int64_t)p.nproj * nblk;
   if (gid >= (int64_t)p.nitems * per_item) return;
   const int item = (int)(gid / per_item);

@@ -166,7 +166,9 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
   }
 
   if (!p.do_plan) return;
-  if (tid == 0 && p.ctrl) p.ctrl[1] = 0;
+  if (tid == 0 && p.ctrl) {
+    p.ctrl[1] = 0;  // bad stage entries
+  }
 
   // expert of every kept position (binary search over the offsets)
   const int kept = s_off[E];
