@@ -312,6 +312,12 @@ struct WideLds {
   static constexpr int kDmaPerIter = kAChunks + 4;
 };
 
+// 16-byte chunk swizzle of A row r (0..15 inside its 16-row block). A row is
+// 128 bytes; the 16 lanes of a fragment read (rows 0..15, one chunk index)
+// land on 16 distinct 16-byte bank groups of a 256-byte bank window, and any
+// 8 consecutive rows on 8 distinct groups of a 128-byte window.
+__device__ __forceinline__ int a_swizzle(int r) { return (r ^ (r >> 3)) & 7; }
+
 // 16-byte-per-lane global->LDS copy: lane L reads sbase + voff and writes
 // LDS byte m0 + 16 L. The wave's LDS destination goes through m0.
 __device__ __forceinline__ void dma16(uint32_t voff, const void *sbase, uint32_t lds_base) {
@@ -359,12 +365,22 @@ __device__ __forceinline__ void column_window_k(int n, int (&idx)[Geom<K>::kLoad
 // k-block's MFMAs (MFMA m: step m / (4 MS), row block (m / 4) % MS, strip
 // m % 4). Units are separated by scheduling barriers so that the in-order
 // issue alternates MFMAs with decode VALU work.
-template <int K, int MS, int U>
+// DMA d of an iteration (G per iteration) is issued in unit (32 d) / G.
+template <int G, int U>
+constexpr int dma_of_unit() {
+  for (int d = 0; d < G; ++d)
+    if (d * 32 / G == U) return d;
+  return -1;
+}
+
+template <int K, int MS, int G, int U, typename Dma>
 __device__ __forceinline__ void wide_unit(const uint32_t (&N)[4][Geom<K>::kNormDw],
                                           uint32_t mask, const f16x8 (&af)[2][MS],
                                           const f16x8 (&bf)[2][4], f32x4 (&pacc)[8][4],
-                                          uint32_t (&nxt)[4][8]) {
+                                          uint32_t (&nxt)[4][8], Dma &dma) {
   constexpr int NS = U / 8, V = U % 8;
+  constexpr int D = dma_of_unit<G, U>();
+  if constexpr (D >= 0) dma(D);
   nxt[NS][V] = column_reg<K, V>(N[NS], mask);
   constexpr int M = 8 * MS, m0 = U * M / 32, m1 = (U + 1) * M / 32;
 #pragma unroll
@@ -375,13 +391,13 @@ __device__ __forceinline__ void wide_unit(const uint32_t (&N)[4][Geom<K>::kNormD
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int K, int MS, int... Us>
+template <int K, int MS, int G, typename Dma, int... Us>
 __device__ __forceinline__ void wide_units(const uint32_t (&N)[4][Geom<K>::kNormDw],
                                            uint32_t mask, const f16x8 (&af)[2][MS],
                                            const f16x8 (&bf)[2][4], f32x4 (&pacc)[8][4],
-                                           uint32_t (&nxt)[4][8],
+                                           uint32_t (&nxt)[4][8], Dma &dma,
                                            std::integer_sequence<int, Us...>) {
-  (wide_unit<K, MS, Us>(N, mask, af, bf, pacc, nxt), ...);
+  (wide_unit<K, MS, G, Us>(N, mask, af, bf, pacc, nxt, dma), ...);
 }
 
 struct WideArgs {
@@ -422,22 +438,28 @@ __device__ __forceinline__ void wide_stage(const WideArgs &c, char *smem, const 
 #pragma unroll
   for (int j = 0; j < ND; ++j)
     traddr[j] = (uint32_t)(L::kTOff + c.w * 4 * kTslot + g * 32 * K + 4 * idx[j]);
-  // A fragment reads: row 16 ms + n, 16-byte chunk (2g + s) ^ (n & 7)
+  // A fragment reads: row 16 ms + n, 16-byte chunk (2g + s) ^ a_swizzle(n)
   uint32_t afrag[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
-    afrag[s] = (uint32_t)(L::kAOff + c.pj * kAbuf + n * 128 + (((2 * g + s) ^ (n & 7)) * 16));
+    afrag[s] = (uint32_t)(L::kAOff + c.pj * kAbuf + n * 128 + (((2 * g + s) ^ a_swizzle(n)) * 16));
   const uint32_t mask = codebook_mask();
 
+  // DMA d of k-block (ka, kt): d < kAChunks copies A chunk d, the others
+  // the trellis segment of strip d - kAChunks (lanes past the segment idle)
+  auto dma_one = [&](int d, int ka, int kt, int abuf, int tbuf) {
+    if (d < L::kAChunks) {
+      const char *ab = uniform_ptr(c.abase + (size_t)ka * 128);
+      dma16(c.avoff[d], ab, c.lds0 + c.adst[d] + abuf * NPROJ * kAbuf);
+    } else {
+      const int ns = d - L::kAChunks;
+      const char *tb = uniform_ptr(tens + (size_t)kt * 4 * 32 * K);
+      if (lane < SEG / 16) dma16(tvoff[ns], tb, c.lds0 + tdst + tbuf * kTbuf + ns * kTslot);
+    }
+  };
   auto issue = [&](int ka, int kt, int abuf, int tbuf) {
-    const char *ab = uniform_ptr(c.abase + (size_t)ka * 128);
 #pragma unroll
-    for (int ch = 0; ch < L::kAChunks; ++ch)
-      dma16(c.avoff[ch], ab, c.lds0 + c.adst[ch] + abuf * NPROJ * kAbuf);
-    const char *tb = uniform_ptr(tens + (size_t)kt * 4 * 32 * K);
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns)
-      dma16(tvoff[ns], tb, c.lds0 + tdst + tbuf * kTbuf + ns * kTslot);
+    for (int d = 0; d < L::kDmaPerIter; ++d) dma_one(d, ka, kt, abuf, tbuf);
   };
   auto decode = [&](int tbuf, uint32_t (&bw)[4][8]) {
 #pragma unroll
@@ -451,7 +473,9 @@ __device__ __forceinline__ void wide_stage(const WideArgs &c, char *smem, const 
   };
   // multiply A[abuf] by the current B registers while decoding the next
   // k-block from T[tbuf] into nxt, interleaved unit by unit
-  auto step = [&](int abuf, int tbuf, const uint32_t (&cur)[4][8], uint32_t (&nxt)[4][8]) {
+  // issuing k-block (ka, kt) into (dabuf, dtbuf) one DMA at a time
+  auto step = [&](int abuf, int tbuf, const uint32_t (&cur)[4][8], uint32_t (&nxt)[4][8],
+                  int ka, int kt, int dabuf, int dtbuf) {
     uint32_t r[4][ND];
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns)
@@ -475,7 +499,9 @@ __device__ __forceinline__ void wide_stage(const WideArgs &c, char *smem, const 
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) column_normalize<K>(r[ns], shift, N[ns]);
     __builtin_amdgcn_sched_barrier(0);
-    wide_units<K, MS>(N, mask, af, bf, pacc, nxt, std::make_integer_sequence<int, 32>{});
+    auto dma = [&](int d) { dma_one(d, ka, kt, dabuf, dtbuf); };
+    wide_units<K, MS, L::kDmaPerIter>(N, mask, af, bf, pacc, nxt, dma,
+                                      std::make_integer_sequence<int, 32>{});
   };
 
   uint32_t bA[4][8], bB[4][8];
@@ -485,7 +511,7 @@ __device__ __forceinline__ void wide_stage(const WideArgs &c, char *smem, const 
   const char *t0 = uniform_ptr(tens);
 #pragma unroll
   for (int ns = 0; ns < 4; ++ns)
-    dma16(tvoff[ns], t0, c.lds0 + tdst + 0 * kTbuf + ns * kTslot);
+    if (lane < SEG / 16) dma16(tvoff[ns], t0, c.lds0 + tdst + 0 * kTbuf + ns * kTslot);
   issue(0, min(1, last), 0, 1);
   issue(min(1, last), min(2, last), 1, 2);
   wait_vmcnt<2 * L::kDmaPerIter>();
@@ -493,13 +519,14 @@ __device__ __forceinline__ void wide_stage(const WideArgs &c, char *smem, const 
   decode(0, bA);
 
   // iteration kb: A[kb] in abuf kb%3, T[kb+1] in tbuf (kb+1)%3; issue
-  // A[kb+2] -> abuf (kb+2)%3 and T[kb+3] -> tbuf kb%3
+  // A[kb+2] -> abuf (kb+2)%3 and T[kb+3] -> tbuf kb%3, spread over the
+  // iteration's units (both buffers were last read in iteration kb-1)
 #define EXL3_WIDE_ITER(KB, AB, TB_NEXT, CUR, NXT)                                       \
   {                                                                                     \
     wait_vmcnt<L::kDmaPerIter>();                                                       \
     __syncthreads();                                                                    \
-    issue(min((KB) + 2, last), min((KB) + 3, last), ((AB) + 2) % 3, (AB));               \
-    step((AB), (TB_NEXT), CUR, NXT);                                                    \
+    step((AB), (TB_NEXT), CUR, NXT, min((KB) + 2, last), min((KB) + 3, last),           \
+         ((AB) + 2) % 3, (AB));                                                         \
   }
   int kb = 0;
   for (; kb + 6 <= nkb; kb += 6) {
@@ -589,7 +616,7 @@ __device__ __forceinline__ void wide_item(const GemmParams &p, char *smem, int b
   const int msub = (c.nrows + 15) >> 4;
 
   // A chunk ch of this wave: 8 rows x 128 B; lane L -> row 8 rg + L/8, LDS
-  // slot L%8 holding the global 16-byte chunk (L%8) ^ (row & 7) (swizzle).
+  // slot L%8 holding the global 16-byte chunk (L%8) ^ a_swizzle(row & 15).
   c.abase = (const char *)(p.A + (int64_t)c.row0 * p.lda);
 #pragma unroll
   for (int ch = 0; ch < L::kAChunks; ++ch) {
@@ -597,7 +624,7 @@ __device__ __forceinline__ void wide_item(const GemmParams &p, char *smem, int b
     const int q = f >> 4, rg = f & 15;
     const int r = 8 * rg + (lane >> 3);
     const int rs = min(r, c.nrows - 1);
-    const int gc = (lane & 7) ^ (r & 7);
+    const int gc = (lane & 7) ^ a_swizzle(r & 15);
     c.avoff[ch] = (uint32_t)(2 * ((int64_t)rs * p.lda + q * p.a_proj_stride + gc * 8));
     c.adst[ch] = (uint32_t)(L::kAOff + q * kAbuf + rg * 1024);
   }
@@ -676,14 +703,18 @@ __device__ __forceinline__ void wide_item(const GemmParams &p, char *smem, int b
   epilogue<EPI>(p, T, L::kLd, kWBM * L::kLd, c.e, c.row0, c.nrows, c.colbase, nblk);
 }
 
-// One workgroup per (tile, 256-column block). The host rounds the tile
-// count up to a multiple of 8: workgroups are dealt to the 8 XCDs
-// round-robin by linear id (x fastest), so every column block of a tile runs
-// on the same XCD and shares its L2 copy of the tile's A rows.
+// One workgroup per (tile, 256-column block) on a 1-D grid of groups of 8
+// tiles x nb column blocks. Workgroups are dealt to the 8 XCDs round-robin by
+// linear id, so tile 8 G + (id % 8) keeps all its column blocks on one XCD
+// (sharing its L2 copy of the tile's A rows), and the dispatch order walks
+// the tiles front to back: tiles past the device's tile count (the launch is
+// sized for the worst case) come last and exit at once.
 template <int EPI, bool MULTI>
-__global__ void __launch_bounds__(256, 1) gemm_wide_kernel(GemmParams p) {
+__global__ void __launch_bounds__(256, 1) gemm_wide_kernel(GemmParams p, int nb) {
   __shared__ __attribute__((aligned(16))) char smem[WideLds<EPI>::kBytes];
-  wide_item<EPI, MULTI>(p, smem, blockIdx.x, blockIdx.y);
+  const int id = blockIdx.x, per = 8 * nb;
+  const int grp = id / per, r = id - grp * per;
+  wide_item<EPI, MULTI>(p, smem, 8 * grp + (r & 7), r >> 3);
 }
 
 hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks, hipStream_t s,
@@ -692,8 +723,9 @@ hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks, hip
   const dim3 grid(tiles, nblocks);
   const bool multi = p.proj[0].num_stages > 1 || (epi == EPI_GATEUP && p.proj[1].num_stages > 1);
   if (wide) {
-    const dim3 wgrid((tiles + 7) / 8 * 8, nblocks);
-#define EXL3_WIDE(E, M) hipLaunchKernelGGL((gemm_wide_kernel<E, M>), wgrid, dim3(256), 0, s, p)
+    const dim3 wgrid((unsigned)((tiles + 7) / 8 * 8 * nblocks));
+#define EXL3_WIDE(E, M) \
+  hipLaunchKernelGGL((gemm_wide_kernel<E, M>), wgrid, dim3(256), 0, s, p, nblocks)
     switch (epi) {
       case EPI_GATEUP: if (multi) EXL3_WIDE(EPI_GATEUP, true); else EXL3_WIDE(EPI_GATEUP, false); break;
       case EPI_DOWN: if (multi) EXL3_WIDE(EPI_DOWN, true); else EXL3_WIDE(EPI_DOWN, false); break;
