@@ -330,6 +330,24 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void *sbase, uint32_t
       : "memory");
 }
 
+// dma16 with only the lanes in `lanes` active. The exec mask is narrowed and
+// restored inside one asm block, so the caller's code stays one basic block
+// (a branch would split the scheduling units of the pipelined loop).
+__device__ __forceinline__ void dma16_lanes(uint32_t voff, const void *sbase, uint32_t lds_base,
+                                            uint64_t lanes) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_and_b64 exec, exec, %4\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_base), "s"(lanes)
+      : "memory");
+}
+
 __device__ __forceinline__ const char *uniform_ptr(const char *ptr) {
   const uint64_t b = (uint64_t)(uintptr_t)ptr;
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
@@ -418,6 +436,7 @@ __device__ __forceinline__ void wide_stage(const WideArgs &c, char *smem, const 
   constexpr int ND = Geom<K>::kLoadDw;
   constexpr int TD = Geom<K>::kTileDw;
   constexpr int SEG = 128 * K;               // bytes of a strip's k-block (4 tiles)
+  constexpr uint64_t kSegLanes = (SEG >= 1024) ? ~0ull : ((1ull << (SEG / 16)) - 1);
   const int lane = c.lane, g = lane >> 4, n = lane & 15;
   const int nkb = c.nkb;
 
@@ -454,7 +473,8 @@ __device__ __forceinline__ void wide_stage(const WideArgs &c, char *smem, const 
     } else {
       const int ns = d - L::kAChunks;
       const char *tb = uniform_ptr(tens + (size_t)kt * 4 * 32 * K);
-      if (lane < SEG / 16) dma16(tvoff[ns], tb, c.lds0 + tdst + tbuf * kTbuf + ns * kTslot);
+      if constexpr (SEG >= 1024) dma16(tvoff[ns], tb, c.lds0 + tdst + tbuf * kTbuf + ns * kTslot);
+      else dma16_lanes(tvoff[ns], tb, c.lds0 + tdst + tbuf * kTbuf + ns * kTslot, kSegLanes);
     }
   };
   auto issue = [&](int ka, int kt, int abuf, int tbuf) {
@@ -511,7 +531,7 @@ __device__ __forceinline__ void wide_stage(const WideArgs &c, char *smem, const 
   const char *t0 = uniform_ptr(tens);
 #pragma unroll
   for (int ns = 0; ns < 4; ++ns)
-    if (lane < SEG / 16) dma16(tvoff[ns], t0, c.lds0 + tdst + 0 * kTbuf + ns * kTslot);
+    dma16_lanes(tvoff[ns], t0, c.lds0 + tdst + 0 * kTbuf + ns * kTslot, kSegLanes);
   issue(0, min(1, last), 0, 1);
   issue(min(1, last), min(2, last), 1, 2);
   wait_vmcnt<2 * L::kDmaPerIter>();
