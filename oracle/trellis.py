@@ -6,8 +6,11 @@ Description) and that residual stages use an "MCG" codebook (exllamav3 #284,
 API contract), but they define neither the codebook nor the bit layout. This
 library fixes its own format, restated here so the oracle can be read alone:
 
-  codebook   h = (s * 0x9E37) mod 2**16 ; a = h >> 6 ; b = h mod 2**10 ;
-             CB(s) = (a - b) / 1024, an exact fp16 value in [-1008, 1008]/1024
+  codebook   h = (s * 0x9E37) mod 2**16 (one step of a multiplicative
+             congruential generator) ; sign = bit 15 of h ;
+             e = bits 10..11 of h ; m = bits 0..9 of h ;
+             CB(s) = (-1)**sign * 2**(e - 3) * (1 + m / 1024),
+             an exact fp16 value with magnitude in [1/8, 2047/1024]
   tile       16 (input k) x 16 (output n) weights, a stream of 256*K bits
              stored as 16*K little-endian uint16 words; stream bit j is bit
              (j mod 16) of word j // 16
@@ -34,13 +37,15 @@ STATE_BITS = 16
 def codebook(states):
     """MCG16 codebook value of 16-bit trellis states, as float64.
 
-    Written from the integer definition above (not from any fp16 bit trick).
+    Written from the sign / exponent / mantissa definition above (not from
+    any fp16 bit pattern).
     """
-    s = np.asarray(states).astype(np.int32) & 0xFFFF
+    s = np.asarray(states).astype(np.int64) & 0xFFFF
     h = (s * MCG_MULT) & 0xFFFF
-    a = h >> 6
-    b = h & 0x3FF
-    return (a - b) / 1024.0
+    sign = np.where((h >> 15) & 1, -1.0, 1.0)
+    e = (h >> 10) & 3
+    m = h & 0x3FF
+    return sign * np.exp2(e - 3.0) * (1.0 + m / 1024.0)
 
 
 def _stream_bits(words):

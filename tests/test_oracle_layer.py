@@ -63,20 +63,19 @@ def test_zero_scale_equals_absent_stage():
 def test_all_zero_and_all_ones_streams_closed_form():
     p = _small_proj(7)
     x = np.random.default_rng(4).standard_normal((2, 256)).astype(np.float16)
-    p.words[0][0] = np.zeros_like(p.words[0][0])
-    assert np.all(linear.linear(x, p, "R") == 0.0)
-    p.words[0][0] = np.full_like(p.words[0][0], 0xFFFF)
-    y = linear.linear(x, p, "R")
-    # W == -66/1024 everywhere: acc[n] = c * sum_k x~_k for every n, so the
-    # output rotation puts sqrt(128) * c * S at n = 0 mod 128 and 0 elsewhere
     xt = linear.rotate_input(x, p, 0, "R")
     S = xt.sum(axis=1, keepdims=True)
-    c = -66 / 1024
     svh = p.svh[0].astype(np.float64)
     cs = p.chscale[0].astype(np.float64)
-    expect = np.zeros_like(y)
-    expect[:, ::128] = np.sqrt(128) * c * S * svh[::128] * cs[::128]
-    assert np.allclose(y, expect, rtol=1e-12, atol=1e-12)
+    # all-zero stream: every state 0 -> W == 1/8; all-ones: W == 1481/8192.
+    # A constant W == c gives acc[n] = c * sum_k x~_k for every n, so the
+    # output rotation puts sqrt(128) * c * S at n = 0 mod 128 and 0 elsewhere
+    for fill, c in ((0x0000, 0.125), (0xFFFF, 1481 / 8192)):
+        p.words[0][0] = np.full_like(p.words[0][0], fill)
+        y = linear.linear(x, p, "R")
+        expect = np.zeros_like(y)
+        expect[:, ::128] = np.sqrt(128) * c * S * svh[::128] * cs[::128]
+        assert np.allclose(y, expect, rtol=1e-12, atol=1e-12)
 
 
 def _tiny_moe(E=8, topk=2, H=256, I=384, rows=6, seed=11, bad=True):

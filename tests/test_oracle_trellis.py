@@ -17,22 +17,30 @@ def _rows(name):
 
 def test_codebook_test_vectors():
     for s, v in _rows("codebook_values.txt"):
-        assert trellis.codebook(int(s, 16)) * 1024 == int(v)
+        assert trellis.codebook(int(s, 16)) * 8192 == int(v)
 
 
 def test_codebook_closed_form_properties():
-    v = trellis.codebook(np.arange(65536)) * 1024
-    # every value is an integer multiple of 2^-10 (exact in fp16)
+    v = trellis.codebook(np.arange(65536)) * 8192
+    # every value is an integer multiple of 2^-13 (exact in fp16)
     assert np.all(v == np.round(v))
-    # a - b = 16u - 63v - c with a = 16u + v, c = h mod 64: range [-1008, 1008]
-    assert v.min() == -1008 and v.max() == 1008
-    assert len(np.unique(v)) == 2017
-    # the hash is a bijection of 16-bit states, so the mean is the mean of
-    # 16u - 63v - c over all (u, v, c): 16*31.5 - 63*7.5 - 31.5 = 0
+    # magnitudes 2^(e-3) (1 + m/1024), e in 0..3, m in 0..1023:
+    # [1024, 8 * 2047] / 8192
+    a = np.abs(v)
+    assert a.min() == 1024 and a.max() == 8 * 2047
+    # the hash is a bijection of 16-bit states and bits 12..14 of h are
+    # unused: every (sign, e, m) appears exactly 8 times
+    vals, counts = np.unique(v, return_counts=True)
+    assert len(vals) == 2 * 4 * 1024 and np.all(counts == 8)
+    # sign is bit 15 of a bijection: exact zero mean
     assert v.sum() == 0
+    # mean square: (1/4) sum_e 4^(e-3) * mean_m (1 + m/1024)^2
+    m = np.arange(1024)
+    ms = np.mean([4.0 ** (e - 3) for e in range(4)]) * np.mean((1 + m / 1024) ** 2)
+    assert abs(np.mean((v / 8192) ** 2) - ms) < 1e-12
     # fp16 representability of every codebook value
-    f = (v / 1024).astype(np.float16).astype(np.float64)
-    assert np.array_equal(f, v / 1024)
+    f = (v / 8192).astype(np.float16).astype(np.float64)
+    assert np.array_equal(f, v / 8192)
 
 
 @pytest.mark.parametrize("K", range(2, 9))
@@ -41,7 +49,7 @@ def test_tile_test_vectors(K):
     b = np.array([(37 * j + 11) % 256 for j in range(32 * K)], dtype=np.uint8)
     words = b.view("<u2")[None, :]
     for dec in (trellis.decode_tiles_window, trellis.decode_tiles_shift):
-        W = dec(words, K)[0] * 1024
+        W = dec(words, K)[0] * 8192
         got = [W[0, 0], W[1, 0], W[0, 1], W[15, 15], W.sum(), (W * W).sum()]
         assert [int(round(g)) for g in got] == [int(x) for x in row[1:]]
 
@@ -59,8 +67,10 @@ def test_two_decoders_agree(K):
 def test_constant_streams(K):
     zero = np.zeros((1, 16 * K), np.uint16)
     ones = np.full((1, 16 * K), 0xFFFF, np.uint16)
-    assert np.all(trellis.decode_tiles_window(zero, K) == 0.0)
-    assert np.all(trellis.decode_tiles_shift(ones, K) == -66 / 1024)
+    # all states 0 -> h = 0 -> 1/8; all states 0xFFFF -> h = 0x61C9 -> 1481/8192
+    for dec in (trellis.decode_tiles_window, trellis.decode_tiles_shift):
+        assert np.all(dec(zero, K) == 0.125)
+        assert np.all(dec(ones, K) == 1481 / 8192)
 
 
 @pytest.mark.parametrize("K", [3, 4, 7])
@@ -90,7 +100,9 @@ def test_tensor_order_is_out_major():
     start = (1 * kt_n + 2) * 16 * K
     w[start:start + 16 * K] = 0xFFFF
     W = trellis.dequantize(w, fin, fout, K)
-    expect = np.zeros((fin, fout))
-    expect[32:48, 16:32] = -66 / 1024
+    # every all-zero tile decodes to the constant 1/8, the all-ones tile to
+    # the constant 1481/8192
+    expect = np.full((fin, fout), 0.125)
+    expect[32:48, 16:32] = 1481 / 8192
     assert np.array_equal(W, expect)
-    assert np.array_equal(trellis.dequantize(w, fin, fout, K, "shift"), W)
+    assert np.array_equal(trellis.dequantize(w, fin, fout, K, "window"), W)

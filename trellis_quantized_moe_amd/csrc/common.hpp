@@ -6,7 +6,8 @@
 // MCG codebook but define neither — exllamav3 PR #284 "MoE: Add fused
 // additive EXL3 kernels", API contract; TensorFold PR #837, What this
 // changes):
-//   CB(s)  = ((h >> 6) - (h & 1023)) / 1024,  h = s * 0x9E37 mod 2^16
+//   CB(s)  = (-1)^h[15] * 2^(h[11:10] - 3) * (1 + h[9:0]/1024),
+//            h = s * 0x9E37 mod 2^16; as fp16 bits: (h & 0x8FFF) | 0x3000
 //   tile   16 (k) x 16 (n) weights, 256*K-bit tail-biting stream; the state of
 //          weight i is the 16 stream bits ending at bit i*K + K - 1; weight i
 //          sits at (k = i mod 16, n = i / 16)
@@ -41,26 +42,21 @@ __device__ __forceinline__ int sigma_inv(int k) {
 
 // ---------------------------------------------------------------- codebook
 // Two MCG16 states in the 16-bit halves of s2 -> two fp16 codebook values.
-// (1 + a/1024) - (1 + b/1024) is exact in fp16, so the packed add returns
-// (a - b)/1024 exactly: v_pk_mul_lo_u16, v_pk_lshrrev_b16, v_or_b32,
-// v_and_or_b32, v_pk_add_f16.
-__device__ __forceinline__ uint32_t codebook2(uint32_t s2, uint32_t mask_lo10) {
+// Bit 15 of h is the fp16 sign, bits 10..11 the low exponent bits under a
+// fixed 0b011 (exponent 12..15), bits 0..9 the mantissa: one
+// v_pk_mul_lo_u16 and one v_and_or_b32 (mask in a VGPR, OR constant in an
+// SGPR) per two weights.
+__device__ __forceinline__ uint32_t codebook2(uint32_t s2, uint32_t mask) {
   u16x2 s = __builtin_bit_cast(u16x2, s2);
   u16x2 h = s * (u16x2){(unsigned short)0x9E37, (unsigned short)0x9E37};
-  u16x2 a = h >> (u16x2){6, 6};
-  const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-  uint32_t A = __builtin_bit_cast(uint32_t, a) | 0x3C003C00u;
-  // (h & 0x03FF03FF) | 0xBC00BC00 is one v_and_or_b32 when the mask sits in a
-  // VGPR (gfx9 VOP3 takes no literal; the OR constant goes to an SGPR)
-  const uint32_t B = (hb & mask_lo10) | 0xBC00BC00u;
-  f16x2 r = __builtin_bit_cast(f16x2, A) + __builtin_bit_cast(f16x2, B);
-  return __builtin_bit_cast(uint32_t, r);
+  return (__builtin_bit_cast(uint32_t, h) & mask) | 0x30003000u;
 }
 
-// A VGPR holding 0x03FF03FF that the compiler cannot fold back into a literal.
+// A VGPR holding 0x8FFF8FFF that the compiler cannot fold back into a literal
+// (gfx9 VOP3 encodings take no literal operand).
 __device__ __forceinline__ uint32_t codebook_mask() {
   uint32_t m;
-  asm volatile("v_mov_b32 %0, 0x3ff03ff" : "=v"(m));
+  asm volatile("v_mov_b32 %0, 0x8fff8fff" : "=v"(m));
   return m;
 }
 
