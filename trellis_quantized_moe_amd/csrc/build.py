@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libexl3moe.so")
-SOURCES = ["gemm.hip", "rotate.hip", "combine.hip", "route_pack.hip", "host.cpp"]
+SOURCES = ["gemm.hip", "gemm_wide.hip", "rotate.hip", "combine.hip", "route_pack.hip", "host.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -91,10 +91,17 @@ struct ColumnWindow {
   }
 };
 
-// 32 bits of the normalised window starting at bit OFF (bits < 0 read 0).
-template <int K, int OFF>
-__device__ __forceinline__ uint32_t window32(const uint32_t (&N)[Geom<K>::kNormDw]) {
-  constexpr int NN = Geom<K>::kNormDw;
+// Geometry of half a tile column (8 consecutive states): the window is
+// 7K + 16 bits long.
+template <int K>
+struct HalfGeom {
+  static constexpr int kLoadDw = (7 * K + 16 + 31 + 31) / 32;  // at any bit offset
+  static constexpr int kNormDw = (7 * K + 16 + 31) / 32;       // shifted to bit 0
+};
+
+// 32 bits of a normalised window N starting at bit OFF (bits < 0 read 0).
+template <int OFF, int NN>
+__device__ __forceinline__ uint32_t window32(const uint32_t (&N)[NN]) {
   if constexpr (OFF < 0) {
     return N[0] << (-OFF);
   } else {
@@ -109,20 +116,67 @@ __device__ __forceinline__ uint32_t window32(const uint32_t (&N)[Geom<K>::kNormD
   }
 }
 
-// Decode one tile column (16 states) from its raw dwords into 8 packed fp16
-// pairs. Register v holds states (j, j+4) with j = (v & 3) + 8 * (v >> 2),
-// so registers 0..3 feed k = {0,4,1,5,2,6,3,7} and 4..7 feed
-// k = {8,12,9,13,10,14,11,15} of the tile column: the kSigma order.
+// Dword D of a normalised window, 0 past its end.
+template <int D, int NN>
+__device__ __forceinline__ uint32_t norm_dw(const uint32_t (&N)[NN]) {
+  if constexpr (D < NN) return N[D];
+  else return 0u;
+}
+
+// Raw dwords of a window (ND of them, the window starting at bit `shift` of
+// raw[0]) shifted down to bit 0 (NN dwords).
+template <int ND, int NN>
+__device__ __forceinline__ void normalize(const uint32_t (&raw)[ND], uint32_t shift,
+                                          uint32_t (&N)[NN]) {
+#pragma unroll
+  for (int j = 0; j < NN; ++j) {
+    const uint32_t hi = (j + 1 < ND) ? raw[(j + 1 < ND) ? j + 1 : j] : 0u;
+    N[j] = __builtin_amdgcn_alignbit(hi, raw[j], shift);
+  }
+}
+
 // The window of one tile column shifted to bit 0 (kNormDw dwords).
 template <int K>
 __device__ __forceinline__ void column_normalize(const uint32_t (&raw)[Geom<K>::kLoadDw],
                                                  uint32_t shift,
                                                  uint32_t (&N)[Geom<K>::kNormDw]) {
-  constexpr int ND = Geom<K>::kLoadDw, NN = Geom<K>::kNormDw;
-#pragma unroll
-  for (int j = 0; j < NN; ++j) {
-    const uint32_t hi = (j + 1 < ND) ? raw[(j + 1 < ND) ? j + 1 : j] : 0u;
-    N[j] = __builtin_amdgcn_alignbit(hi, raw[j], shift);
+  normalize(raw, shift, N);
+}
+
+// States (j, j + 4) of a normalised window (state i starting at bit iK) in
+// the low and high 16-bit halves of one dword (bits above a state's 16 are
+// don't-care for the 16-bit hash). State j starts at bit o1 = jK, state
+// j + 4 at o2 = o1 + 4K. Chosen per (K, j) at compile time:
+//   4K == 16          one funnel shift (K = 4)
+//   both byte-aligned one or two byte permutes of the window dwords (K = 8;
+//                     K = 6 and K = 2 for j = 0 mod 4)
+//   4K == 8           one funnel shift and a byte permute (K = 2)
+//   otherwise         two funnel shifts and a byte permute
+// v_perm_b32 byte selector s picks byte s of {hi, lo} (0..3 from lo).
+template <int K, int j, int NN>
+__device__ __forceinline__ uint32_t column_pair(const uint32_t (&N)[NN]) {
+  constexpr int o1 = j * K, o2 = (j + 4) * K;
+  if constexpr (o2 - o1 == 16) {
+    return window32<o1>(N);
+  } else if constexpr (o1 % 8 == 0 && o2 % 8 == 0) {
+    constexpr int w = o1 / 32;
+    constexpr uint32_t b1 = o1 / 8 - 4 * w, b2 = o2 / 8 - 4 * w;
+    if constexpr (b2 + 1 <= 7) {
+      constexpr uint32_t sel = b1 | ((b1 + 1) << 8) | (b2 << 16) | ((b2 + 1) << 24);
+      return __builtin_amdgcn_perm(norm_dw<w + 1>(N), N[w], sel);
+    } else {
+      // b2 = 7: byte b2 + 1 is byte 0 of dword w + 2
+      constexpr uint32_t sel1 = b1 | ((b1 + 1) << 8) | (b2 << 16) | (b2 << 24);
+      const uint32_t t = __builtin_amdgcn_perm(norm_dw<w + 1>(N), N[w], sel1);
+      return __builtin_amdgcn_perm(norm_dw<w + 2>(N), t, 0x04020100u);
+    }
+  } else if constexpr (o2 - o1 == 8) {
+    const uint32_t x = window32<o1>(N);
+    return __builtin_amdgcn_perm(x, x, 0x02010100u);
+  } else {
+    const uint32_t lo = window32<o1>(N);
+    const uint32_t hi = window32<o2 - 16>(N);
+    return __builtin_amdgcn_perm(hi, lo, 0x07060100u);
   }
 }
 
@@ -133,9 +187,14 @@ template <int K, int V>
 __device__ __forceinline__ uint32_t column_reg(const uint32_t (&N)[Geom<K>::kNormDw],
                                                uint32_t mask) {
   constexpr int j = (V & 3) + 8 * (V >> 2);
-  const uint32_t lo = window32<K, j * K>(N);
-  const uint32_t hi = window32<K, (j + 4) * K - 16>(N);
-  return codebook2((lo & 0x0000FFFFu) | (hi & 0xFFFF0000u), mask);
+  return codebook2(column_pair<K, j>(N), mask);
+}
+
+// Register r (0..3) of a decoded half column (window normalised to its first
+// state): states (r, r + 4) of the half, fp16 k-slots {0,4,1,5,2,6,3,7}.
+template <int K, int r, int NN>
+__device__ __forceinline__ uint32_t half_reg(const uint32_t (&N)[NN], uint32_t mask) {
+  return codebook2(column_pair<K, r>(N), mask);
 }
 
 // Decode one tile column (16 states) from its raw dwords into 8 packed fp16

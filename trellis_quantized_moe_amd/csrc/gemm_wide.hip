@@ -1,0 +1,503 @@
+// Grouped EXL3 GEMM on 128-row tiles (prefill-size work) for gfx950: the
+// trellis is decoded straight into MFMA B operands and multiplied with fp16
+// MFMA into fp32 accumulators. Additive stages and the shared epilogues are
+// handled here too.
+//
+// What is computed follows TensorFold PR #837 "cuda: EXL3 linear and grouped
+// routed experts, every codebook and width, a width per expert" (What this
+// changes: decode straight into the matrix-core operands; grouped experts with
+// SwiGLU and down) and exllamav3 PR #284 "MoE: Add fused additive EXL3
+// kernels" (Summary: FP32 accumulation and output scaling; stage tables with
+// zero-scale sparse entries). The per-element arithmetic is the one the
+// narrow kernel uses: for each output, an MFMA chain over ascending 32-input
+// k-steps (each two whole trellis tiles) starting from 0, then
+// acc = fmaf(s_t, P_t, acc) over the stages, then the shared epilogue.
+//
+// Tile: 128 rows x 256 columns per workgroup of 4 waves. Wave w owns 64
+// output columns (4 strips of 16) over all 128 rows (8 MFMA row blocks): 32
+// 16x16 fp32 accumulator blocks, held in AGPRs. GATEUP: waves 0-1 compute gate
+// and waves 2-3 compute up (128 columns each), so the epilogue has both
+// halves of SwiGLU in one workgroup.
+//
+// Two workgroups share a CU (80 KB of LDS and at most 256 registers per wave
+// each). On gfx950 a wave's VALU work and its own MFMAs do not overlap, while
+// the VALU decode of one wave does run under the MFMAs of the other wave on
+// the same SIMD.
+//
+// Pipeline over 32-input stages (one MFMA k-step; 2 trellis tiles along k):
+//  - A (rotated activations) is copied global->LDS by DMA into a ring of 3
+//    slots. Each wave copies a quarter and all waves read all of it, so one
+//    barrier per stage publishes it.
+//  - Trellis words are copied global->LDS by DMA into a ring of 4 slots per
+//    wave. A wave copies and reads only its own strips, so its own vmcnt
+//    wait is enough (no barrier).
+//  - In stage ks a wave multiplies A[ks] by B[ks], which it decoded in the
+//    previous stage into registers. Meanwhile it decodes T[ks+1] into the
+//    other register set and issues the DMAs of A[ks+2] and then T[ks+4].
+//    The work is cut into units of two MFMAs plus a share of the decode,
+//    separated by scheduling barriers.
+//  - Lane (g, n) of a strip decodes states 8(g & 1) .. 8(g & 1) + 7 of column
+//    n of tile g >> 1: the 8 k-entries the MFMA takes from that lane, in the
+//    kSigma order of the rotated activations.
+//  - Every wave issues the same DMAs in every stage (past the end it
+//    re-copies the last stage). The wait for A[ks] and T[ks+1] is therefore an
+//    exact vmcnt that leaves T[ks+2], A[ks+1] and T[ks+3] in flight.
+#include <utility>
+
+#include "gemm_shared.hpp"
+
+namespace exl3 {
+
+constexpr int kWBM = 128;
+constexpr int kARing = 3;
+constexpr int kTRing = 4;
+constexpr int kArow = 64;             // bytes of one A row per stage (32 fp16)
+constexpr int kAbuf = kWBM * kArow;   // one projection's A stage: 8 KB
+constexpr int kTstrip = 512;          // one strip's stage: 2 tiles of 32K bytes (K <= 8)
+constexpr int kTwave = 4 * kTstrip;   // one wave's 4 strips
+constexpr int kTstage = 4 * kTwave;   // 4 waves
+
+template <int EPI>
+struct WideLds {
+  static constexpr int NPROJ = (EPI == EPI_GATEUP) ? 2 : 1;
+  static constexpr int kCols = (EPI == EPI_GATEUP) ? 128 : 256;  // per projection
+  static constexpr int kLd = kCols + 4;
+  static constexpr int kHalf = 64;  // epilogue rows per round
+  static constexpr int kTileBytes = NPROJ * kHalf * kLd * 4;
+  static constexpr int kAStage = NPROJ * kAbuf;
+  static constexpr int kAOff = 0;
+  static constexpr int kTOff = kARing * kAStage;
+  static constexpr int kRingBytes = kTOff + kTRing * kTstage;
+  static constexpr int kBytes = kTileBytes > kRingBytes ? kTileBytes : kRingBytes;
+  static constexpr int kAChunks = NPROJ * 8 / 4;  // 1 KB A chunks per wave per stage
+  static constexpr int kTDma = 2;                 // trellis DMAs per wave per stage
+  static constexpr int kDma = kAChunks + kTDma;
+};
+static_assert(WideLds<EPI_GATEUP>::kBytes <= 80 * 1024, "two workgroups per CU");
+static_assert(WideLds<EPI_LINEAR>::kBytes <= 80 * 1024, "two workgroups per CU");
+
+// 16-byte chunk swizzle of A row r (0..15 inside its 16-row block); a row is
+// 64 bytes (4 chunks). The 8 lanes that read (rows 0..7 or 8..15, one chunk
+// index) hit 8 distinct 16-byte groups of a 128-byte bank window, and the 16
+// lanes of rows 0..15 hit 16 distinct groups of a 256-byte window.
+__device__ __forceinline__ int a_swizzle(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// 16-byte-per-lane global->LDS copy: lane L reads sbase + voff and writes
+// LDS byte m0 + 16 L. The wave's LDS destination goes through m0.
+__device__ __forceinline__ void dma16(uint32_t voff, const void *sbase, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory");
+}
+
+// dma16 with only the lanes in `lanes` active. The exec mask is narrowed and
+// restored inside one asm block, so the caller's code stays one basic block
+// (a branch would split the scheduling units of the pipelined loop).
+__device__ __forceinline__ void dma16_lanes(uint32_t voff, const void *sbase, uint32_t lds_base,
+                                            uint64_t lanes) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_and_b64 exec, exec, %4\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_base), "s"(lanes)
+      : "memory");
+}
+
+__device__ __forceinline__ const char *uniform_ptr(const char *ptr) {
+  const uint64_t b = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  return (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+struct WideArgs {
+  int e, row0, nrows, nb, w, pj, lane, nks, colbase;
+  const char *abase;     // A rows of the tile (uniform)
+  uint32_t avoff[4];     // per A chunk: lane's byte offset from abase
+  uint32_t adst[4];      // per A chunk: LDS byte offset inside an A slot (uniform)
+  uint32_t lds0;         // LDS address of smem
+};
+
+// Decoded B registers of one stage: one MFMA B operand per strip.
+typedef u32x4 BRegs[4];
+
+// Per-stage context of one wave.
+template <int EPI, int K, int MS>
+struct WideIter {
+  using L = WideLds<EPI>;
+  static constexpr int ND = HalfGeom<K>::kLoadDw, NN = HalfGeom<K>::kNormDw;
+  static constexpr int U = 2 * MS;     // units per stage, two MFMAs each
+  static constexpr int PPU = 16 / U;   // decode pairs per unit
+  static constexpr int SEG = 64 * K;   // bytes of a strip's stage
+  static constexpr uint64_t kHalfLanes = (SEG >= 512) ? 0xFFFFFFFFull : ((1ull << (SEG / 16)) - 1);
+  static constexpr uint64_t kSegLanes = kHalfLanes | (kHalfLanes << 32);
+
+  const WideArgs &c;
+  const char *smem;
+  const char *tens;
+  uint32_t shift, mask;
+  uint32_t tvoff[2];
+  uint32_t traddr[ND];
+  uint32_t afrag;
+  uint32_t tdst;  // LDS address of this wave's T region (uniform)
+
+  // one stage's working set
+  uint32_t raw[4][ND];
+  uint32_t N[NN];
+  f16x8 af[3];
+  uint32_t ar;  // A fragment address in the current slot
+
+  __device__ __forceinline__ WideIter(const WideArgs &c_, const char *smem_, const char *tens_,
+                                      int nt0, int ktiles)
+      : c(c_), smem(smem_), tens(tens_) {
+    const int lane = c.lane, g = lane >> 4, n = lane & 15;
+    const int sl = lane & 31;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const int ns = 2 * d + (lane >> 5);
+      tvoff[d] = (uint32_t)((nt0 + ns) * ktiles * 32 * K + 16 * min(sl, SEG / 16 - 1));
+    }
+    tdst = uniform_u32(c.lds0 + L::kTOff + c.w * kTwave);
+    // window of states 8h .. 8h+7 of column n of tile t: first bit
+    // 16nK + 8hK + K - 16 of the tile's tail-biting stream
+    const int t = g >> 1, h = g & 1;
+    const int b = 16 * n * K + 8 * h * K + K - 16;
+    const int d0 = b >> 5;  // floor
+    shift = (uint32_t)(b & 31);
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+      int d = d0 + j;
+      d += (d < 0) ? 8 * K : 0;
+      d -= (d >= 8 * K) ? 8 * K : 0;
+      traddr[j] = (uint32_t)(L::kTOff + c.w * kTwave + t * 32 * K + 4 * d);
+    }
+    afrag = (uint32_t)(L::kAOff + c.pj * kAbuf + n * kArow + ((g ^ a_swizzle(n)) * 16));
+    mask = codebook_mask();
+  }
+
+  // DMA d (0 .. kDma-1) of stages (ka, kt) into slots (sa, st): A chunks
+  // first, then the trellis (two strips per DMA).
+  __device__ __forceinline__ void dma(int d, int ka, int kt, int sa, int st) const {
+    if (d < L::kAChunks) {
+      const char *ab = uniform_ptr(c.abase + (size_t)ka * kArow);
+      dma16(c.avoff[d], ab, uniform_u32(c.lds0 + c.adst[d] + sa * L::kAStage));
+    } else {
+      const int td = d - L::kAChunks;
+      const char *tb = uniform_ptr(tens + (size_t)kt * 2 * 32 * K);
+      const uint32_t dst = uniform_u32(tdst + st * kTstage + td * 2 * kTstrip);
+      if constexpr (SEG >= 512) dma16(tvoff[td], tb, dst);
+      else dma16_lanes(tvoff[td], tb, dst, kSegLanes);
+    }
+  }
+
+  __device__ __forceinline__ void read_raw(int st) {
+    const uint32_t off = (uint32_t)(st * kTstage);
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+      for (int j = 0; j < ND; ++j)
+        raw[ns][j] = *(const uint32_t *)(smem + traddr[j] + off + ns * kTstrip);
+  }
+
+  template <int Q>
+  __device__ __forceinline__ void decode_pair(BRegs &bn) {
+    constexpr int ns = Q / 4, r = Q % 4;
+    if constexpr (r == 0) normalize(raw[ns], shift, N);
+    bn[ns][r] = half_reg<K, r>(N, mask);
+  }
+  template <int... Qs>
+  __device__ __forceinline__ void decode_seq(BRegs &bn, std::integer_sequence<int, Qs...>) {
+    (decode_pair<Qs>(bn), ...);
+  }
+  template <int Q0, int CNT>
+  __device__ __forceinline__ void decode_range(BRegs &bn) {
+    decode_off<Q0>(bn, std::make_integer_sequence<int, CNT>{});
+  }
+  template <int Q0, int... Is>
+  __device__ __forceinline__ void decode_off(BRegs &bn, std::integer_sequence<int, Is...>) {
+    (decode_pair<Q0 + Is>(bn), ...);
+  }
+
+  __device__ __forceinline__ void load_af(int slot_ms, int ms) {
+    af[slot_ms] = *(const f16x8 *)(smem + ar + ms * 16 * kArow);
+  }
+
+  // Unit u: its DMAs, an A fragment prefetch, PPU decode pairs, two MFMAs.
+  template <int u>
+  __device__ __forceinline__ void unit(const BRegs &bc, BRegs &bn, f32x4 (&pacc)[8][4], int ka,
+                                       int kt, int sa_w, int st_w) {
+    constexpr int ms = u / 2, ns0 = (u & 1) * 2;
+#pragma unroll
+    for (int d = 0; d < L::kDma; ++d)
+      if ((d * U) / L::kDma == u) dma(d, ka, kt, sa_w, st_w);
+    if constexpr ((u & 1) == 0 && ms + 2 < MS) load_af((ms + 2) % 3, ms + 2);
+    decode_range<u * PPU, PPU>(bn);
+    pacc[ms][ns0] = mfma16x16x32(af[ms % 3], __builtin_bit_cast(f16x8, bc[ns0]), pacc[ms][ns0]);
+    pacc[ms][ns0 + 1] =
+        mfma16x16x32(af[ms % 3], __builtin_bit_cast(f16x8, bc[ns0 + 1]), pacc[ms][ns0 + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  template <int... Us>
+  __device__ __forceinline__ void units(const BRegs &bc, BRegs &bn, f32x4 (&pacc)[8][4], int ka,
+                                        int kt, int sa_w, int st_w,
+                                        std::integer_sequence<int, Us...>) {
+    (unit<Us>(bc, bn, pacc, ka, kt, sa_w, st_w), ...);
+  }
+
+  // Stage ks: A[ks] in A slot ks % 3 (= sa), T[ks+1] in T slot (ks+1) % 4.
+  __device__ __forceinline__ void iteration(int ks, int sa, const BRegs &bc, BRegs &bn,
+                                            f32x4 (&pacc)[8][4]) {
+    const int last = c.nks - 1;
+    wait_vmcnt<L::kDma + L::kTDma>();
+    __syncthreads();
+    ar = afrag + (uint32_t)(sa * L::kAStage);
+    load_af(0, 0);
+    load_af(1, 1);
+    read_raw((ks + 1) & 3);
+    const int sa_w = (sa == 0) ? 2 : sa - 1;  // (ks + 2) % 3
+    units(bc, bn, pacc, min(ks + 2, last), min(ks + 4, last), sa_w, ks & 3,
+          std::make_integer_sequence<int, U>{});
+  }
+
+  // One projection stage over all k: pacc += A x W.
+  __device__ __forceinline__ void run(f32x4 (&pacc)[8][4]) {
+    const int nks = c.nks, last = nks - 1;
+    BRegs b0, b1;
+    __syncthreads();  // the LDS rings are free
+    // prologue, in the order of the steady state: T[0], T[1], A[0] T[2],
+    // A[1] T[3]
+#pragma unroll
+    for (int d = L::kAChunks; d < L::kDma; ++d) dma(d, 0, 0, 0, 0);
+#pragma unroll
+    for (int d = L::kAChunks; d < L::kDma; ++d) dma(d, 0, min(1, last), 0, 1);
+#pragma unroll
+    for (int d = 0; d < L::kAChunks; ++d) dma(d, 0, 0, 0, 0);
+#pragma unroll
+    for (int d = L::kAChunks; d < L::kDma; ++d) dma(d, 0, min(2, last), 0, 2);
+#pragma unroll
+    for (int d = 0; d < L::kAChunks; ++d) dma(d, min(1, last), 0, 1, 0);
+#pragma unroll
+    for (int d = L::kAChunks; d < L::kDma; ++d) dma(d, 0, min(3, last), 0, 3);
+    wait_vmcnt<3 * L::kTDma + 2 * L::kAChunks>();  // T[0] (this wave's own copy)
+    read_raw(0);
+    decode_seq(b0, std::make_integer_sequence<int, 16>{});
+    int sa = 0;
+    for (int ks = 0; ks < nks; ks += 2) {  // nks is a multiple of 4
+      iteration(ks, sa, b0, b1, pacc);
+      sa = (sa == 2) ? 0 : sa + 1;
+      iteration(ks + 1, sa, b1, b0, pacc);
+      sa = (sa == 2) ? 0 : sa + 1;
+    }
+    wait_vmcnt<0>();  // no DMA may land after the LDS is reused
+  }
+};
+
+// A wave with no work for this stage still copies its share of A and takes
+// part in the barrier cadence of its workgroup (1 + nks barriers).
+template <int EPI>
+__device__ __forceinline__ void wide_idle_stage(const WideArgs &c) {
+  using L = WideLds<EPI>;
+  const int nks = c.nks, last = nks - 1;
+  auto issue = [&](int ka, int sa) {
+    const char *ab = uniform_ptr(c.abase + (size_t)ka * kArow);
+#pragma unroll
+    for (int ch = 0; ch < L::kAChunks; ++ch)
+      dma16(c.avoff[ch], ab, uniform_u32(c.lds0 + c.adst[ch] + sa * L::kAStage));
+  };
+  __syncthreads();
+  issue(0, 0);
+  issue(min(1, last), 1);
+  int sa = 0;
+  for (int ks = 0; ks < nks; ++ks) {
+    wait_vmcnt<L::kAChunks>();
+    __syncthreads();
+    issue(min(ks + 2, last), (sa == 0) ? 2 : sa - 1);
+    sa = (sa == 2) ? 0 : sa + 1;
+  }
+  wait_vmcnt<0>();
+}
+
+template <int EPI, int K>
+__device__ __forceinline__ void wide_stage_rows(const WideArgs &c, char *smem, const char *tens,
+                                                int nt0, int ktiles, int msub,
+                                                f32x4 (&pacc)[8][4]) {
+  if (msub <= 2) {
+    WideIter<EPI, K, 2> it(c, smem, tens, nt0, ktiles);
+    it.run(pacc);
+  } else if (msub <= 4) {
+    WideIter<EPI, K, 4> it(c, smem, tens, nt0, ktiles);
+    it.run(pacc);
+  } else {
+    WideIter<EPI, K, 8> it(c, smem, tens, nt0, ktiles);
+    it.run(pacc);
+  }
+}
+
+// One work item: rows of tile `bx` times 256-column block `by`.
+template <int EPI, bool MULTI>
+__device__ __forceinline__ void wide_item(const GemmParams &p, char *smem, int bx, int by) {
+  using L = WideLds<EPI>;
+  constexpr int NPROJ = L::NPROJ;
+
+  WideArgs c;
+  if (!tile_of_block(p, kWBM, bx, c.e, c.row0, c.nrows)) return;
+  c.nb = by;
+  c.lane = threadIdx.x & 63;
+  c.w = wave_id();
+  c.pj = (EPI == EPI_GATEUP) ? (c.w >> 1) : 0;
+  c.colbase = (EPI == EPI_GATEUP) ? c.nb * 128 : c.nb * 256;
+  c.nks = p.in_f >> 5;
+  c.lds0 = (uint32_t)(uintptr_t)smem;
+  const int w = c.w, lane = c.lane, g = lane >> 4, n = lane & 15;
+  const int colw = c.colbase + ((EPI == EPI_GATEUP) ? 64 * (w & 1) : 64 * w);
+  const bool col_ok = colw < p.out_f;
+  const int nt0 = colw >> 4;
+  const int ktiles = p.in_f >> 4;
+  const int msub = (c.nrows + 15) >> 4;
+
+  // A chunk ch of this wave: 16 rows x 64 B of one stage; lane L -> row
+  // 16 rg + L/4, LDS slot L%4 holding the global 16-byte chunk
+  // (L%4) ^ a_swizzle(row & 15). Rows past the tile's end re-read its last
+  // row (never stored).
+  c.abase = (const char *)(p.A + (int64_t)c.row0 * p.lda);
+#pragma unroll
+  for (int ch = 0; ch < L::kAChunks; ++ch) {
+    const int f = w * L::kAChunks + ch;
+    const int q = f >> 3, rg = f & 7;
+    const int r = 16 * rg + (lane >> 2);
+    const int rs = min(r, c.nrows - 1);
+    const int gc = (lane & 3) ^ a_swizzle(r & 15);
+    c.avoff[ch] = (uint32_t)(2 * ((int64_t)rs * p.lda + q * p.a_proj_stride + gc * 8));
+    c.adst[ch] = uniform_u32((uint32_t)(L::kAOff + q * kAbuf + rg * 1024));
+  }
+
+  f32x4 acc[MULTI ? 8 : 1][4];
+  f32x4 pacc[8][4];
+#pragma unroll
+  for (int ms = 0; ms < (MULTI ? 8 : 1); ++ms)
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const ProjDev pd = (c.pj == 0) ? p.proj[0] : p.proj[NPROJ - 1];
+  const int nst = MULTI ? max(p.proj[0].num_stages, p.proj[NPROJ - 1].num_stages) : 1;
+  for (int t = 0; t < nst; ++t) {
+    float sc = 0.0f;
+    int K = 0;
+    const char *tens = nullptr;
+    if (t < pd.num_stages && col_ok) {
+      sc = uload_f32(pd.scale + t * p.E + c.e);
+      K = uload_i32(pd.bits + t * p.E + c.e);
+      tens = (const char *)uload_ptr(pd.trellis + t * p.E + c.e);
+      if (sc != 0.0f && (tens == nullptr || K < 2 || K > 8)) {
+        if (c.nb == 0 && (w & 1) == 0 && lane == 0) atomicAdd(p.ctrl + 1, 1);
+        sc = 0.0f;
+      }
+    }
+    const bool active = __builtin_amdgcn_readfirstlane(sc != 0.0f ? 1 : 0) != 0;
+#pragma unroll
+    for (int ms = 0; ms < 8; ++ms)
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) pacc[ms][ns] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (!active) {
+      wide_idle_stage<EPI>(c);
+    } else {
+      switch (K) {
+        case 2: wide_stage_rows<EPI, 2>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 3: wide_stage_rows<EPI, 3>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 4: wide_stage_rows<EPI, 4>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 5: wide_stage_rows<EPI, 5>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 6: wide_stage_rows<EPI, 6>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 7: wide_stage_rows<EPI, 7>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        default: wide_stage_rows<EPI, 8>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+      }
+    }
+    // acc = fmaf(s_t, P_t, acc) from acc = 0; a skipped stage leaves acc alone
+#pragma unroll
+    for (int ms = 0; ms < 8; ++ms)
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (MULTI) {
+            if (active) acc[ms][ns][r] = fmaf(sc, pacc[ms][ns][r], acc[ms][ns][r]);
+          } else {
+            pacc[ms][ns][r] = active ? fmaf(sc, pacc[ms][ns][r], 0.0f) : 0.0f;
+          }
+        }
+  }
+  const f32x4(&fin)[8][4] =
+      *reinterpret_cast<const f32x4(*)[8][4]>(MULTI ? &acc[0][0] : &pacc[0][0]);
+
+  // ---- epilogue: accumulators -> LDS tile -> shared epilogue, in two
+  // rounds of 64 rows (row blocks 0-3, then 4-7)
+  float *T = (float *)smem;
+  const int cw = (EPI == EPI_GATEUP) ? 64 * (w & 1) : 64 * w;  // column of the wave in T
+  const int nblk = (EPI == EPI_GATEUP) ? 1 : min(2, (p.out_f - c.colbase) / 128);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int hrows = min(L::kHalf, c.nrows - L::kHalf * half);
+    if (hrows <= 0) break;  // uniform
+    __syncthreads();
+#pragma unroll
+    for (int ms = 4 * half; ms < 4 * half + 4; ++ms)
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          T[c.pj * (L::kHalf * L::kLd) + (16 * (ms - 4 * half) + 4 * g + r) * L::kLd + cw +
+            16 * ns + n] = fin[ms][ns][r];
+    __syncthreads();
+    epilogue<EPI>(p, T, L::kLd, L::kHalf * L::kLd, c.e, c.row0 + L::kHalf * half, hrows,
+                  c.colbase, nblk);
+  }
+}
+
+// One workgroup per (tile, 256-column block) on a 1-D grid of groups of 8
+// tiles x nb column blocks. Workgroups are dealt to the 8 XCDs round-robin by
+// linear id, so tile 8 G + (id % 8) keeps all its column blocks on one XCD
+// (sharing its L2 copy of the tile's A rows), and the dispatch order walks
+// the tiles front to back: tiles past the device's tile count (the launch is
+// sized for the worst case) come last and exit at once.
+template <int EPI, bool MULTI>
+__global__ void __launch_bounds__(256, MULTI ? 1 : 2) gemm_wide_kernel(GemmParams p, int nb) {
+  __shared__ __attribute__((aligned(16))) char smem[WideLds<EPI>::kBytes];
+  const int id = blockIdx.x, per = 8 * nb;
+  const int grp = id / per, r = id - grp * per;
+  wide_item<EPI, MULTI>(p, smem, 8 * grp + (r & 7), r >> 3);
+}
+
+hipError_t launch_gemm_wide(int epi, const GemmParams &p, int tiles, int nblocks, hipStream_t s) {
+  if (tiles <= 0 || nblocks <= 0) return hipSuccess;
+  const bool multi = p.proj[0].num_stages > 1 || (epi == EPI_GATEUP && p.proj[1].num_stages > 1);
+  const dim3 wgrid((unsigned)((tiles + 7) / 8 * 8 * nblocks));
+#define EXL3_WIDE(E, M) \
+  hipLaunchKernelGGL((gemm_wide_kernel<E, M>), wgrid, dim3(256), 0, s, p, nblocks)
+  switch (epi) {
+    case EPI_GATEUP: if (multi) EXL3_WIDE(EPI_GATEUP, true); else EXL3_WIDE(EPI_GATEUP, false); break;
+    case EPI_DOWN: if (multi) EXL3_WIDE(EPI_DOWN, true); else EXL3_WIDE(EPI_DOWN, false); break;
+    default: if (multi) EXL3_WIDE(EPI_LINEAR, true); else EXL3_WIDE(EPI_LINEAR, false); break;
+  }
+#undef EXL3_WIDE
+  return hipGetLastError();
+}
+
+}  // namespace exl3

@@ -88,6 +88,9 @@ struct PackParams {
 
 hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks,
                        hipStream_t s, bool wide);
+// 128-row tiles (gemm_wide.hip); called by launch_gemm.
+hipError_t launch_gemm_wide(int epi, const GemmParams &p, int tiles, int nblocks,
+                            hipStream_t s);
 hipError_t launch_rotate(const RotParams &p, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int npos, hipStream_t s);
 hipError_t launch_pack(const PackParams &p, hipStream_t s);
