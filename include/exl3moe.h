@@ -155,7 +155,9 @@ int32_t exl3_route_pack(const void *ids, int32_t ids_dtype, const void *w,
  * Plain EXL3 linear [p2 What this changes: row-invariant linear; prompt rows
  * in blocks]. x: [rows][in] fp16; out: [rows][out] fp16 (RNE) or fp32.
  * A row's output bytes do not depend on rows or on how rows are chunked.
- * ws: device workspace of at least exl3_linear_workspace_size() bytes.
+ * ws: device workspace of at least exl3_linear_workspace_size() bytes (the
+ * rotated rows, plus pre-rotation sums and completion counts for small row
+ * counts); calls that share it must be ordered on one stream.
  */
 size_t exl3_linear_workspace_size(int32_t rows, int32_t in_features,
                                   int32_t out_features);
@@ -213,6 +215,9 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t rows, int32_t topk,
  *   at          fp16 [C][intermediate] rotated down inputs a~ of the pass
  *   d           fp32 [C][hidden]     weighted per-pair down outputs
  *   yacc        fp32 [rows][hidden]  running row sums across passes
+ *   (then private scratch of the 16-row tile path, used when rows * topk <
+ *   64 * num_experts: pre-rotation fp32 sums [C][max(2 intermediate,
+ *   hidden)] and int32 completion counts; not part of the layout struct)
  * Rotated vectors (xt, at) are stored with the 16 entries of each aligned
  * group of 16 permuted as k = {0,4,1,5,2,6,3,7,8,12,9,13,10,14,11,15}[p]
  * (stored slot p holds entry k). exl3_moe_layout() returns the offsets.

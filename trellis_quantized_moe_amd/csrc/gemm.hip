@@ -25,185 +25,337 @@
 
 namespace exl3 {
 
-// Narrow tiles: rows per tile are 16 (one MFMA row block); each wave owns one
-// 16-column strip (one tile column nt) over the whole input dimension. Two
-// register buffers of kGroup k-blocks (64 inputs each) alternate: one is in
-// flight while the other is decoded and multiplied. Every load is issued
-// unconditionally (tail groups re-read the last group) so the compiler can
-// count outstanding loads exactly.
+// Narrow tiles (decode-size work): a work item is a tile of at most 16 rows
+// of one expert times 64 output columns of one projection, one workgroup of
+// 4 waves. Wave w streams strip 4 cg + w (16 columns) over the whole input.
+// Waves never wait for each other until the end, so there is one 64-column
+// work item per few CUs' worth of waves even at one routed row.
 //
-// MFMA k-step s (0, 1) of k-block kb covers inputs 64 kb + 32 s .. +31, i.e.
-// trellis tiles 4 kb + 2 s and 4 kb + 2 s + 1 along k. Lane (g, n) supplies
-// states 8 (g & 1) .. +7 of column n of tile 4 kb + 2 s + (g >> 1) (a half
-// column) and the matching 8 rotated inputs. The 128-row kernel uses the same
+// Trellis: each wave copies its strip global->LDS by DMA in blocks of 128
+// inputs (8 tiles, 256K bytes) into a ring of kNRing slots of its own, five
+// blocks ahead of the one it decodes. A (rotated rows, L2-resident) goes
+// straight to registers four blocks ahead: vector loads complete in order, so
+// the wait for A[b] also waits for every trellis block issued before it, and
+// A's lead bounds the trellis lead. Every wave issues the same loads every
+// block (past the end it re-reads the last block), so each wait is an exact
+// vmcnt.
+//
+// MFMA k-step s of block b covers inputs 128 b + 32 s .. +31, i.e. trellis
+// tiles 8 b + 2 s and 8 b + 2 s + 1 along k. Lane (g, n) supplies states
+// 8 (g & 1) .. +7 of column n of tile 8 b + 2 s + (g >> 1) (a half column)
+// and the matching 8 rotated inputs. The 128-row kernel uses the same
 // k-steps, so both run one MFMA chain per output.
-constexpr int kGroup = 2;
+//
+// The pre-rotation fp32 sums go to workspace scratch; the last of the work
+// items of a 128-column block (an atomic count: 2, or 4 for gate + up) runs
+// the shared epilogue on the whole block.
+constexpr int kNRing = 6;
+constexpr int kNSlot = 2048;  // bytes: one block at K <= 8
 
 template <int K>
-struct ChainBuf {
-  uint32_t raw[kGroup][2][HalfGeom<K>::kLoadDw];
-  u32x4 a[kGroup][2];
+struct StreamGeom {
+  static constexpr int kBlk = 256 * K;                        // bytes per block
+  static constexpr int kDma = (kBlk + 1023) / 1024;           // 1 or 2
+  static constexpr int kLanes1 = (kBlk > 1024) ? (kBlk - 1024) / 16 : 0;
+  static constexpr uint64_t kMask0 = (kBlk >= 1024) ? ~0ull : ((1ull << (kBlk / 16)) - 1);
+  static constexpr uint64_t kMask1 = (kLanes1 >= 64) ? ~0ull : ((1ull << kLanes1) - 1);
 };
 
-template <int K>
-__device__ __forceinline__ void chain_load(ChainBuf<K> &b, __amdgpu_buffer_rsrc_t wr,
-                                           const uint32_t (&voff)[HalfGeom<K>::kLoadDw],
-                                           __amdgpu_buffer_rsrc_t ar, uint32_t avoff, int kb0) {
-  constexpr int TD = Geom<K>::kTileDw;
-#pragma unroll
-  for (int u = 0; u < kGroup; ++u) {
-    const int kb = kb0 + u;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int koff = (kb * 4 + 2 * s) * TD * 4;  // bytes of the k-step's first tile
-#pragma unroll
-      for (int j = 0; j < HalfGeom<K>::kLoadDw; ++j)
-        b.raw[u][s][j] = __builtin_amdgcn_raw_buffer_load_b32(wr, voff[j], koff, 0);
-      b.a[u][s] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, avoff, kb * 128 + 64 * s, 0));
-    }
-  }
+// 16-byte-per-lane global->LDS copy (lanes in `lanes`): lane L reads
+// sbase + voff and writes LDS byte m0 + 16 L.
+__device__ __forceinline__ void sdma16(uint32_t voff, const void *sbase, uint32_t lds_base,
+                                       uint64_t lanes) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_and_b64 exec, exec, %4\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_base), "s"(lanes)
+      : "memory");
 }
 
-template <int K>
-__device__ __forceinline__ void chain_compute(const ChainBuf<K> &b, uint32_t shift, uint32_t mask,
-                                              int nvalid, f32x4 &acc) {
-  constexpr int NN = HalfGeom<K>::kNormDw;
-#pragma unroll
-  for (int u = 0; u < kGroup; ++u) {
-    if (u < nvalid) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        uint32_t N[NN];
-        normalize(b.raw[u][s], shift, N);
-        const u32x4 w = {half_reg<K, 0>(N, mask), half_reg<K, 1>(N, mask),
-                         half_reg<K, 2>(N, mask), half_reg<K, 3>(N, mask)};
-        acc = mfma16x16x32(__builtin_bit_cast(f16x8, b.a[u][s]), __builtin_bit_cast(f16x8, w), acc);
-      }
-    }
-  }
+template <int N>
+__device__ __forceinline__ void swait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// The 4 A fragments of one block (16 bytes each, 64 bytes apart) into
+// registers, on the lanes in `lanes` only (rows past the tile's end are never
+// loaded: their MFMA output rows are discarded). Invisible to the compiler's
+// wait counting: the chain's own vmcnt waits cover it (see a_wait).
+__device__ __forceinline__ void aload_block(u32x4 &a0, u32x4 &a1, u32x4 &a2, u32x4 &a3,
+                                            uint32_t voff, const char *sbase, uint64_t lanes) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %4, exec\n\t"
+      "s_and_b64 exec, exec, %7\n\t"
+      "global_load_dwordx4 %0, %5, %6 offset:0\n\t"
+      "global_load_dwordx4 %1, %5, %6 offset:64\n\t"
+      "global_load_dwordx4 %2, %5, %6 offset:128\n\t"
+      "global_load_dwordx4 %3, %5, %6 offset:192\n\t"
+      "s_mov_b64 exec, %4"
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lanes)
+      : "memory");
+}
+
+// Wait until at most N vector loads are outstanding; the A registers of the
+// block about to be used are tied to the wait so no use moves above it.
+template <int N>
+__device__ __forceinline__ void a_wait(u32x4 &a0, u32x4 &a1, u32x4 &a2, u32x4 &a3) {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3) : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ const char *sgpr_ptr(const void *ptr) {
+  const uint64_t b = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  return (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 // P = MFMA chain of one stage over all inputs for this wave's strip.
-// strip: the 16-column strip's tiles (in_f/16 tiles of 32K bytes);
-// ar/avoff: A rows (kSigma order) and this lane's byte offset of its row.
-// in_f is a multiple of 128.
+constexpr int kNADist = 4;  // A blocks in flight ahead of the one in use
+
 template <int K>
-__device__ __forceinline__ f32x4 stage_chain(const uint32_t *strip, int in_f,
-                                             __amdgpu_buffer_rsrc_t ar, uint32_t avoff, int lane) {
-  constexpr int ND = HalfGeom<K>::kLoadDw, TD = Geom<K>::kTileDw;
+struct StreamChain {
+  using G = StreamGeom<K>;
+  static constexpr int ND = HalfGeom<K>::kLoadDw, NN = HalfGeom<K>::kNormDw;
+  static constexpr int TD = Geom<K>::kTileDw;
+  static constexpr int kIssue = 4 + G::kDma;  // loads per block: A, then T
+  static_assert(kNADist + 1 == kNRing - 1, "the A lead equals the trellis lead");
+
+  const char *strip;  // uniform: the strip's trellis
+  const char *ring;   // this wave's LDS ring
+  uint32_t ring_lds;  // its LDS address (uniform)
+  const char *abase;  // uniform: A rows of the tile
+  uint32_t avoff;     // lane's A byte offset (row, k-group)
+  uint64_t alanes;    // lanes whose A row is inside the tile
+  uint32_t tvoff;     // lane's byte offset inside a block
+  uint32_t traddr[ND];
+  uint32_t shift, mask;
+  int nblk;
+  u32x4 a[kNADist + 1][4];  // A of blocks b .. b + kNADist (ring by b % 5)
+
+  __device__ __forceinline__ void load_a(int ba, int aslot) {
+    const char *src = sgpr_ptr(abase + (size_t)ba * 256);
+    aload_block(a[aslot][0], a[aslot][1], a[aslot][2], a[aslot][3], avoff, src, alanes);
+  }
+  __device__ __forceinline__ void issue(int b, int aslot) {
+    const int last = nblk - 1;
+    load_a(min(b + kNADist, last), aslot);
+    issue_t(min(b + kNRing - 1, last));
+  }
+  __device__ __forceinline__ void issue_t(int bt) {
+    const char *src = sgpr_ptr(strip + (size_t)bt * G::kBlk);
+    const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(ring_lds + (uint32_t)((bt % kNRing) * kNSlot)));
+    sdma16(tvoff, src, dst, G::kMask0);
+    if constexpr (G::kDma > 1) sdma16(tvoff + 1024, src, dst + 1024, G::kMask1);
+  }
+
+  __device__ __forceinline__ void compute(int b, int aslot, f32x4 &acc) {
+    const uint32_t base = (uint32_t)((b % kNRing) * kNSlot);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint32_t raw[ND];
+#pragma unroll
+      for (int j = 0; j < ND; ++j)
+        raw[j] = *(const uint32_t *)(ring + base + traddr[j] + s * 2 * TD * 4);
+      uint32_t N[NN];
+      normalize(raw, shift, N);
+      const u32x4 w = {half_reg<K, 0>(N, mask), half_reg<K, 1>(N, mask),
+                       half_reg<K, 2>(N, mask), half_reg<K, 3>(N, mask)};
+      acc = mfma16x16x32(__builtin_bit_cast(f16x8, a[aslot][s]), __builtin_bit_cast(f16x8, w), acc);
+    }
+  }
+
+  // Block b: wait for A[b] (issued kNADist blocks earlier, first in its
+  // group; T[b] was issued before it), issue A[b + 4] and T[b + 5], compute.
+  template <int AS>
+  __device__ __forceinline__ void block(int b, f32x4 &acc) {
+    a_wait<kNADist * kIssue - 4>(a[AS][0], a[AS][1], a[AS][2], a[AS][3]);
+    issue(b, (AS + kNADist) % (kNADist + 1));
+    compute(b, AS, acc);
+  }
+
+  __device__ __forceinline__ f32x4 run() {
+    const int last = nblk - 1;
+    // prologue in steady-state order: T[0], then A[j] T[j + 1] for j = 0..3
+    issue_t(0);
+#pragma unroll
+    for (int j = 0; j < kNADist; ++j) {
+      load_a(min(j, last), j);
+      issue_t(min(j + 1, last));
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < nblk; b += 5) {
+      block<0>(b, acc);
+      if (b + 1 < nblk) block<1>(b + 1, acc);
+      if (b + 2 < nblk) block<2>(b + 2, acc);
+      if (b + 3 < nblk) block<3>(b + 3, acc);
+      if (b + 4 < nblk) block<4>(b + 4, acc);
+    }
+    swait_vmcnt<0>();  // no DMA may land after the ring is reused
+    return acc;
+  }
+};
+
+template <int K>
+__device__ __forceinline__ f32x4 stream_chain(const char *strip, int in_f, const char *ring,
+                                              const char *abase, uint32_t avoff, uint64_t alanes,
+                                              int lane) {
+  StreamChain<K> c;
+  c.alanes = alanes;
   const int g = lane >> 4, n = lane & 15;
+  c.strip = sgpr_ptr(strip);
+  c.ring = ring;
+  c.ring_lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)ring);
+  c.abase = sgpr_ptr(abase);
+  c.avoff = avoff + 16u * g;  // 8 halves per k-group
+  c.tvoff = 16u * (uint32_t)lane;
+  c.nblk = in_f >> 7;
   // window of states 8h .. 8h+7 of column n: first bit 16nK + 8hK + K - 16
   const int b = 16 * n * K + 8 * (g & 1) * K + K - 16;
   const int d0 = b >> 5;  // floor
-  const uint32_t shift = (uint32_t)(b & 31);
-  uint32_t voff[ND];
+  c.shift = (uint32_t)(b & 31);
+  constexpr int TD = Geom<K>::kTileDw;
 #pragma unroll
-  for (int j = 0; j < ND; ++j) {
+  for (int j = 0; j < StreamChain<K>::ND; ++j) {
     int d = d0 + j;
     d += (d < 0) ? TD : 0;
     d -= (d >= TD) ? TD : 0;
-    voff[j] = (uint32_t)((g >> 1) * TD + d) * 4u;
+    c.traddr[j] = (uint32_t)((g >> 1) * TD + d) * 4u;
   }
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(strip, (uint32_t)(in_f / 16) * 32u * K);
-  avoff += 16u * g;  // 8 halves per k-group
-  const uint32_t mask = codebook_mask();
-  const int nkb = in_f >> 6;
-  const int last = nkb - kGroup;  // start of the last full group
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  ChainBuf<K> A, B;
-  chain_load<K>(A, wr, voff, ar, avoff, 0);
-  for (int kb0 = 0; kb0 < nkb; kb0 += 2 * kGroup) {
-    chain_load<K>(B, wr, voff, ar, avoff, min(kb0 + kGroup, last));
-    chain_compute<K>(A, shift, mask, nkb - kb0, acc);
-    chain_load<K>(A, wr, voff, ar, avoff, min(kb0 + 2 * kGroup, last));
-    chain_compute<K>(B, shift, mask, nkb - kb0 - kGroup, acc);
-  }
-  return acc;
+  c.mask = codebook_mask();
+  return c.run();
 }
 
 // Stage loop of one projection for one wave: acc = sum fmaf(s_t, P_t, acc).
-__device__ __forceinline__ f32x4 project_strip(const ProjDev &pd, int E, int e,
-                                               int in_f, int nt,
-                                               __amdgpu_buffer_rsrc_t ar, uint32_t avoff,
-                                               int lane, int32_t *ctrl, bool report) {
+__device__ __forceinline__ f32x4 stream_strip(const ProjDev &pd, int E, int e, int in_f, int nt,
+                                              const char *ring, const char *abase,
+                                              uint32_t avoff, uint64_t alanes, int lane,
+                                              int32_t *ctrl, bool report) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const size_t strip_dw_per_bit = (size_t)nt * (in_f / 16) * 8;  // x K
   for (int t = 0; t < pd.num_stages; ++t) {
     const float s = uload_f32(pd.scale + t * E + e);
     if (s == 0.0f) continue;  // zero scale: the stage is skipped entirely
-    const uint32_t *tens = uload_ptr(pd.trellis + t * E + e);
+    const char *tens = (const char *)uload_ptr(pd.trellis + t * E + e);
     const int K = uload_i32(pd.bits + t * E + e);
     if (tens == nullptr || K < 2 || K > 8) {
       if (report && lane == 0) atomicAdd(ctrl + 1, 1);
       continue;
     }
-    const uint32_t *strip = tens + strip_dw_per_bit * K;
-    f32x4 p;
+    const char *strip = tens + (size_t)nt * (in_f / 16) * 32 * K;
+    f32x4 q;
     switch (K) {
-      case 2: p = stage_chain<2>(strip, in_f, ar, avoff, lane); break;
-      case 3: p = stage_chain<3>(strip, in_f, ar, avoff, lane); break;
-      case 4: p = stage_chain<4>(strip, in_f, ar, avoff, lane); break;
-      case 5: p = stage_chain<5>(strip, in_f, ar, avoff, lane); break;
-      case 6: p = stage_chain<6>(strip, in_f, ar, avoff, lane); break;
-      case 7: p = stage_chain<7>(strip, in_f, ar, avoff, lane); break;
-      default: p = stage_chain<8>(strip, in_f, ar, avoff, lane); break;
+      case 2: q = stream_chain<2>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      case 3: q = stream_chain<3>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      case 4: q = stream_chain<4>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      case 5: q = stream_chain<5>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      case 6: q = stream_chain<6>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      case 7: q = stream_chain<7>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      default: q = stream_chain<8>(strip, in_f, ring, abase, avoff, alanes, lane); break;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = fmaf(s, p[r], acc[r]);
+    for (int r = 0; r < 4; ++r) acc[r] = fmaf(s, q[r], acc[r]);
   }
   return acc;
 }
 
-// ------------------------------------------------------------ narrow tiles
-// 16 rows; one wave per 16-column strip over the whole input dimension.
+// grid: x = tile, y = NPROJ * (out_f / 64) column groups (projection major).
 template <int EPI>
-__global__ void __launch_bounds__(EPI == EPI_GATEUP ? 1024 : 512)
-    gemm_narrow_kernel(GemmParams p) {
+__global__ void __launch_bounds__(256, 3) gemm_narrow_kernel(GemmParams p) {
   constexpr int NPROJ = (EPI == EPI_GATEUP) ? 2 : 1;
-  __shared__ float tile[NPROJ][kBM][kLdsStride];
+  __shared__ __attribute__((aligned(16))) char smem[4 * kNRing * kNSlot];
+  __shared__ int s_last;
 
   int e, row0, nrows;
   if (!tile_of_block(p, kBM, blockIdx.x, e, row0, nrows)) return;
-  const int nb = blockIdx.y;  // 128-column output block
+  const int ncg = p.out_f >> 6;
+  const int pj = (EPI == EPI_GATEUP) ? (int)(blockIdx.y / ncg) : 0;
+  const int cg = blockIdx.y - pj * ncg;
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
-  const int pj = (EPI == EPI_GATEUP) ? (w >> 3) : 0;
-  const int c16 = w & 7;
-  const int nt = nb * 8 + c16;
+  const int nt = cg * 4 + w;
 
   // Lanes of rows past the tile's end read the last valid row (same cache
   // lines, no extra traffic); their results are never stored.
   const int arow = min(lane & 15, nrows - 1);
   const uint16_t *a_tile = p.A + (int64_t)row0 * p.lda + pj * p.a_proj_stride;
-  const __amdgpu_buffer_rsrc_t ar =
-      make_rsrc(a_tile, (uint32_t)((int64_t)(nrows - 1) * p.lda * 2 + 2 * p.in_f));
   const uint32_t avoff = (uint32_t)(arow * p.lda * 2);
 
+  // lanes n < nrows of every 16-lane group carry rows of the tile
+  const uint64_t rows16 = (nrows >= 16) ? 0xFFFFull : ((1ull << nrows) - 1);
+  const uint64_t alanes = rows16 | (rows16 << 16) | (rows16 << 32) | (rows16 << 48);
   const ProjDev pd = (pj == 0) ? p.proj[0] : p.proj[1];
-  const f32x4 acc = project_strip(pd, p.E, e, p.in_f, nt, ar, avoff, lane, p.ctrl,
-                                  nb == 0 && c16 == 0);
+  const f32x4 acc = stream_strip(pd, p.E, e, p.in_f, nt, smem + w * kNRing * kNSlot,
+                                 (const char *)a_tile, avoff, alanes, lane, p.ctrl,
+                                 cg == 0 && w == 0);
 
+  // Pre-rotation sums of this work item -> scratch [row][NPROJ][out_f].
+  // Hand-off to the last work item of the 128-column block without cache
+  // maintenance: the sums are written and read with device-coherent
+  // (agent-scope) relaxed atomic accesses, every store has completed
+  // (vmcnt 0) before the count is incremented, and the reads start only
+  // after the increment that saw every other count.
+  const int64_t ldn = (int64_t)NPROJ * p.out_f;
+  const int col = nt * 16 + (lane & 15);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) tile[pj][4 * (lane >> 4) + r][c16 * 16 + (lane & 15)] = acc[r];
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * (lane >> 4) + r;
+    if (row < nrows)
+      __hip_atomic_store(p.nacc + (int64_t)(row0 + row) * ldn + pj * p.out_f + col, acc[r],
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  epilogue<EPI>(p, &tile[0][0][0], kLdsStride, kBM * kLdsStride, e, row0, nrows, nb * 128, 1);
+  const int blk = cg >> 1;
+  int32_t *cnt = p.ncnt + (int64_t)blockIdx.x * (p.out_f >> 7) + blk;
+  if (threadIdx.x == 0)
+    s_last = (__hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              2 * NPROJ - 1)
+                 ? 1
+                 : 0;
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0)  // ready for the next launch
+    __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float *T = (float *)smem;  // [NPROJ][16][kLdsStride]
+  for (int i = threadIdx.x; i < NPROJ * kBM * 128; i += blockDim.x) {
+    const int q = i / (kBM * 128), rem = i - q * (kBM * 128);
+    const int row = rem >> 7, c = rem & 127;
+    T[(q * kBM + row) * kLdsStride + c] =
+        row < nrows ? __hip_atomic_load(p.nacc + (int64_t)(row0 + row) * ldn + q * p.out_f +
+                                            blk * 128 + c,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : 0.0f;
+  }
+  __syncthreads();
+  epilogue<EPI>(p, T, kLdsStride, kBM * kLdsStride, e, row0, nrows, blk * 128, 1);
 }
 
 hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks, hipStream_t s,
                        bool wide) {
   if (tiles <= 0 || nblocks <= 0) return hipSuccess;
   if (wide) return launch_gemm_wide(epi, p, tiles, nblocks, s);
-  const dim3 grid(tiles, nblocks);
+  // nblocks: 128-column blocks per projection
+  const int nproj = (epi == EPI_GATEUP) ? 2 : 1;
+  const dim3 grid(tiles, nproj * 2 * nblocks);
   switch (epi) {
     case EPI_GATEUP:
-      hipLaunchKernelGGL(gemm_narrow_kernel<EPI_GATEUP>, grid, dim3(1024), 0, s, p);
+      hipLaunchKernelGGL(gemm_narrow_kernel<EPI_GATEUP>, grid, dim3(256), 0, s, p);
       break;
     case EPI_DOWN:
-      hipLaunchKernelGGL(gemm_narrow_kernel<EPI_DOWN>, grid, dim3(512), 0, s, p);
+      hipLaunchKernelGGL(gemm_narrow_kernel<EPI_DOWN>, grid, dim3(256), 0, s, p);
       break;
     default:
-      hipLaunchKernelGGL(gemm_narrow_kernel<EPI_LINEAR>, grid, dim3(512), 0, s, p);
+      hipLaunchKernelGGL(gemm_narrow_kernel<EPI_LINEAR>, grid, dim3(256), 0, s, p);
       break;
   }
   return hipGetLastError();

@@ -163,7 +163,7 @@ struct WideIter {
   // one stage's working set
   uint32_t raw[4][ND];
   uint32_t N[NN];
-  f16x8 af[3];
+  f16x8 af[MS];
   uint32_t ar;  // A fragment address in the current slot
 
   __device__ __forceinline__ WideIter(const WideArgs &c_, const char *smem_, const char *tens_,
@@ -241,7 +241,7 @@ struct WideIter {
     af[slot_ms] = *(const f16x8 *)(smem + ar + ms * 16 * kArow);
   }
 
-  // Unit u: its DMAs, an A fragment prefetch, PPU decode pairs, two MFMAs.
+  // Unit u: its DMAs, PPU decode pairs, two MFMAs.
   template <int u>
   __device__ __forceinline__ void unit(const BRegs &bc, BRegs &bn, f32x4 (&pacc)[8][4], int ka,
                                        int kt, int sa_w, int st_w) {
@@ -249,11 +249,10 @@ struct WideIter {
 #pragma unroll
     for (int d = 0; d < L::kDma; ++d)
       if ((d * U) / L::kDma == u) dma(d, ka, kt, sa_w, st_w);
-    if constexpr ((u & 1) == 0 && ms + 2 < MS) load_af((ms + 2) % 3, ms + 2);
     decode_range<u * PPU, PPU>(bn);
-    pacc[ms][ns0] = mfma16x16x32(af[ms % 3], __builtin_bit_cast(f16x8, bc[ns0]), pacc[ms][ns0]);
+    pacc[ms][ns0] = mfma16x16x32(af[ms], __builtin_bit_cast(f16x8, bc[ns0]), pacc[ms][ns0]);
     pacc[ms][ns0 + 1] =
-        mfma16x16x32(af[ms % 3], __builtin_bit_cast(f16x8, bc[ns0 + 1]), pacc[ms][ns0 + 1]);
+        mfma16x16x32(af[ms], __builtin_bit_cast(f16x8, bc[ns0 + 1]), pacc[ms][ns0 + 1]);
     __builtin_amdgcn_sched_barrier(0);
   }
   template <int... Us>
@@ -270,8 +269,10 @@ struct WideIter {
     wait_vmcnt<L::kDma + L::kTDma>();
     __syncthreads();
     ar = afrag + (uint32_t)(sa * L::kAStage);
-    load_af(0, 0);
-    load_af(1, 1);
+    // every A fragment of the stage at once: under load an LDS read takes a
+    // few hundred cycles, so only the first MFMA waits for one
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) load_af(ms, ms);
     read_raw((ks + 1) & 3);
     const int sa_w = (sa == 0) ? 2 : sa - 1;  // (ks + 2) % 3
     units(bc, bn, pacc, min(ks + 2, last), min(ks + 4, last), sa_w, ks & 3,

@@ -107,10 +107,20 @@ ProjDev to_dev(const exl3_proj *p) {
 
 bool out_dtype_ok(int32_t t) { return t == EXL3_F16 || t == EXL3_F32; }
 
+// Tile shape choice (never changes results: both tile shapes run the same
+// per-element MFMA chain and the same epilogue code). Wide 128-row tiles pay
+// off once expert spans average 64+ rows; otherwise 16-row tiles keep the
+// machine full at decode sizes.
+bool moe_wide(int64_t pairs, int E) { return pairs >= 64 * (int64_t)E; }
+bool linear_wide(int rows, int out) {
+  return (int64_t)((rows + kBMWide - 1) / kBMWide) * ((out + 255) / 256) >= 256;
+}
+
 struct MoeLayout {
   size_t ctrl, count, offset, pair_of_pos, weight_of_pos, pos_of_pair, num_active, status;
-  size_t expert_of_pos, plan, xt, at, d, yacc, total;
-  int passes, slots, cap;
+  size_t expert_of_pos, plan, xt, at, d, yacc, nacc, ncnt, total;
+  int passes, slots, cap, ncnt_ints;
+  bool wide;
 };
 
 MoeLayout moe_layout(int32_t rows, int32_t topk, int32_t E, int32_t H, int32_t I,
@@ -141,18 +151,15 @@ MoeLayout moe_layout(int32_t rows, int32_t topk, int32_t E, int32_t H, int32_t I
   L.at = take(2 * (size_t)C * I);
   L.d = take(4 * (size_t)C * H);
   L.yacc = take(4 * (size_t)rows * H);
+  // 16-row tiles: pre-rotation sums and completion counts of the GEMMs
+  L.wide = P > 0 && moe_wide(P, E);
+  L.ncnt_ints = L.wide ? 0 : L.slots * (std::max(I, H) / 128);
+  L.nacc = take(L.wide ? 0 : 4 * (size_t)C * std::max(2 * I, H));
+  L.ncnt = take(4 * (size_t)L.ncnt_ints);
   L.total = o;
   return L;
 }
 
-// Tile shape choice (never changes results: both tile shapes run the same
-// per-element MFMA chain and the same epilogue code). Wide 128-row tiles pay
-// off once expert spans average 64+ rows; otherwise 16-row tiles keep the
-// machine full at decode sizes.
-bool moe_wide(int64_t pairs, int E) { return pairs >= 64 * (int64_t)E; }
-bool linear_wide(int rows, int out) {
-  return (int64_t)((rows + kBMWide - 1) / kBMWide) * ((out + 255) / 256) >= 256;
-}
 
 template <typename T>
 T *at(void *ws, size_t off) {
@@ -201,7 +208,7 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
   const int64_t P = (int64_t)rows * topk;
   const int32_t *total_valid = offset + E;
   int32_t *ctrl = at<int32_t>(ws, L.ctrl);
-  const bool wide = moe_wide(P, E);
+  const bool wide = L.wide;
   const int bm = wide ? kBMWide : kBM;
   for (int pass = 0; pass < L.passes; ++pass) {
     const int pb = pass * L.cap;
@@ -244,6 +251,8 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     g.out_h = at<uint16_t>(ws, L.at);
     g.ldo = I;
     g.ctrl = ctrl;
+    g.nacc = at<float>(ws, L.nacc);
+    g.ncnt = at<int32_t>(ws, L.ncnt);
     {
       ProfScope ps(st, EXL3_K_GATEUP);
       if (launch_gemm(EPI_GATEUP, g, tiles, I / 128, st, wide) != hipSuccess) return EXL3_E_LAUNCH;
@@ -263,6 +272,8 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     dn.weight_of_pos = weight_of_pos;
     dn.pass_base = pb;
     dn.ctrl = ctrl;
+    dn.nacc = at<float>(ws, L.nacc);
+    dn.ncnt = at<int32_t>(ws, L.ncnt);
     {
       ProfScope ps(st, EXL3_K_DOWN);
       const int nbd = wide ? (H + 255) / 256 : H / 128;
@@ -291,6 +302,25 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
   return EXL3_OK;
 }
 
+// Linear workspace: 256 B control word block, the rotated rows, and for
+// 16-row tiles the pre-rotation sums and completion counts.
+struct LinLayout {
+  size_t xt, nacc, ncnt, total;
+  int ncnt_ints;
+  bool wide;
+};
+LinLayout lin_layout(int32_t rows, int32_t in_features, int32_t out_features) {
+  LinLayout L{};
+  L.wide = linear_wide(rows, out_features);
+  L.xt = 256;
+  L.nacc = L.xt + align_up(2 * (size_t)rows * in_features);
+  const size_t nacc_bytes = L.wide ? 0 : 4 * (size_t)rows * out_features;
+  L.ncnt = L.nacc + align_up(nacc_bytes);
+  L.ncnt_ints = L.wide ? 0 : ((rows + kBM - 1) / kBM) * (out_features / 128);
+  L.total = L.ncnt + align_up(4 * (size_t)L.ncnt_ints);
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -313,9 +343,8 @@ const char *exl3_status_string(int32_t s) {
 }
 
 size_t exl3_linear_workspace_size(int32_t rows, int32_t in_features, int32_t out_features) {
-  (void)out_features;
-  if (rows < 0 || in_features < 0) return 0;
-  return 256 + align_up(2 * (size_t)rows * in_features);
+  if (rows < 0 || in_features < 0 || out_features < 0) return 0;
+  return lin_layout(rows, in_features, out_features).total;
 }
 
 int32_t exl3_linear(const uint16_t *x, int32_t rows, const exl3_proj *proj, void *out,
@@ -334,8 +363,9 @@ int32_t exl3_linear(const uint16_t *x, int32_t rows, const exl3_proj *proj, void
   if (int32_t s = check_proj_device(proj)) return s;
 
   hipStream_t st = (hipStream_t)stream;
+  const LinLayout LL = lin_layout(rows, proj->in_features, proj->out_features);
   int32_t *ctrl = (int32_t *)ws;
-  uint16_t *xt = at<uint16_t>(ws, 256);
+  uint16_t *xt = at<uint16_t>(ws, LL.xt);
   RotParams rp{};
   rp.x = x;
   rp.H = proj->in_features;
@@ -344,6 +374,8 @@ int32_t exl3_linear(const uint16_t *x, int32_t rows, const exl3_proj *proj, void
   rp.nitems = rows;
   rp.xt = xt;
   rp.ctrl_clear = ctrl;
+  rp.zero = LL.ncnt_ints ? at<int32_t>(ws, LL.ncnt) : nullptr;
+  rp.nzero = LL.ncnt_ints;
   {
     ProfScope ps(st, EXL3_K_ROTATE);
     if (launch_rotate(rp, st) != hipSuccess) return EXL3_E_LAUNCH;
@@ -361,9 +393,11 @@ int32_t exl3_linear(const uint16_t *x, int32_t rows, const exl3_proj *proj, void
   if (out_dtype == EXL3_F32) g.out_f32 = (float *)out;
   else g.out_h = (uint16_t *)out;
   g.ctrl = ctrl;
+  g.nacc = at<float>(ws, LL.nacc);
+  g.ncnt = at<int32_t>(ws, LL.ncnt);
   ProfScope ps(st, EXL3_K_LINEAR);
   const int fo = proj->out_features;
-  const bool wide = linear_wide(rows, fo);
+  const bool wide = LL.wide;
   const hipError_t le =
       wide ? launch_gemm(EPI_LINEAR, g, (rows + kBMWide - 1) / kBMWide, (fo + 255) / 256, st, true)
            : launch_gemm(EPI_LINEAR, g, (rows + kBM - 1) / kBM, fo / 128, st, false);
@@ -497,6 +531,8 @@ int32_t exl3_moe_forward(const uint16_t *x, int32_t rows, const void *ids, int32
   p.out_f32 = out_dtype == EXL3_F32;
   p.H = H;
   p.ctrl = at<int32_t>(ws, L.ctrl);
+  p.zero = L.ncnt_ints ? at<int32_t>(ws, L.ncnt) : nullptr;
+  p.nzero = L.ncnt_ints;
   {
     ProfScope ps(st, EXL3_K_PACK);
     if (launch_pack(p, st) != hipSuccess) return EXL3_E_LAUNCH;
@@ -547,6 +583,8 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t rows, int32_t topk,
   p.out_f32 = out_dtype == EXL3_F32;
   p.H = H;
   p.ctrl = at<int32_t>(ws, L.ctrl);
+  p.zero = L.ncnt_ints ? at<int32_t>(ws, L.ncnt) : nullptr;
+  p.nzero = L.ncnt_ints;
   {
     ProfScope ps(st, EXL3_K_PACK);
     if (launch_pack(p, st) != hipSuccess) return EXL3_E_LAUNCH;

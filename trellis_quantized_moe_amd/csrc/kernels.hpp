@@ -37,6 +37,10 @@ struct GemmParams {
   const float *weight_of_pos;  // DOWN
   int pass_base;               // DOWN: packed position of tile row 0
   int32_t *ctrl;               // [1] counts bad stage entries
+  // narrow tiles: pre-rotation sums [rows][NPROJ][out_f] and per (tile,
+  // 128-column block) completion counts, zero between launches
+  float *nacc;
+  int32_t *ncnt;
 };
 
 struct RotParams {
@@ -53,6 +57,8 @@ struct RotParams {
   int nitems;  // positions of this pass (upper bound) or rows
   uint16_t *xt;  // [nitems][nproj][H]
   int32_t *ctrl_clear;  // if set, block 0 zeroes ctrl[1] (bad stage entries)
+  int32_t *zero;        // if set, zeroed (nzero ints) before the GEMMs run
+  int nzero;
 };
 
 struct CombineParams {
@@ -84,6 +90,8 @@ struct PackParams {
   void *out;
   int out_f32, H;
   int32_t *ctrl;  // [0] dropped pairs, [1] bad stage entries (cleared)
+  int32_t *zero;  // narrow-tile completion counts, zeroed (nzero ints)
+  int nzero;
 };
 
 hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks,

@@ -20,6 +20,11 @@ __global__ void __launch_bounds__(256) rotate_kernel(RotParams p) {
   if (p.ctrl_clear && blockIdx.x == 0 && threadIdx.x == 0) {
     p.ctrl_clear[1] = 0;  // bad stage entries
   }
+  if (p.zero) {  // narrow-tile completion counts of the GEMM that follows
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < p.nzero;
+         i += (int64_t)gridDim.x * blockDim.x)
+      p.zero[i] = 0;
+  }
   const int64_t per_item = (int64_t)p.nproj * nblk;
   if (gid >= (int64_t)p.nitems * per_item) return;
   const int item = (int)(gid / per_item);

@@ -169,6 +169,7 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
   if (tid == 0 && p.ctrl) {
     p.ctrl[1] = 0;  // bad stage entries
   }
+  for (int i = tid; i < p.nzero; i += kPackThreads) p.zero[i] = 0;
 
   // expert of every kept position (binary search over the offsets)
   const int kept = s_off[E];
