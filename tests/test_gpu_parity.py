@@ -307,3 +307,80 @@ def test_linear_wide_multistage_parity():
     ref = olinear.linear(x[[0, 4, 1023]], p, "R")
     assert _rel_err(y.cpu().double().numpy()[[0, 4, 1023]], ref) <= TOL
     assert torch.equal(y_small.view(torch.int32), y[:5].view(torch.int32))
+
+
+# ------------------------------------------ prefill workload at full scale
+def _ulp_dist(a16, b16):
+    """Distance in fp16 ulps between two fp16 arrays (ordered bit patterns)."""
+    def ordered(v):
+        i = v.view(np.uint16).astype(np.int32)
+        return np.where(i & 0x8000, 0x8000 - (i & 0x7FFF), 0x8000 + i)
+    return np.abs(ordered(a16) - ordered(b16))
+
+
+def test_prefill_workload_full_scale():
+    """The mixed-width prefill layer at its full size: 192 experts, top-8,
+    hidden 6144, intermediate 2048, K per expert in {3,4,5,6,8}, 3072 rows,
+    Zipf(1.2) routing, capacity 2048 pairs (12 passes, expert spans cut across
+    passes). Checks, in the launch configuration the benchmark times:
+      - capacity invariance at full scale: 12 passes == one pass, bit for bit;
+      - the rotated down input a~ of sampled rows (read from the one-pass
+        workspace) against the oracle's: within one fp16 ulp of the oracle
+        value plus 2^-16 of the row's largest |a~| (the GPU rounds an fp32
+        value carrying the error of 6144-term fp32 MFMA accumulations, a few
+        1e-6 of the row's scale, so entries that cancel to near zero may
+        differ by more than one ulp);
+      - the down projection + combine of those rows, teacher-forced with the
+        GPU's a~, against the oracle (the 2e-3 RMS-relative bar);
+      - the end-to-end rows against the oracle (reported; a~ rounding flips
+        on heavy-tailed SwiGLU outputs set its size)."""
+    from oracle import route as oroute
+    _say("prefill workload: drawing inputs")
+    wl = synth.moe_workload("prefill", materialize=False)
+    P = wl.rows * wl.topk
+    counts = np.bincount(wl.ids.reshape(-1), minlength=wl.num_experts)
+    assert int(np.sum(counts > wl.capacity)) >= 2
+    gate, up, down = (exl3.DeviceProj(p, DEV, words_fn=synth.realize_words)
+                      for p in (wl.gate, wl.up, wl.down))
+    x, ids, w = exl3.device_inputs(wl, DEV)
+    _say("prefill workload: 12-pass forward")
+    y = exl3.exl3_moe_forward(x, ids, w, gate, up, down, wl.capacity, torch.float32)
+    _say("prefill workload: one-pass forward")
+    lay = exl3.moe_layout(wl.rows, wl.topk, wl.num_experts, wl.hidden, wl.intermediate, P)
+    assert lay.passes == 1
+    ws = torch.empty(lay.total, dtype=torch.uint8, device=DEV)
+    y1 = exl3.exl3_moe_forward(x, ids, w, gate, up, down, P, torch.float32, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y1.view(torch.int32))
+
+    at_all = ws[lay.at:lay.at + P * wl.intermediate * 2].view(torch.float16)
+    at_all = exl3.unpermute_rotated(at_all.view(P, wl.intermediate))
+    pack = oroute.route_pack(wl.ids, wl.weights_f64, wl.num_experts)
+    sample = [5, 2999]
+    experts = {int(wl.ids[r, j]) for r in sample for j in range(wl.topk)}
+    views = [synth.materialized_view(p, experts) for p in (wl.gate, wl.up, wl.down)]
+    y_tf = np.zeros((len(sample), wl.hidden))
+    y_e2e = np.zeros((len(sample), wl.hidden))
+    ulps, excess = [], []
+    for li, r in enumerate(sample):
+        for j in range(wl.topk):
+            e = int(wl.ids[r, j])
+            pos = int(pack["pos_of_pair"][r * wl.topk + j])
+            at_ref = omoe.stage1(wl.x[r:r + 1].astype(np.float64), e, *views, "R")
+            at_gpu = at_all[pos].cpu().numpy()
+            ref16 = at_ref[0].astype(np.float16)
+            ulps.append(_ulp_dist(at_gpu, ref16))
+            ulp = np.spacing(np.abs(ref16)).astype(np.float64)
+            bound = ulp + 2.0 ** -16 * np.abs(at_ref[0]).max()
+            excess.append(np.abs(at_gpu.astype(np.float64) - at_ref[0]) / bound)
+            wt = wl.weights_f64[r, j]
+            y_tf[li] += wt * omoe.down_output(at_gpu.astype(np.float64)[None], e, views[2])[0]
+            y_e2e[li] += wt * omoe.down_output(at_ref, e, views[2])[0]
+    ulps, excess = np.concatenate(ulps), np.concatenate(excess)
+    got = y.cpu().double().numpy()[sample]
+    e_tf, e_e2e = _rel_err(got, y_tf), _rel_err(got, y_e2e)
+    _say("  a~ max ulp %d, fraction off %.2e, max |diff|/bound %.3f; teacher-forced err "
+         "%.3e; end-to-end err %.3e" % (ulps.max(), np.mean(ulps > 0), excess.max(), e_tf, e_e2e))
+    assert excess.max() <= 1.0
+    assert e_tf <= TOL
+    assert e_e2e <= TOL
