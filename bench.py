@@ -200,6 +200,20 @@ def cpu_baseline(wl, synth):
                       "token" % dt}
 
 
+KERNEL_SOURCES = ("gemm_wide.hip", "gemm_shared.hpp", "common.hpp", "kernels.hpp")
+
+
+def kernel_source_sha():
+    """SHA-256 over the sources of the 128-row GEMM (the prefill's dominant
+    kernel): a committed counter summary applies only to this exact code."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "trellis_quantized_moe_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def copy_probe(torch, gib=1.0, reps=5):
     """Plain device copy of known size, used to calibrate HBM counters."""
     n = int(gib * (1 << 30))
@@ -256,9 +270,7 @@ def main():
         import hashlib
         with open(args.traffic) as f:
             t = json.load(f)
-        src = os.path.join(ROOT, "trellis_quantized_moe_amd", "csrc", "gemm.hip")
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = kernel_source_sha()
         if (t.get("kernel") == dom and t.get("workload") == "prefill"
                 and t.get("source_sha256") == sha):
             traffic = t.get("bytes_per_launch")
