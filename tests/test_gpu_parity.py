@@ -384,3 +384,79 @@ def test_prefill_workload_full_scale():
     assert excess.max() <= 1.0
     assert e_tf <= TOL
     assert e_e2e <= TOL
+
+
+# ------------------------------------- graph capture and cartridge swapping
+def test_additive_graph_capture_cartridge_swap():
+    """exl3_moe_additive captured once in a graph; between replays only the
+    contents of the residual-stage tables change (pointer and scale rows of
+    stage 1: cartridge A -> cartridge B -> no residual -> A). Every replay
+    equals an eager call with the same tables bit for bit, and restoring the
+    tables restores the output bytes (exllamav3 PR #284 "MoE: Add fused
+    additive EXL3 kernels", Summary and API contract: graph-safe additive
+    stages; table contents may change between replays)."""
+    small = dict(rows=24, E=16, topk=4, H=256, I=512)
+    wa = synth.moe_workload("additive", **small)
+    wb = synth.moe_workload("additive", seed=77, **small)
+
+    def with_residual(p, q):
+        return synth.Proj(p.in_features, p.out_features, p.num_experts,
+                          [p.words[0], q.words[1]], np.stack([p.scale[0], q.scale[1]]),
+                          np.stack([p.bits[0], q.bits[1]]), p.suh, p.svh, p.chscale)
+
+    projs_a = [exl3.DeviceProj(p, DEV) for p in (wa.gate, wa.up, wa.down)]
+    projs_b = [exl3.DeviceProj(with_residual(p, q), DEV)
+               for p, q in zip((wa.gate, wa.up, wa.down), (wb.gate, wb.up, wb.down))]
+    x, ids, w = exl3.device_inputs(wa, DEV)
+    meta = exl3.exl3_route_pack(ids, w, wa.num_experts)
+    cap = wa.rows * wa.topk
+    need = exl3.moe_workspace_size(wa.rows, wa.topk, wa.num_experts, wa.hidden,
+                                   wa.intermediate, cap)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    out = torch.empty(wa.rows, wa.hidden, dtype=torch.float32, device=DEV)
+    saved = [(p.trellis.clone(), p.scale.clone()) for p in projs_a]
+
+    def set_cartridge(src):
+        for p, s in zip(projs_a, src):
+            p.trellis[1].copy_(s[0][1])
+            p.scale[1].copy_(s[1][1])
+
+    def eager():
+        y = exl3.exl3_moe_additive(x, wa.topk, meta, *projs_a, cap, torch.float32)
+        torch.cuda.synchronize()
+        return y.clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        exl3.exl3_moe_additive(x, wa.topk, meta, *projs_a, cap, torch.float32, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        exl3.exl3_moe_additive(x, wa.topk, meta, *projs_a, cap, torch.float32, out=out, ws=ws)
+    torch.cuda.synchronize()
+
+    def replay():
+        out.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        return out.clone()
+
+    bits = lambda t: t.view(torch.int32)
+    ya = replay()
+    assert torch.equal(bits(ya), bits(eager()))
+    set_cartridge([(p.trellis, p.scale) for p in projs_b])
+    yb = replay()
+    assert torch.equal(bits(yb), bits(eager()))
+    assert not torch.equal(bits(yb), bits(ya))
+    for p in projs_a:
+        p.scale[1].zero_()
+    y0 = replay()
+    assert torch.equal(bits(y0), bits(eager()))
+    set_cartridge(saved)
+    assert torch.equal(bits(replay()), bits(ya))
+    # the replayed outputs also meet the oracle bar (cartridge A)
+    ref = omoe.moe_forward(wa.x, wa.ids, wa.weights_f64, wa.gate, wa.up, wa.down, "R")
+    assert _rel_err(ya.cpu().double().numpy(), ref) <= TOL

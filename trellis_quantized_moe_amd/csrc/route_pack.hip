@@ -204,9 +204,10 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
   }
 
   // rows whose pairs were all dropped produce zeros: one row per thread to
-  // find them (rare), then the row is cleared by that thread
+  // find them (rare), then the row is cleared by that thread. A pack that
+  // dropped nothing has no such row.
   __syncthreads();
-  if (p.out) {
+  if (p.out && (!p.do_pack || s_dropped > 0)) {
     for (int r = tid; r < p.rows; r += kPackThreads) {
       bool any = false;
       for (int j = 0; j < p.topk; ++j) any |= p.pos_of_pair[r * p.topk + j] >= 0;
