@@ -32,11 +32,13 @@ namespace exl3 {
 // work item per few CUs' worth of waves even at one routed row.
 //
 // Trellis: each wave copies its strip global->LDS by DMA in blocks of 128
-// inputs (8 tiles, 256K bytes) into a ring of kNRing slots of its own, five
+// inputs (8 tiles, 256K bytes) into a ring of kNRing slots of its own, three
 // blocks ahead of the one it decodes. A (rotated rows, L2-resident) goes
-// straight to registers four blocks ahead: vector loads complete in order, so
+// straight to registers two blocks ahead: vector loads complete in order, so
 // the wait for A[b] also waits for every trellis block issued before it, and
-// A's lead bounds the trellis lead. Every wave issues the same loads every
+// A's lead bounds the trellis lead. (Deeper rings measured slower: the
+// kernel is bound by issue and VALU more than by memory latency, and four
+// waves per SIMD beat a deeper ring per wave.) Every wave issues the same loads every
 // block (past the end it re-reads the last block), so each wait is an exact
 // vmcnt.
 //
@@ -49,7 +51,7 @@ namespace exl3 {
 // The pre-rotation fp32 sums go to workspace scratch; the last of the work
 // items of a 128-column block (an atomic count: 2, or 4 for gate + up) runs
 // the shared epilogue on the whole block.
-constexpr int kNRing = 6;
+constexpr int kNRing = 4;
 constexpr int kNSlot = 2048;  // bytes: one block at K <= 8
 
 template <int K>
@@ -120,7 +122,7 @@ __device__ __forceinline__ const char *sgpr_ptr(const void *ptr) {
 }
 
 // P = MFMA chain of one stage over all inputs for this wave's strip.
-constexpr int kNADist = 4;  // A blocks in flight ahead of the one in use
+constexpr int kNADist = kNRing - 2;  // A blocks in flight ahead of the one in use
 
 template <int K>
 struct StreamChain {
@@ -140,7 +142,7 @@ struct StreamChain {
   uint32_t traddr[ND];
   uint32_t shift, mask;
   int nblk;
-  u32x4 a[kNADist + 1][4];  // A of blocks b .. b + kNADist (ring by b % 5)
+  u32x4 a[kNADist + 1][4];  // A of blocks b .. b + kNADist (ring by b % (kNADist + 1))
 
   __device__ __forceinline__ void load_a(int ba, int aslot) {
     const char *src = sgpr_ptr(abase + (size_t)ba * 256);
@@ -161,14 +163,17 @@ struct StreamChain {
 
   __device__ __forceinline__ void compute(int b, int aslot, f32x4 &acc) {
     const uint32_t base = (uint32_t)((b % kNRing) * kNSlot);
+    // the block's trellis words first (one LDS wait), then decode + MFMA
+    uint32_t raw[4][ND];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint32_t raw[ND];
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int j = 0; j < ND; ++j)
-        raw[j] = *(const uint32_t *)(ring + base + traddr[j] + s * 2 * TD * 4);
+        raw[s][j] = *(const uint32_t *)(ring + base + traddr[j] + s * 2 * TD * 4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
       uint32_t N[NN];
-      normalize(raw, shift, N);
+      normalize(raw[s], shift, N);
       const u32x4 w = {half_reg<K, 0>(N, mask), half_reg<K, 1>(N, mask),
                        half_reg<K, 2>(N, mask), half_reg<K, 3>(N, mask)};
       acc = mfma16x16x32(__builtin_bit_cast(f16x8, a[aslot][s]), __builtin_bit_cast(f16x8, w), acc);
@@ -184,6 +189,12 @@ struct StreamChain {
     compute(b, AS, acc);
   }
 
+  // blocks b .. b + kNADist (A ring slots 0 .. kNADist), those < nblk
+  template <int... Is>
+  __device__ __forceinline__ void blocks(int b, f32x4 &acc, std::integer_sequence<int, Is...>) {
+    ((b + Is < nblk ? block<Is>(b + Is, acc) : void()), ...);
+  }
+
   __device__ __forceinline__ f32x4 run() {
     const int last = nblk - 1;
     // prologue in steady-state order: T[0], then A[j] T[j + 1] for j = 0..3
@@ -194,13 +205,8 @@ struct StreamChain {
       issue_t(min(j + 1, last));
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int b = 0; b < nblk; b += 5) {
-      block<0>(b, acc);
-      if (b + 1 < nblk) block<1>(b + 1, acc);
-      if (b + 2 < nblk) block<2>(b + 2, acc);
-      if (b + 3 < nblk) block<3>(b + 3, acc);
-      if (b + 4 < nblk) block<4>(b + 4, acc);
-    }
+    for (int b = 0; b < nblk; b += kNADist + 1)
+      blocks(b, acc, std::make_integer_sequence<int, kNADist + 1>{});
     swait_vmcnt<0>();  // no DMA may land after the ring is reused
     return acc;
   }
@@ -270,7 +276,7 @@ __device__ __forceinline__ f32x4 stream_strip(const ProjDev &pd, int E, int e, i
 
 // grid: x = tile, y = NPROJ * (out_f / 64) column groups (projection major).
 template <int EPI>
-__global__ void __launch_bounds__(256, 3) gemm_narrow_kernel(GemmParams p) {
+__global__ void __launch_bounds__(256, 4) gemm_narrow_kernel(GemmParams p) {
   constexpr int NPROJ = (EPI == EPI_GATEUP) ? 2 : 1;
   __shared__ __attribute__((aligned(16))) char smem[4 * kNRing * kNSlot];
   __shared__ int s_last;
