@@ -9,10 +9,11 @@
 
 namespace exl3 {
 
-// One 16-lane group per (item, projection, 128-block), 16 groups per block.
-// Lane i loads entries 8i..8i+7 (16 bytes), transforms, and stores them as
-// one 16-byte run in the kSigma order: slots 0..7 of its half-group hold
-// entries {0,4,1,5,2,6,3,7} of the lane's 8.
+// One 16-lane group per (item, 128-block), 16 groups per block; the group
+// loads the x block once and writes it rotated for every projection. Lane i
+// loads entries 8i..8i+7 (16 bytes), transforms, and stores them as one
+// 16-byte run in the kSigma order: slots 0..7 of its half-group hold entries
+// {0,4,1,5,2,6,3,7} of the lane's 8.
 __global__ void __launch_bounds__(256) rotate_kernel(RotParams p) {
   const int nblk = p.H >> 7;
   const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -25,11 +26,9 @@ __global__ void __launch_bounds__(256) rotate_kernel(RotParams p) {
          i += (int64_t)gridDim.x * blockDim.x)
       p.zero[i] = 0;
   }
-  const int64_t per_item = (int64_t)p.nproj * nblk;
-  if (gid >= (int64_t)p.nitems * per_item) return;
-  const int item = (int)(gid / per_item);
-  const int rem = (int)(gid - (int64_t)item * per_item);
-  const int pj = rem / nblk, blk = rem - pj * nblk;
+  if (gid >= (int64_t)p.nitems * nblk) return;
+  const int item = (int)(gid / nblk);
+  const int blk = (int)(gid - (int64_t)item * nblk);
 
   int row, e;
   if (p.pair_of_pos != nullptr) {
@@ -43,29 +42,38 @@ __global__ void __launch_bounds__(256) rotate_kernel(RotParams p) {
     row = item;
     e = 0;
   }
-  const u32x4 xv = *(const u32x4 *)(p.x + (int64_t)row * p.H + blk * 128 + 8 * i);
-  const u32x4 sv = *(const u32x4 *)(p.suh[pj] + (int64_t)e * p.H + blk * 128 + 8 * i);
-  // halves are unpacked with shifts: this compiler mis-compiles a bit_cast
-  // of a vector element taken inside an unrolled loop (it reuses element 0)
-  float v[8];
+  const int64_t col = blk * 128 + 8 * i;
+  const u32x4 xv = *(const u32x4 *)(p.x + (int64_t)row * p.H + col);
+  u32x4 sv[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t xw = xv[j], sw = sv[j];
-    v[2 * j] = f16_bits_to_f32((uint16_t)(xw & 0xFFFFu)) * f16_bits_to_f32((uint16_t)(sw & 0xFFFFu));
-    v[2 * j + 1] = f16_bits_to_f32((uint16_t)(xw >> 16)) * f16_bits_to_f32((uint16_t)(sw >> 16));
+  for (int pj = 0; pj < 2; ++pj)
+    if (pj < p.nproj) sv[pj] = *(const u32x4 *)(p.suh[pj] + (int64_t)e * p.H + col);
+#pragma unroll
+  for (int pj = 0; pj < 2; ++pj) {
+    if (pj >= p.nproj) break;
+    // halves are unpacked with shifts: this compiler mis-compiles a bit_cast
+    // of a vector element taken inside an unrolled loop (it reuses element 0)
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t xw = xv[j], sw = sv[pj][j];
+      v[2 * j] = f16_bits_to_f32((uint16_t)(xw & 0xFFFFu)) * f16_bits_to_f32((uint16_t)(sw & 0xFFFFu));
+      v[2 * j + 1] = f16_bits_to_f32((uint16_t)(xw >> 16)) * f16_bits_to_f32((uint16_t)(sw >> 16));
+    }
+    fwht128_lane8(v);
+    uint16_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = f32_to_f16_bits(v[j] * kRsqrt128);
+    const u32x4 o = {(uint32_t)h[0] | ((uint32_t)h[4] << 16), (uint32_t)h[1] | ((uint32_t)h[5] << 16),
+                     (uint32_t)h[2] | ((uint32_t)h[6] << 16), (uint32_t)h[3] | ((uint32_t)h[7] << 16)};
+    *(u32x4 *)(p.xt + ((int64_t)item * p.nproj + pj) * p.H + col) = o;
   }
-  fwht128_lane8(v);
-  uint16_t h[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) h[j] = f32_to_f16_bits(v[j] * kRsqrt128);
-  const u32x4 o = {(uint32_t)h[0] | ((uint32_t)h[4] << 16), (uint32_t)h[1] | ((uint32_t)h[5] << 16),
-                   (uint32_t)h[2] | ((uint32_t)h[6] << 16), (uint32_t)h[3] | ((uint32_t)h[7] << 16)};
-  *(u32x4 *)(p.xt + ((int64_t)item * p.nproj + pj) * p.H + blk * 128 + 8 * i) = o;
 }
 
 hipError_t launch_rotate(const RotParams &p, hipStream_t s) {
-  const int64_t groups = (int64_t)p.nitems * p.nproj * (p.H >> 7);
+  const int64_t groups = (int64_t)p.nitems * (p.H >> 7);
   if (groups <= 0) return hipSuccess;
+  if (p.nproj < 1 || p.nproj > 2) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rotate_kernel, dim3((unsigned)((groups + 15) / 16)), dim3(256), 0, s, p);
   return hipGetLastError();
 }

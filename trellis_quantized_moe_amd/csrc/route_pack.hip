@@ -5,10 +5,13 @@
 // API contract: num_active counts non-empty experts and is only a hint;
 // Relationship to #246: route histogram, scan and stable packing).
 //
-// One workgroup of 1024 threads (16 waves). Pairs are visited in chunks of
-// 1024 in pair order; inside a chunk each lane finds the lanes of its wave
-// holding the same expert with a bitwise ballot match, and earlier waves'
-// counts come from an LDS table, so positions follow pair order exactly.
+// One workgroup of 1024 threads (16 waves). Wave w owns one contiguous
+// segment of the pairs and walks it twice, 64 pairs per round in pair order:
+// first it counts its pairs per expert into an LDS row of its own, then (once
+// the counts are scanned over experts and over the waves before it) it gives
+// each pair the next position of its expert. Inside a round, the lanes that
+// hold the same expert find each other with bitwise ballots, so positions
+// follow pair order exactly without atomics on the positions.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -41,6 +44,39 @@ __device__ int block_exclusive_scan(int v, int *tmp, int &total) {
   return before + x - v;
 }
 
+// Inclusive prefix maximum over the block (1024 threads); `tmp` holds
+// kPackWaves ints. Returns the prefix and sets `all` to the block maximum.
+__device__ int block_inclusive_max(int v, int *tmp, int &all) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x = max(x, y);
+  }
+  if (lane == 63) tmp[w] = x;
+  __syncthreads();
+  int before = x, m = INT_MIN;
+  for (int k = 0; k < kPackWaves; ++k) {
+    const int t = tmp[k];
+    if (k < w) before = max(before, t);
+    m = max(m, t);
+  }
+  __syncthreads();
+  all = m;
+  return before;
+}
+
+// Last expert whose span starts at or before `pos` (offsets nondecreasing).
+__device__ __forceinline__ int expert_at(const int *off, int E, int pos) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= pos) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 __device__ __forceinline__ float load_weight(const void *w, int dtype, int q) {
   if (dtype == 3) return ((const float *)w)[q];
   const uint16_t b = ((const uint16_t *)w)[q];
@@ -57,11 +93,23 @@ __device__ __forceinline__ int load_expert(const void *ids, int i64, int q, int 
   return (v >= 0 && v < E) ? v : -1;
 }
 
+// Lanes of the wave holding the same key as this lane (among `live`), using
+// the low `nb` bits of the key.
+__device__ __forceinline__ uint64_t match_key(int key, uint64_t live, int nb) {
+  uint64_t m = live;
+  for (int b = 0; b < nb; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    m &= bit ? bal : ~bal;
+  }
+  return m;
+}
+
+constexpr int kPackBatch = 8;  // rounds whose loads are issued together
+
 __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
-  __shared__ int s_cnt[kMaxE];
+  __shared__ int s_wc[kPackWaves][kMaxE];  // per wave: count, then next position
   __shared__ int s_off[kMaxE + 1];
-  __shared__ int s_cur[kMaxE];
-  __shared__ uint8_t s_wcnt[kPackWaves][kMaxE];
   __shared__ int s_tmp[kPackWaves];
   __shared__ int s_dropped;
 
@@ -70,39 +118,54 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
   const int pairs = p.rows * p.topk;
 
   if (p.do_pack) {
-    for (int e = tid; e < E; e += kPackThreads) s_cnt[e] = 0;
-    for (int k = tid; k < kPackWaves * kMaxE; k += kPackThreads) (&s_wcnt[0][0])[k] = 0;
+    // the wave's segment: whole rounds of 64 pairs
+    const int seg = (((pairs + kPackWaves - 1) / kPackWaves) + 63) & ~63;
+    const int q0 = w * seg;
+    const int q1 = min(q0 + seg, pairs);
+    const int nb = 32 - __clz(E);  // bits of the keys 0 .. E
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int *wc = s_wc[w];
+    for (int e = lane; e < E; e += 64) wc[e] = 0;
     if (tid == 0) s_dropped = 0;
     __syncthreads();
-    // a1: histogram (integer LDS atomics: the counts are order-free)
+
+    // a1: this wave's histogram (only this wave touches its row)
     int drop = 0;
-    for (int q = tid; q < pairs; q += kPackThreads) {
-      const int e = load_expert(p.ids, p.ids_i64, q, E);
-      if (e >= 0) atomicAdd(&s_cnt[e], 1);
-      else ++drop;
+    for (int qb = q0; qb < q1; qb += 64 * kPackBatch) {
+      int eb[kPackBatch];
+#pragma unroll
+      for (int i = 0; i < kPackBatch; ++i) {
+        const int q = qb + 64 * i + lane;
+        eb[i] = (q < q1) ? load_expert(p.ids, p.ids_i64, q, E) : -2;
+      }
+#pragma unroll
+      for (int i = 0; i < kPackBatch; ++i) {
+        const int e = eb[i];
+        if (e >= 0) atomicAdd(&wc[e], 1);  // counts are order-free
+        drop += (e == -1) ? 1 : 0;
+      }
     }
     if (drop) atomicAdd(&s_dropped, drop);
     __syncthreads();
-  } else {
-    // caller-supplied offsets, clamped so every index stays inside the pairs
-    for (int e = tid; e <= E; e += kPackThreads) s_off[e] = min(max(p.offset[e], 0), pairs);
-    __syncthreads();
-    for (int e = tid; e < E; e += kPackThreads) s_cnt[e] = max(s_off[e + 1] - s_off[e], 0);
-    __syncthreads();
-  }
 
-  // a2: exclusive scan (E <= 1024: one expert per thread)
-  {
-    const int c = (tid < E) ? s_cnt[tid] : 0;
-    int total;
-    const int ex = block_exclusive_scan(c, s_tmp, total);
-    int nact;
-    const int act = block_exclusive_scan((tid < E && c > 0) ? 1 : 0, s_tmp, nact);
-    (void)act;
-    if (p.do_pack) {
+    // a2: counts over the waves, exclusive scan over experts, then each
+    // wave's first position per expert
+    {
+      int c = 0;
+      if (tid < E)
+        for (int k = 0; k < kPackWaves; ++k) c += s_wc[k][tid];
+      int total;
+      const int ex = block_exclusive_scan(c, s_tmp, total);
+      int nact;
+      block_exclusive_scan((tid < E && c > 0) ? 1 : 0, s_tmp, nact);
       if (tid < E) {
+        int run = ex;
+        for (int k = 0; k < kPackWaves; ++k) {
+          const int t = s_wc[k][tid];
+          s_wc[k][tid] = run;
+          run += t;
+        }
         s_off[tid] = ex;
-        s_cur[tid] = ex;
         p.count[tid] = c;
         p.offset[tid] = ex;
       }
@@ -113,56 +176,54 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
         *p.status = s_dropped;
         if (p.ctrl) p.ctrl[0] = s_dropped;
       }
-    }
-    __syncthreads();
-  }
-
-  if (p.do_pack) {
-    // a3: stable scatter, 1024 pairs per round in pair order
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < pairs; base += kPackThreads) {
-      const int q = base + tid;
-      const bool in = q < pairs;
-      const int e = in ? load_expert(p.ids, p.ids_i64, q, E) : -1;
-      const bool valid = e >= 0;
-      // lanes of this wave with the same key (key = E for invalid lanes)
-      const int key = valid ? e : E;
-      uint64_t m = __ballot(in);
-#pragma unroll
-      for (int b = 0; b < 11; ++b) {
-        const bool bit = (key >> b) & 1;
-        const uint64_t bal = __ballot(bit);
-        m &= bit ? bal : ~bal;
-      }
-      const int rank = __popcll(m & lt_mask);
-      if (in && valid && rank == 0) s_wcnt[w][e] = (uint8_t)__popcll(m);
       __syncthreads();
-      if (in) {
+    }
+
+    // a3: stable scatter, the same walk again
+    for (int qb = q0; qb < q1; qb += 64 * kPackBatch) {
+      int eb[kPackBatch];
+      float wb[kPackBatch];
+#pragma unroll
+      for (int i = 0; i < kPackBatch; ++i) {
+        const int q = qb + 64 * i + lane;
+        const bool in = q < q1;
+        eb[i] = in ? load_expert(p.ids, p.ids_i64, q, E) : -2;
+        wb[i] = in ? load_weight(p.w, p.w_dtype, q) : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < kPackBatch; ++i) {
+        if (qb + 64 * i >= q1) break;  // uniform
+        const int q = qb + 64 * i + lane;
+        const int e = eb[i];
+        const bool valid = e >= 0;
+        const uint64_t m = match_key(valid ? e : E, __ballot(valid), nb);
         if (valid) {
-          int pos = s_cur[e] + rank;
-          for (int k = 0; k < w; ++k) pos += s_wcnt[k][e];
+          const int rank = __popcll(m & lt_mask);
+          const int base = wc[e];
+          const int pos = base + rank;
+          if (rank == 0) wc[e] = base + __popcll(m);
           p.pair_of_pos[pos] = q;
-          p.weight_of_pos[pos] = load_weight(p.w, p.w_dtype, q);
+          p.weight_of_pos[pos] = wb[i];
           p.pos_of_pair[q] = pos;
-        } else {
+        } else if (e == -1) {
           p.pos_of_pair[q] = -1;
         }
       }
-      __syncthreads();
-      for (int x = tid; x < E; x += kPackThreads) {
-        int add = 0;
-        for (int k = 0; k < kPackWaves; ++k) {
-          add += s_wcnt[k][x];
-          s_wcnt[k][x] = 0;
-        }
-        s_cur[x] += add;
-      }
-      __syncthreads();
     }
     for (int pos = s_off[E] + tid; pos < pairs; pos += kPackThreads) {
       p.pair_of_pos[pos] = -1;
       p.weight_of_pos[pos] = 0.0f;
     }
+  } else {
+    // caller-supplied offsets, clamped into the pairs and made nondecreasing
+    // (a prefix maximum leaves consistent offsets unchanged), so every index
+    // derived from them stays inside the pairs and the experts
+    const int v = (tid < E) ? min(max(p.offset[tid], 0), pairs) : 0;
+    int vmax;
+    const int m = block_inclusive_max(v, s_tmp, vmax);
+    if (tid < E) s_off[tid] = m;
+    if (tid == 0) s_off[E] = max(min(max(p.offset[E], 0), pairs), vmax);
+    __syncthreads();
   }
 
   if (!p.do_plan) return;
@@ -171,36 +232,50 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
   }
   for (int i = tid; i < p.nzero; i += kPackThreads) p.zero[i] = 0;
 
-  // expert of every kept position (binary search over the offsets)
+  // expert of every kept position, one expert per wave at a time (positions
+  // before the first span, possible only with caller-supplied offsets, get
+  // expert 0)
   const int kept = s_off[E];
-  for (int pos = tid; pos < kept; pos += kPackThreads) {
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {  // last e with s_off[e] <= pos
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= pos) lo = mid; else hi = mid - 1;
-    }
-    p.expert_of_pos[pos] = lo;
+  for (int e = w; e < E; e += kPackWaves) {
+    const int a = (e == 0) ? 0 : s_off[e], b = s_off[e + 1];
+    for (int pos = a + lane; pos < b; pos += 64) p.expert_of_pos[pos] = e;
   }
 
-  // a4: per pass, the row tiles of every expert's sub-span
-  for (int pass = 0; pass < p.passes; ++pass) {
-    const int pb = pass * p.capacity, pe = pb + p.capacity;
-    int lo = 0, hi = 0, nt = 0;
-    if (tid < E) {
-      lo = max(s_off[tid], pb);
-      hi = min(s_off[tid + 1], pe);
-      nt = hi > lo ? (hi - lo + p.bm - 1) / p.bm : 0;
-    }
-    int total;
-    const int slot0 = block_exclusive_scan(nt, s_tmp, total);
+  // a4: per pass (one wave each), the row tiles of every expert's sub-span
+  // inside the pass, in expert order; only the experts overlapping the pass
+  // are visited
+  for (int pass = w; pass < p.passes; pass += kPackWaves) {
+    const int pb = pass * p.capacity;
+    const int pe = (int)min((int64_t)pb + p.capacity, (int64_t)kept);
     int32_t *plan = p.plan + (int64_t)pass * (1 + 3 * p.slots);
-    for (int t = 0; t < nt; ++t) {
-      int32_t *d = plan + 1 + 3 * (slot0 + t);
-      d[0] = tid;
-      d[1] = lo - pb + t * p.bm;
-      d[2] = min(p.bm, hi - lo - t * p.bm);
+    int total = 0;
+    if (pb < pe) {
+      const int e_lo = expert_at(s_off, E, pb), e_hi = expert_at(s_off, E, pe - 1);
+      for (int eb = e_lo; eb <= e_hi; eb += 64) {
+        const int e = eb + lane;
+        int lo = 0, hi = 0, nt = 0;
+        if (e <= e_hi) {
+          lo = max(s_off[e], pb);
+          hi = min(s_off[e + 1], pe);
+          nt = hi > lo ? (hi - lo + p.bm - 1) / p.bm : 0;
+        }
+        int x = nt;  // inclusive scan over the wave
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(x, d, 64);
+          if (lane >= d) x += y;
+        }
+        const int slot0 = total + x - nt;
+        for (int t = 0; t < nt; ++t) {
+          int32_t *d = plan + 1 + 3 * (slot0 + t);
+          d[0] = e;
+          d[1] = lo - pb + t * p.bm;
+          d[2] = min(p.bm, hi - lo - t * p.bm);
+        }
+        total += __shfl(x, 63, 64);
+      }
     }
-    if (tid == 0) plan[0] = total;
+    if (lane == 0) plan[0] = total;
   }
 
   // rows whose pairs were all dropped produce zeros: one row per thread to
