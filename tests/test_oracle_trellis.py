@@ -106,3 +106,15 @@ def test_tensor_order_is_out_major():
     expect[32:48, 16:32] = 1481 / 8192
     assert np.array_equal(W, expect)
     assert np.array_equal(trellis.dequantize(w, fin, fout, K, "window"), W)
+
+
+def test_golden_files_match_their_generator():
+    # the stored vectors are exactly what the independent bit-by-bit
+    # generator beside them prints
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "make_vectors", os.path.join(GOLDEN, "make_vectors.py"))
+    mv = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mv)
+    assert mv.stored_lines("codebook_values.txt") == mv.codebook_lines()
+    assert mv.stored_lines("tile_vectors.txt") == mv.tile_lines()
