@@ -296,7 +296,9 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     cp.out_f32 = out_dtype == EXL3_F32;
     {
       ProfScope ps(st, EXL3_K_COMBINE);
-      if (launch_combine(cp, npos, st) != hipSuccess) return EXL3_E_LAUNCH;
+      const hipError_t err =
+          (L.passes == 1) ? launch_combine_rows(cp, st) : launch_combine(cp, npos, st);
+      if (err != hipSuccess) return EXL3_E_LAUNCH;
     }
   }
   return EXL3_OK;

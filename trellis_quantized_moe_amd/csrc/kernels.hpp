@@ -101,6 +101,7 @@ hipError_t launch_gemm_wide(int epi, const GemmParams &p, int tiles, int nblocks
                             hipStream_t s);
 hipError_t launch_rotate(const RotParams &p, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int npos, hipStream_t s);
+hipError_t launch_combine_rows(const CombineParams &p, hipStream_t s);
 hipError_t launch_pack(const PackParams &p, hipStream_t s);
 hipError_t launch_decode_tiles(const uint16_t *words, int ntiles, int K,
                                uint16_t *out, hipStream_t s);
