@@ -206,7 +206,9 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t rows, int32_t topk,
 /*
  * Workspace layout of exl3_moe_forward / exl3_moe_additive (byte offsets
  * from ws, each region 256-byte aligned, in this order):
- *   ctrl        256 B   int32[64]: [0] dropped pairs, [1] bad stage entries
+ *   ctrl        256 B   int32[64]: [0] dropped pairs, [1] bad stage entries,
+ *               [2] waits between the gate/up and down items of one pass that
+ *               gave up (never expected; the output is then invalid)
  *   meta        forward only: count[E], offset[E+1], pair_of_pos[P],
  *               weight_of_pos[P], pos_of_pair[P], num_active[1] (P = pairs)
  *   expert_of_pos int32[P]
@@ -250,7 +252,8 @@ int32_t exl3_decode_tiles(const uint16_t *words, int32_t ntiles, int32_t K,
  */
 enum exl3_kernel_id {
   EXL3_K_PACK = 1, EXL3_K_ROTATE = 2, EXL3_K_GATEUP = 3, EXL3_K_DOWN = 4,
-  EXL3_K_COMBINE = 5, EXL3_K_LINEAR = 6, EXL3_K_DECODE = 7
+  EXL3_K_COMBINE = 5, EXL3_K_LINEAR = 6, EXL3_K_DECODE = 7,
+  EXL3_K_EXPERTS = 8 /* gate/up and down of one pass in one launch (128-row tiles) */
 };
 int32_t exl3_profile_begin(int32_t max_launches);
 int32_t exl3_profile_end(int32_t *kernel_ids /* host */, float *ms /* host */,

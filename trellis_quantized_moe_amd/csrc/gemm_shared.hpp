@@ -31,7 +31,9 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // was computed in. T is an LDS tile of fp32 pre-rotation accumulators:
 // T[pj * proj_stride + row * ld + c], c = 0 .. 128*nblk-1 (columns relative
 // to colbase). One 16-lane group handles one (row, 128-block) at a time.
-template <int EPI>
+// COH: a~ (gate/up) is written with device-coherent stores, for a reader in
+// the same launch.
+template <int EPI, bool COH = false>
 __device__ __forceinline__ void epilogue(const GemmParams &p, float *T, int ld, int proj_stride,
                                          int e, int row0, int nrows, int colbase, int nblk) {
   const int ngroups = blockDim.x >> 4;
@@ -69,7 +71,13 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, float *T, int ld, 
       fwht128_group16(v);
       uint16_t *o = p.out_h + (int64_t)(row0 + row) * p.ldo + colbase;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o[16 * j + sigma_inv(i)] = f32_to_f16_bits(v[j] * kRsqrt128);
+      for (int j = 0; j < 8; ++j) {
+        const uint16_t h = f32_to_f16_bits(v[j] * kRsqrt128);
+        if constexpr (COH)
+          __hip_atomic_store(o + 16 * j + sigma_inv(i), h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          o[16 * j + sigma_inv(i)] = h;
+      }
     }
   } else {
     const ProjDev &pd = p.proj[0];

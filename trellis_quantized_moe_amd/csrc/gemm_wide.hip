@@ -94,6 +94,24 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void *sbase, uint32_t
       : "memory");
 }
 
+// dma16 with device-coherent loads (sc1): never served by a stale L2 line,
+// for data another workgroup of the same launch wrote.
+__device__ __forceinline__ void dma16_coh(uint32_t voff, const void *sbase, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1 sc1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory");
+}
+
+template <bool COH>
+__device__ __forceinline__ void dma16_a(uint32_t voff, const void *sbase, uint32_t lds_base) {
+  if constexpr (COH) dma16_coh(voff, sbase, lds_base);
+  else dma16(voff, sbase, lds_base);
+}
+
 // dma16 with only the lanes in `lanes` active. The exec mask is narrowed and
 // restored inside one asm block, so the caller's code stays one basic block
 // (a branch would split the scheduling units of the pipelined loop).
@@ -141,7 +159,7 @@ struct WideArgs {
 typedef u32x4 BRegs[4];
 
 // Per-stage context of one wave.
-template <int EPI, int K, int MS>
+template <int EPI, int K, int MS, bool COH>
 struct WideIter {
   using L = WideLds<EPI>;
   static constexpr int ND = HalfGeom<K>::kLoadDw, NN = HalfGeom<K>::kNormDw;
@@ -199,7 +217,7 @@ struct WideIter {
   __device__ __forceinline__ void dma(int d, int ka, int kt, int sa, int st) const {
     if (d < L::kAChunks) {
       const char *ab = uniform_ptr(c.abase + (size_t)ka * kArow);
-      dma16(c.avoff[d], ab, uniform_u32(c.lds0 + c.adst[d] + sa * L::kAStage));
+      dma16_a<COH>(c.avoff[d], ab, uniform_u32(c.lds0 + c.adst[d] + sa * L::kAStage));
     } else {
       const int td = d - L::kAChunks;
       const char *tb = uniform_ptr(tens + (size_t)kt * 2 * 32 * K);
@@ -314,7 +332,7 @@ struct WideIter {
 
 // A wave with no work for this stage still copies its share of A and takes
 // part in the barrier cadence of its workgroup (1 + nks barriers).
-template <int EPI>
+template <int EPI, bool COH>
 __device__ __forceinline__ void wide_idle_stage(const WideArgs &c) {
   using L = WideLds<EPI>;
   const int nks = c.nks, last = nks - 1;
@@ -322,7 +340,7 @@ __device__ __forceinline__ void wide_idle_stage(const WideArgs &c) {
     const char *ab = uniform_ptr(c.abase + (size_t)ka * kArow);
 #pragma unroll
     for (int ch = 0; ch < L::kAChunks; ++ch)
-      dma16(c.avoff[ch], ab, uniform_u32(c.lds0 + c.adst[ch] + sa * L::kAStage));
+      dma16_a<COH>(c.avoff[ch], ab, uniform_u32(c.lds0 + c.adst[ch] + sa * L::kAStage));
   };
   __syncthreads();
   issue(0, 0);
@@ -337,30 +355,35 @@ __device__ __forceinline__ void wide_idle_stage(const WideArgs &c) {
   wait_vmcnt<0>();
 }
 
-template <int EPI, int K>
+template <int EPI, int K, bool COH>
 __device__ __forceinline__ void wide_stage_rows(const WideArgs &c, char *smem, const char *tens,
                                                 int nt0, int ktiles, int msub,
                                                 f32x4 (&pacc)[8][4]) {
   if (msub <= 2) {
-    WideIter<EPI, K, 2> it(c, smem, tens, nt0, ktiles);
+    WideIter<EPI, K, 2, COH> it(c, smem, tens, nt0, ktiles);
     it.run(pacc);
   } else if (msub <= 4) {
-    WideIter<EPI, K, 4> it(c, smem, tens, nt0, ktiles);
+    WideIter<EPI, K, 4, COH> it(c, smem, tens, nt0, ktiles);
     it.run(pacc);
   } else {
-    WideIter<EPI, K, 8> it(c, smem, tens, nt0, ktiles);
+    WideIter<EPI, K, 8, COH> it(c, smem, tens, nt0, ktiles);
     it.run(pacc);
   }
 }
 
 // One work item: rows of tile `bx` times 256-column block `by`.
-template <int EPI, bool MULTI>
-__device__ __forceinline__ void wide_item(const GemmParams &p, char *smem, int bx, int by) {
+// COH (within one launch, for the pass kernel): the down projection reads its
+// A rows with device-coherent loads, the gate/up epilogue writes a~ with
+// device-coherent stores. Returns false when the tile does not exist.
+template <int EPI, bool MULTI, bool COH = false>
+__device__ __forceinline__ bool wide_item(const GemmParams &p, char *smem, int bx, int by) {
   using L = WideLds<EPI>;
   constexpr int NPROJ = L::NPROJ;
+  constexpr bool kCohLoad = COH && EPI == EPI_DOWN;
+  constexpr bool kCohStore = COH && EPI == EPI_GATEUP;
 
   WideArgs c;
-  if (!tile_of_block(p, kWBM, bx, c.e, c.row0, c.nrows)) return;
+  if (!tile_of_block(p, kWBM, bx, c.e, c.row0, c.nrows)) return false;
   c.nb = by;
   c.lane = threadIdx.x & 63;
   c.w = wave_id();
@@ -419,16 +442,16 @@ __device__ __forceinline__ void wide_item(const GemmParams &p, char *smem, int b
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns) pacc[ms][ns] = (f32x4){0.f, 0.f, 0.f, 0.f};
     if (!active) {
-      wide_idle_stage<EPI>(c);
+      wide_idle_stage<EPI, kCohLoad>(c);
     } else {
       switch (K) {
-        case 2: wide_stage_rows<EPI, 2>(c, smem, tens, nt0, ktiles, msub, pacc); break;
-        case 3: wide_stage_rows<EPI, 3>(c, smem, tens, nt0, ktiles, msub, pacc); break;
-        case 4: wide_stage_rows<EPI, 4>(c, smem, tens, nt0, ktiles, msub, pacc); break;
-        case 5: wide_stage_rows<EPI, 5>(c, smem, tens, nt0, ktiles, msub, pacc); break;
-        case 6: wide_stage_rows<EPI, 6>(c, smem, tens, nt0, ktiles, msub, pacc); break;
-        case 7: wide_stage_rows<EPI, 7>(c, smem, tens, nt0, ktiles, msub, pacc); break;
-        default: wide_stage_rows<EPI, 8>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 2: wide_stage_rows<EPI, 2, kCohLoad>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 3: wide_stage_rows<EPI, 3, kCohLoad>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 4: wide_stage_rows<EPI, 4, kCohLoad>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 5: wide_stage_rows<EPI, 5, kCohLoad>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 6: wide_stage_rows<EPI, 6, kCohLoad>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        case 7: wide_stage_rows<EPI, 7, kCohLoad>(c, smem, tens, nt0, ktiles, msub, pacc); break;
+        default: wide_stage_rows<EPI, 8, kCohLoad>(c, smem, tens, nt0, ktiles, msub, pacc); break;
       }
     }
     // acc = fmaf(s_t, P_t, acc) from acc = 0; a skipped stage leaves acc alone
@@ -467,9 +490,10 @@ __device__ __forceinline__ void wide_item(const GemmParams &p, char *smem, int b
           T[c.pj * (L::kHalf * L::kLd) + (16 * (ms - 4 * half) + 4 * g + r) * L::kLd + cw +
             16 * ns + n] = fin[ms][ns][r];
     __syncthreads();
-    epilogue<EPI>(p, T, L::kLd, L::kHalf * L::kLd, c.e, c.row0 + L::kHalf * half, hrows,
-                  c.colbase, nblk);
+    epilogue<EPI, kCohStore>(p, T, L::kLd, L::kHalf * L::kLd, c.e, c.row0 + L::kHalf * half,
+                             hrows, c.colbase, nblk);
   }
+  return true;
 }
 
 // One workgroup per (tile, 256-column block) on a 1-D grid of groups of 8
@@ -484,6 +508,74 @@ __global__ void __launch_bounds__(256, MULTI ? 1 : 2) gemm_wide_kernel(GemmParam
   const int id = blockIdx.x, per = 8 * nb;
   const int grp = id / per, r = id - grp * per;
   wide_item<EPI, MULTI>(p, smem, 8 * grp + (r & 7), r >> 3);
+}
+
+// One pass of the routed experts in one launch: the gate/up items (tile x
+// 128-column block of the intermediate, ids [0, g1)), then the down items
+// (tile x 256-column block of the hidden size), both in the tile-major,
+// XCD-aware order of gemm_wide_kernel. A down item needs only the a~ rows of
+// its own tile, which that tile's nb_gu gate/up items write with
+// device-coherent stores; each waits until its stores are complete and
+// counts itself in done[tile]. The down item waits for done[tile] == nb_gu
+// and reads a~ with device-coherent loads, so the down work of finished
+// tiles runs while slower tiles are still in gate/up. Workgroups are
+// dispatched in id order on every XCD and gate/up items never wait, so every
+// item a down item waits on is resident or finished and the wait ends; it
+// is bounded anyway (a timeout is counted in ctrl[2]). (Handing down work out
+// in the order tiles finish, through a claim counter, measured slower.)
+// done holds `slots` ints, zero at launch.
+template <bool MULTI>
+__global__ void __launch_bounds__(256, MULTI ? 1 : 2)
+    gemm_wide_pass_kernel(GemmParams gu, GemmParams dn, int nb_gu, int nb_dn, int g1, int slots,
+                          int32_t *done) {
+  constexpr int kBytes = WideLds<EPI_GATEUP>::kBytes > WideLds<EPI_DOWN>::kBytes
+                             ? WideLds<EPI_GATEUP>::kBytes
+                             : WideLds<EPI_DOWN>::kBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kBytes];
+  int id = blockIdx.x;
+  if (id < g1) {
+    const int per = 8 * nb_gu, grp = id / per, r = id - grp * per;
+    const int bx = 8 * grp + (r & 7);
+    if (bx >= slots || !wide_item<EPI_GATEUP, MULTI, true>(gu, smem, bx, r >> 3)) return;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's a~ stores
+    __syncthreads();                                     // ... and every wave's
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(done + bx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  id -= g1;
+  const int per = 8 * nb_dn, grp = id / per, r = id - grp * per;
+  const int bx = 8 * grp + (r & 7);
+  if (bx >= slots || bx >= uload_i32(dn.plan_ntiles)) return;
+  if (threadIdx.x == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(done + bx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nb_gu) {
+      if (++spins > (1 << 22)) {
+        atomicAdd(dn.ctrl + 2, 1);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
+    }
+  }
+  __syncthreads();
+  wide_item<EPI_DOWN, MULTI, true>(dn, smem, bx, r >> 3);
+}
+
+hipError_t launch_gemm_wide_pass(const GemmParams &gu, const GemmParams &dn, int tiles,
+                                 int slots, int nb_gu, int nb_dn, int32_t *q, hipStream_t s) {
+  if (tiles <= 0 || nb_gu <= 0 || nb_dn <= 0) return hipSuccess;
+  const bool multi = gu.proj[0].num_stages > 1 || gu.proj[1].num_stages > 1 ||
+                     dn.proj[0].num_stages > 1;
+  const int t8 = (tiles + 7) / 8 * 8;
+  const int g1 = t8 * nb_gu;
+  const dim3 grid((unsigned)(g1 + t8 * nb_dn));
+  if (multi)
+    hipLaunchKernelGGL(gemm_wide_pass_kernel<true>, grid, dim3(256), 0, s, gu, dn, nb_gu, nb_dn,
+                       g1, slots, q);
+  else
+    hipLaunchKernelGGL(gemm_wide_pass_kernel<false>, grid, dim3(256), 0, s, gu, dn, nb_gu, nb_dn,
+                       g1, slots, q);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_wide(int epi, const GemmParams &p, int tiles, int nblocks, hipStream_t s) {

@@ -153,7 +153,9 @@ MoeLayout moe_layout(int32_t rows, int32_t topk, int32_t E, int32_t H, int32_t I
   L.yacc = take(4 * (size_t)rows * H);
   // 16-row tiles: pre-rotation sums and completion counts of the GEMMs
   L.wide = P > 0 && moe_wide(P, E);
-  L.ncnt_ints = L.wide ? 0 : L.slots * (std::max(I, H) / 128);
+  // 16-row tiles: per (tile, 128-column block) completion counts; 128-row
+  // tiles: per tile, the finished gate/up items of the pass
+  L.ncnt_ints = L.wide ? L.slots : L.slots * (std::max(I, H) / 128);
   L.nacc = take(L.wide ? 0 : 4 * (size_t)C * std::max(2 * I, H));
   L.ncnt = take(4 * (size_t)L.ncnt_ints);
   L.total = o;
@@ -231,6 +233,10 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     rp.nitems = npos;
     rp.xt = at<uint16_t>(ws, L.xt);
     rp.ctrl_clear = nullptr;
+    if (wide) {  // the pass kernel's per-tile counts start at zero every pass
+      rp.zero = at<int32_t>(ws, L.ncnt);
+      rp.nzero = L.ncnt_ints;
+    }
     {
       ProfScope ps(st, EXL3_K_ROTATE);
       if (launch_rotate(rp, st) != hipSuccess) return EXL3_E_LAUNCH;
@@ -253,7 +259,7 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     g.ctrl = ctrl;
     g.nacc = at<float>(ws, L.nacc);
     g.ncnt = at<int32_t>(ws, L.ncnt);
-    {
+    if (!wide) {
       ProfScope ps(st, EXL3_K_GATEUP);
       if (launch_gemm(EPI_GATEUP, g, tiles, I / 128, st, wide) != hipSuccess) return EXL3_E_LAUNCH;
     }
@@ -274,10 +280,14 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     dn.ctrl = ctrl;
     dn.nacc = at<float>(ws, L.nacc);
     dn.ncnt = at<int32_t>(ws, L.ncnt);
-    {
+    if (wide) {
+      ProfScope ps(st, EXL3_K_EXPERTS);
+      if (launch_gemm_wide_pass(g, dn, tiles, L.slots, I / 128, (H + 255) / 256,
+                                at<int32_t>(ws, L.ncnt), st) != hipSuccess)
+        return EXL3_E_LAUNCH;
+    } else {
       ProfScope ps(st, EXL3_K_DOWN);
-      const int nbd = wide ? (H + 255) / 256 : H / 128;
-      if (launch_gemm(EPI_DOWN, dn, tiles, nbd, st, wide) != hipSuccess) return EXL3_E_LAUNCH;
+      if (launch_gemm(EPI_DOWN, dn, tiles, H / 128, st, wide) != hipSuccess) return EXL3_E_LAUNCH;
     }
 
     CombineParams cp{};

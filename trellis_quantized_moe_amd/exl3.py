@@ -69,7 +69,7 @@ _SIGS = {
                                 ctypes.POINTER(ctypes.c_float), _i32]),
 }
 KERNEL_NAMES = {1: "route_pack", 2: "rotate", 3: "gemm_gateup", 4: "gemm_down",
-                5: "combine", 6: "gemm_linear", 7: "decode_tiles"}
+                5: "combine", 6: "gemm_linear", 7: "decode_tiles", 8: "gemm_experts"}
 
 
 def lib():
