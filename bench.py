@@ -53,10 +53,10 @@ def prefill_step_flops(wl):
     return {"gemm_gateup": gu, "gemm_down": dn, "gemm_experts": gu + dn}
 
 
-def run_prefill(args, torch, exl3, synth):
-    _log("prefill: drawing inputs")
+def run_prefill(args, torch, exl3, synth, **over):
+    _log("prefill %s: drawing inputs" % (over or ""))
     t0 = time.time()
-    wl = synth.moe_workload("prefill", materialize=False)
+    wl = synth.moe_workload("prefill", materialize=False, **over)
     gate, up, down = (exl3.DeviceProj(p, "cuda", words_fn=synth.realize_words)
                       for p in (wl.gate, wl.up, wl.down))
     x, ids, w = exl3.device_inputs(wl, "cuda")
@@ -106,8 +106,8 @@ def run_prefill(args, torch, exl3, synth):
     return wl, res
 
 
-def run_decode(args, torch, exl3, synth, M, groups=16):
-    wl = synth.moe_workload("decode", rows=M)
+def run_decode(args, torch, exl3, synth, M, groups=16, **over):
+    wl = synth.moe_workload("decode", rows=M, **over)
     gate, up, down = (exl3.DeviceProj(p, "cuda") for p in (wl.gate, wl.up, wl.down))
     x, _, _ = exl3.device_inputs(wl, "cuda")
     routings = []
@@ -235,6 +235,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode extras")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-tp", action="store_true",
+                    help="skip the 4-way tensor-parallel shard shapes (intermediate / 4)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -264,6 +266,12 @@ def main():
         for M in (1, 32):
             _log("decode M=%d" % M)
             extra["decode_M%d" % M] = run_decode(args, torch, exl3, synth, M)
+    if not args.no_tp:
+        # one GPU's share under 4-way tensor parallelism: intermediate / 4
+        _log("tp4 shard: decode M=32, intermediate 384")
+        extra["tp4_shard_decode_M32"] = run_decode(args, torch, exl3, synth, 32, I=384)
+        _log("tp4 shard: prefill, intermediate 512")
+        extra["tp4_shard_prefill"] = run_prefill(args, torch, exl3, synth, I=512)[1]
 
     dom = pre["dominant"]
     # HBM bytes per launch of the dominant kernel from the committed rocprofv3

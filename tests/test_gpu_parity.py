@@ -386,6 +386,49 @@ def test_prefill_workload_full_scale():
     assert e_e2e <= TOL
 
 
+# ------------------------------------------- tensor-parallel shard shapes
+# One GPU's share of the layer under 4-way tensor parallelism: the
+# intermediate size split into 128-aligned quarters (decode 1536 / 4 = 384,
+# prefill 2048 / 4 = 512), hidden size and routing unchanged.
+def test_tp4_shard_decode_sampled():
+    _say("tp4 shard decode M=32, I=384")
+    wl = synth.moe_workload("decode", rows=32, I=384)
+    assert _sampled_parity(wl, [0, 31], 32 * 8) <= TOL
+
+
+def test_tp4_shard_prefill_sampled():
+    """1536 rows of the prefill layer at I = 512: 12288 pairs = 64 per expert,
+    so 128-row tiles, and capacity 2048 makes 6 passes. Checks 6 passes
+    against one pass bit for bit, and sampled rows end to end against the
+    oracle."""
+    _say("tp4 shard prefill: drawing inputs")
+    wl = synth.moe_workload("prefill", rows=1536, I=512, materialize=False)
+    P = wl.rows * wl.topk
+    lay = exl3.moe_layout(wl.rows, wl.topk, wl.num_experts, wl.hidden, wl.intermediate,
+                          wl.capacity)
+    assert lay.passes == 6
+    gate, up, down = (exl3.DeviceProj(p, DEV, words_fn=synth.realize_words)
+                      for p in (wl.gate, wl.up, wl.down))
+    x, ids, w = exl3.device_inputs(wl, DEV)
+    _say("tp4 shard prefill: 6-pass and one-pass forwards")
+    y = exl3.exl3_moe_forward(x, ids, w, gate, up, down, wl.capacity, torch.float32)
+    y1 = exl3.exl3_moe_forward(x, ids, w, gate, up, down, P, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y1.view(torch.int32))
+    sample = [0, wl.rows - 1]
+    experts = {int(wl.ids[r, j]) for r in sample for j in range(wl.topk)}
+    views = [synth.materialized_view(p, experts) for p in (wl.gate, wl.up, wl.down)]
+    ref = np.zeros((len(sample), wl.hidden))
+    for li, r in enumerate(sample):
+        for j in range(wl.topk):
+            e = int(wl.ids[r, j])
+            at_ref = omoe.stage1(wl.x[r:r + 1].astype(np.float64), e, *views, "R")
+            ref[li] += wl.weights_f64[r, j] * omoe.down_output(at_ref, e, views[2])[0]
+    err = _rel_err(y.cpu().double().numpy()[sample], ref)
+    _say("  sampled rows", sample, "err %.3e" % err)
+    assert err <= TOL
+
+
 # ------------------------------------- graph capture and cartridge swapping
 def test_additive_graph_capture_cartridge_swap():
     """exl3_moe_additive captured once in a graph; between replays only the
