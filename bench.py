@@ -203,7 +203,8 @@ def cpu_baseline(wl, synth):
                       "token" % dt}
 
 
-KERNEL_SOURCES = ("gemm_wide.hip", "gemm_shared.hpp", "common.hpp", "kernels.hpp")
+KERNEL_SOURCES = ("gemm_wide.hip", "gemm_shared.hpp", "common.hpp", "kernels.hpp",
+                  "rotate_dev.hpp")
 
 
 def kernel_source_sha():

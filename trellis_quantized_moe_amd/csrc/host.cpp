@@ -154,8 +154,9 @@ MoeLayout moe_layout(int32_t rows, int32_t topk, int32_t E, int32_t H, int32_t I
   // 16-row tiles: pre-rotation sums and completion counts of the GEMMs
   L.wide = P > 0 && moe_wide(P, E);
   // 16-row tiles: per (tile, 128-column block) completion counts; 128-row
-  // tiles: per tile, the finished gate/up items of the pass
-  L.ncnt_ints = L.wide ? L.slots : L.slots * (std::max(I, H) / 128);
+  // tiles: two sets (alternate passes) of per-tile finished gate/up items
+  // and their total
+  L.ncnt_ints = L.wide ? 2 * (L.slots + 1) : L.slots * (std::max(I, H) / 128);
   L.nacc = take(L.wide ? 0 : 4 * (size_t)C * std::max(2 * I, H));
   L.ncnt = take(4 * (size_t)L.ncnt_ints);
   L.total = o;
@@ -212,12 +213,9 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
   int32_t *ctrl = at<int32_t>(ws, L.ctrl);
   const bool wide = L.wide;
   const int bm = wide ? kBMWide : kBM;
-  for (int pass = 0; pass < L.passes; ++pass) {
+  // rotation of the inputs of one pass
+  auto rot_params = [&](int pass) {
     const int pb = pass * L.cap;
-    const int npos = (int)std::min<int64_t>(L.cap, P - pb);
-    const int tiles = std::min(E, npos) + (npos + bm - 1) / bm;
-    const int32_t *plan = at<int32_t>(ws, L.plan) + (size_t)pass * (1 + 3 * (size_t)L.slots);
-
     RotParams rp{};
     rp.x = x;
     rp.H = H;
@@ -230,14 +228,27 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     rp.total_valid = total_valid;
     rp.pass_base = pb;
     rp.pairs = (int)P;
-    rp.nitems = npos;
+    rp.nitems = (int)std::min<int64_t>(L.cap, P - pb);
     rp.xt = at<uint16_t>(ws, L.xt);
     rp.ctrl_clear = nullptr;
-    if (wide) {  // the pass kernel's per-tile counts start at zero every pass
-      rp.zero = at<int32_t>(ws, L.ncnt);
-      rp.nzero = L.ncnt_ints;
-    }
-    {
+    return rp;
+  };
+  // 128-row tiles: two sets of pass-kernel counts (slots + 1 ints each), the
+  // set of pass p + 1 zeroed by the rotation items of pass p's kernel
+  const int nq = L.slots + 1;
+  auto qset = [&](int pass) { return at<int32_t>(ws, L.ncnt) + (size_t)(pass & 1) * nq; };
+  for (int pass = 0; pass < L.passes; ++pass) {
+    const int pb = pass * L.cap;
+    const int npos = (int)std::min<int64_t>(L.cap, P - pb);
+    const int tiles = std::min(E, npos) + (npos + bm - 1) / bm;
+    const int32_t *plan = at<int32_t>(ws, L.plan) + (size_t)pass * (1 + 3 * (size_t)L.slots);
+
+    if (!wide || pass == 0) {  // later passes of 128-row tiles: rotated by the previous launch
+      RotParams rp = rot_params(pass);
+      if (wide) {
+        rp.zero = qset(0);
+        rp.nzero = nq;
+      }
       ProfScope ps(st, EXL3_K_ROTATE);
       if (launch_rotate(rp, st) != hipSuccess) return EXL3_E_LAUNCH;
     }
@@ -281,9 +292,15 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     dn.nacc = at<float>(ws, L.nacc);
     dn.ncnt = at<int32_t>(ws, L.ncnt);
     if (wide) {
+      RotParams rn{};
+      if (pass + 1 < L.passes) {
+        rn = rot_params(pass + 1);
+        rn.zero = qset(pass + 1);
+        rn.nzero = nq;
+      }
       ProfScope ps(st, EXL3_K_EXPERTS);
-      if (launch_gemm_wide_pass(g, dn, tiles, L.slots, I / 128, (H + 255) / 256,
-                                at<int32_t>(ws, L.ncnt), st) != hipSuccess)
+      if (launch_gemm_wide_pass(g, dn, rn, tiles, L.slots, I / 128, (H + 255) / 256, qset(pass),
+                                st) != hipSuccess)
         return EXL3_E_LAUNCH;
     } else {
       ProfScope ps(st, EXL3_K_DOWN);

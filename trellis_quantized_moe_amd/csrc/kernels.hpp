@@ -100,10 +100,13 @@ hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks,
 hipError_t launch_gemm_wide(int epi, const GemmParams &p, int tiles, int nblocks,
                             hipStream_t s);
 // One pass of 128-row routed experts: gate/up and down in one launch, a
-// tile's down work starting once its own gate/up items are done. `q` holds
-// `slots` ints, zero at launch (slots >= plan tiles of the pass).
-hipError_t launch_gemm_wide_pass(const GemmParams &gu, const GemmParams &dn, int tiles,
-                                 int slots, int nb_gu, int nb_dn, int32_t *q, hipStream_t s);
+// tile's down work starting once its own gate/up items are done, then the
+// input rotation of the next pass (rn; rn.nitems == 0: none), which also
+// zeroes rn.zero. `q` holds slots + 1 ints, zero at launch (slots >= plan
+// tiles of the pass).
+hipError_t launch_gemm_wide_pass(const GemmParams &gu, const GemmParams &dn, const RotParams &rn,
+                                 int tiles, int slots, int nb_gu, int nb_dn, int32_t *q,
+                                 hipStream_t s);
 hipError_t launch_rotate(const RotParams &p, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int npos, hipStream_t s);
 hipError_t launch_combine_rows(const CombineParams &p, hipStream_t s);

@@ -1,0 +1,67 @@
+// Input rotation of one (item, 128-block) by one 16-lane group, shared by the
+// rotate kernel and the per-pass expert kernel (which rotates the next pass's
+// inputs while its own down work finishes).
+// x~ = fp16_rne(H128(x * suh) / sqrt(128)) for the GEMM A operands, stored in
+// the kSigma k-order the decoded B operands use. exllamav3 PR #284 "MoE: Add
+// fused additive EXL3 kernels" (API contract: each projection's suh/svh
+// rotations, reused by residual stages) and TensorFold PR #837 (What this
+// changes: the input rotation, each expert's rotation for gate and up).
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace exl3 {
+
+// Unit gid = item * (H / 128) + block. Lane i (0..15 of the group) loads
+// entries 8i..8i+7 (16 bytes) of the x block once, transforms it for every
+// projection, and stores each result as one 16-byte run in the kSigma order:
+// slots 0..7 of its half-group hold entries {0,4,1,5,2,6,3,7} of the lane's
+// 8. Every lane of the group must call this with the same gid.
+__device__ __forceinline__ void rotate_unit(const RotParams &p, int64_t gid, int i) {
+  const int nblk = p.H >> 7;
+  if (gid >= (int64_t)p.nitems * nblk) return;
+  const int item = (int)(gid / nblk);
+  const int blk = (int)(gid - (int64_t)item * nblk);
+
+  int row, e;
+  if (p.pair_of_pos != nullptr) {
+    const int pos = p.pass_base + item;
+    if (pos >= min(*p.total_valid, p.pairs)) return;  // uniform per group
+    const int q = p.pair_of_pos[pos];
+    if (q < 0 || q >= p.pairs) return;  // inconsistent metadata: drop
+    row = q / p.topk;
+    e = p.expert_of_pos[pos];
+  } else {
+    row = item;
+    e = 0;
+  }
+  const int64_t col = blk * 128 + 8 * i;
+  const u32x4 xv = *(const u32x4 *)(p.x + (int64_t)row * p.H + col);
+  u32x4 sv[2];
+#pragma unroll
+  for (int pj = 0; pj < 2; ++pj)
+    if (pj < p.nproj) sv[pj] = *(const u32x4 *)(p.suh[pj] + (int64_t)e * p.H + col);
+#pragma unroll
+  for (int pj = 0; pj < 2; ++pj) {
+    if (pj >= p.nproj) break;
+    // halves are unpacked with shifts: this compiler mis-compiles a bit_cast
+    // of a vector element taken inside an unrolled loop (it reuses element 0)
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t xw = xv[j], sw = sv[pj][j];
+      v[2 * j] = f16_bits_to_f32((uint16_t)(xw & 0xFFFFu)) * f16_bits_to_f32((uint16_t)(sw & 0xFFFFu));
+      v[2 * j + 1] = f16_bits_to_f32((uint16_t)(xw >> 16)) * f16_bits_to_f32((uint16_t)(sw >> 16));
+    }
+    fwht128_lane8(v);
+    uint16_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = f32_to_f16_bits(v[j] * kRsqrt128);
+    const u32x4 o = {(uint32_t)h[0] | ((uint32_t)h[4] << 16), (uint32_t)h[1] | ((uint32_t)h[5] << 16),
+                     (uint32_t)h[2] | ((uint32_t)h[6] << 16), (uint32_t)h[3] | ((uint32_t)h[7] << 16)};
+    *(u32x4 *)(p.xt + ((int64_t)item * p.nproj + pj) * p.H + col) = o;
+  }
+}
+
+}  // namespace exl3

@@ -242,8 +242,13 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
   }
 
   // a4: per pass (one wave each), the row tiles of every expert's sub-span
-  // inside the pass, in expert order; only the experts overlapping the pass
-  // are visited
+  // inside the pass; only the experts overlapping the pass are visited.
+  // Order: full tiles (bm rows) first, in expert order, then the partial
+  // tiles (at most one per expert: the end of its span); for 128-row tiles
+  // and at most 128 experts in the pass those go by rows descending, ties in
+  // expert order, otherwise in expert order. Heavy tiles so come first in dispatch order,
+  // where each gets a CU of its own before the light ones fill the second
+  // slots; the order never changes a result.
   for (int pass = w; pass < p.passes; pass += kPackWaves) {
     const int pb = pass * p.capacity;
     const int pe = (int)min((int64_t)pb + p.capacity, (int64_t)kept);
@@ -251,29 +256,71 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
     int total = 0;
     if (pb < pe) {
       const int e_lo = expert_at(s_off, E, pb), e_hi = expert_at(s_off, E, pe - 1);
-      for (int eb = e_lo; eb <= e_hi; eb += 64) {
+      const int bm = p.bm;
+      auto span = [&](int e, int &lo, int &hi) {
+        lo = max(s_off[e], pb);
+        hi = min(s_off[e + 1], pe);
+      };
+      for (int eb = e_lo; eb <= e_hi; eb += 64) {  // full tiles
         const int e = eb + lane;
-        int lo = 0, hi = 0, nt = 0;
+        int lo = 0, hi = 0, nf = 0;
         if (e <= e_hi) {
-          lo = max(s_off[e], pb);
-          hi = min(s_off[e + 1], pe);
-          nt = hi > lo ? (hi - lo + p.bm - 1) / p.bm : 0;
+          span(e, lo, hi);
+          nf = hi > lo ? (hi - lo) / bm : 0;
         }
-        int x = nt;  // inclusive scan over the wave
+        int x = nf;  // inclusive scan over the wave
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
           const int y = __shfl_up(x, d, 64);
           if (lane >= d) x += y;
         }
-        const int slot0 = total + x - nt;
-        for (int t = 0; t < nt; ++t) {
+        const int slot0 = total + x - nf;
+        for (int t = 0; t < nf; ++t) {
           int32_t *d = plan + 1 + 3 * (slot0 + t);
           d[0] = e;
-          d[1] = lo - pb + t * p.bm;
-          d[2] = min(p.bm, hi - lo - t * p.bm);
+          d[1] = lo - pb + t * bm;
+          d[2] = bm;
         }
         total += __shfl(x, 63, 64);
       }
+      // partial rows of the experts e_lo + lane and e_lo + 64 + lane
+      int prow[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int e = e_lo + 64 * c + lane;
+        int lo = 0, hi = 0;
+        if (e <= e_hi) span(e, lo, hi);
+        prow[c] = hi > lo ? (hi - lo) % bm : 0;
+      }
+      const bool sort = bm == kBMWide && e_hi - e_lo < 128;
+      const int nfull = total;
+      int npart = 0;
+      for (int eb = e_lo; eb <= e_hi; eb += 64) {  // partial tiles
+        const int e = eb + lane, c = (eb - e_lo) >> 6;
+        int lo = 0, hi = 0;
+        if (e <= e_hi) span(e, lo, hi);
+        const int rows = (c < 2) ? prow[c & 1] : (hi > lo ? (hi - lo) % bm : 0);
+        const uint64_t has = __ballot(rows > 0);
+        int rank = npart + __popcll(has & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+        if (sort) {  // rows descending, then expert order, over both chunks
+          rank = 0;
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2)
+            for (int l = 0; l < 64; ++l) {
+              const int r2 = __shfl(prow[c2], l, 64);
+              const int e2 = e_lo + 64 * c2 + l;
+              rank += (r2 > rows || (r2 == rows && e2 < e)) ? 1 : 0;
+            }
+        }
+        if (rows > 0) {
+          int32_t *d = plan + 1 + 3 * (nfull + rank);
+          d[0] = e;
+          d[1] = lo - pb + (hi - lo) / bm * bm;
+          d[2] = rows;
+        }
+        npart += __popcll(has);
+      }
+      total = nfull + npart;
     }
     if (lane == 0) plan[0] = total;
   }
