@@ -197,6 +197,39 @@ __device__ __forceinline__ uint32_t half_reg(const uint32_t (&N)[NN], uint32_t m
   return codebook2(column_pair<K, r>(N), mask);
 }
 
+// K = 4 and K = 8: the first state of every half column starts at the same
+// bit of the half column's first loaded dword (20 for K = 4, 24 for K = 8:
+// 16nK + 8hK + K - 16 is 20 resp. 24 mod 32 for every column n and half h),
+// so the state pairs are cut straight from the loaded dwords with
+// compile-time shifts and byte selectors, with no per-lane normalisation.
+template <int K>
+constexpr bool kRawPairs = (K == 4 || K == 8);
+
+// Register r (0..3) of a decoded half column from its loaded dwords (K = 4
+// or 8): states (r, r + 4), as half_reg.
+template <int K, int r, int ND>
+__device__ __forceinline__ uint32_t half_reg_raw(const uint32_t (&raw)[ND], uint32_t mask) {
+  static_assert(kRawPairs<K>, "constant window start only for K = 4, 8");
+  uint32_t pair;
+  if constexpr (K == 4) {
+    // states r, r + 4 = the 32 bits from bit 20 + 4r
+    constexpr int o = 20 + 4 * r, w = o >> 5, sh = o & 31;
+    if constexpr (sh == 0) pair = raw[w];
+    else pair = __builtin_amdgcn_alignbit(raw[w + 1], raw[w], sh);
+  } else {
+    // state r = bytes 3 + r, 4 + r; state r + 4 = bytes 7 + r, 8 + r
+    if constexpr (r == 0) {
+      const uint32_t t = __builtin_amdgcn_perm(raw[1], raw[0], 0x07070403u);  // b3 b4 b7 b7
+      pair = __builtin_amdgcn_perm(raw[2], t, 0x04020100u);                      // b8 in byte 3
+    } else {
+      constexpr uint32_t a = r - 1;  // bytes 4 + r.. of raw[1] are bytes a.. of it
+      constexpr uint32_t sel = a | ((a + 1) << 8) | ((a + 4) << 16) | ((a + 5) << 24);
+      pair = __builtin_amdgcn_perm(raw[2], raw[1], sel);
+    }
+  }
+  return codebook2(pair, mask);
+}
+
 // Decode one tile column (16 states) from its raw dwords into 8 packed fp16
 // pairs (register order as in column_reg).
 template <int K>

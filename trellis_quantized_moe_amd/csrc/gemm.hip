@@ -173,9 +173,15 @@ struct StreamChain {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint32_t N[NN];
-      normalize(raw[s], shift, N);
-      const u32x4 w = {half_reg<K, 0>(N, mask), half_reg<K, 1>(N, mask),
-                       half_reg<K, 2>(N, mask), half_reg<K, 3>(N, mask)};
+      u32x4 w;
+      if constexpr (kRawPairs<K>) {
+        w = (u32x4){half_reg_raw<K, 0>(raw[s], mask), half_reg_raw<K, 1>(raw[s], mask),
+                    half_reg_raw<K, 2>(raw[s], mask), half_reg_raw<K, 3>(raw[s], mask)};
+      } else {
+        normalize(raw[s], shift, N);
+        w = (u32x4){half_reg<K, 0>(N, mask), half_reg<K, 1>(N, mask), half_reg<K, 2>(N, mask),
+                    half_reg<K, 3>(N, mask)};
+      }
       acc = mfma16x16x32(__builtin_bit_cast(f16x8, a[aslot][s]), __builtin_bit_cast(f16x8, w), acc);
     }
   }

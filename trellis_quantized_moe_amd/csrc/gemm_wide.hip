@@ -240,8 +240,12 @@ struct WideIter {
   template <int Q>
   __device__ __forceinline__ void decode_pair(BRegs &bn) {
     constexpr int ns = Q / 4, r = Q % 4;
-    if constexpr (r == 0) normalize(raw[ns], shift, N);
-    bn[ns][r] = half_reg<K, r>(N, mask);
+    if constexpr (kRawPairs<K>) {
+      bn[ns][r] = half_reg_raw<K, r>(raw[ns], mask);
+    } else {
+      if constexpr (r == 0) normalize(raw[ns], shift, N);
+      bn[ns][r] = half_reg<K, r>(N, mask);
+    }
   }
   template <int... Qs>
   __device__ __forceinline__ void decode_seq(BRegs &bn, std::integer_sequence<int, Qs...>) {
