@@ -46,6 +46,7 @@
 
 #include "gemm_shared.hpp"
 #include "rotate_dev.hpp"
+#include "combine_dev.hpp"
 
 namespace exl3 {
 
@@ -515,97 +516,141 @@ __global__ void __launch_bounds__(256, MULTI ? 1 : 2) gemm_wide_kernel(GemmParam
   wide_item<EPI, MULTI>(p, smem, 8 * grp + (r & 7), r >> 3);
 }
 
-// One pass of the routed experts in one launch, and the input rotation of
-// the next pass. Items, in dispatch order:
-//  - gate/up (tile x 128-column block of the intermediate, ids [0, g1)),
-//  - down (tile x 256-column block of the hidden size, the next g2 ids, tiles
-//    in reverse order),
-//  - rotation of the next pass (16 (item, 128-block) units each, the rest),
-// with tiles in the tile-major, XCD-aware order of gemm_wide_kernel.
-// A down item needs only the a~ rows of its own tile, which that tile's nb_gu
-// gate/up items write with device-coherent stores; each waits until its
-// stores are complete and counts itself in q[tile] and in q[slots]. The down
-// item waits for q[tile] == nb_gu and reads a~ with device-coherent loads,
-// so the down work of finished tiles runs while slower tiles are still in
-// gate/up. The next pass's rotation overwrites x~, which only gate/up items
-// read: its items wait until q[slots] counts every gate/up item of the pass,
-// then also zero the next pass's counts (qn = rn.zero; this launch uses q).
-// Workgroups are dispatched in id order on every XCD and an item waits only
-// for items before it, which never wait for later ones, so every wait ends;
-// it is bounded anyway (a timeout is counted in ctrl[2]). (Handing down work
-// out in the order tiles finish, through a claim counter, measured slower.)
-// q holds slots + 1 ints, zero at launch.
+// One pass of the routed experts in one launch (calls with a single pass;
+// several passes run pipelined, gemm_wide_pipe_kernel). Items, in dispatch
+// order: gate/up (tile x 128-column block of the intermediate, ids [0, g1)),
+// then down (tile x 256-column block of the hidden size, tiles in reverse
+// plan order), in the XCD-aware order of gemm_wide_kernel. A down item needs
+// only the a~ rows of its own tile, which that tile's nb_gu gate/up items
+// write with device-coherent stores; each waits until its stores are
+// complete and counts itself in q[tile]. The down item waits for q[tile] ==
+// nb_gu and reads a~ with device-coherent loads, so the down work of finished
+// tiles runs while slower tiles are still in gate/up. The plan puts heavy
+// tiles first, so the first down items dispatched belong to tiles that finish
+// early. Workgroups are dispatched in id order on every XCD and gate/up items
+// never wait, so every item a down item waits on is resident or finished and
+// the wait ends; it is bounded anyway (a timeout is counted in ctrl[2]).
+// (Handing down work out in the order tiles finish, through a claim counter,
+// measured slower.) q holds `slots` ints, zero at launch.
 template <bool MULTI>
 __global__ void __launch_bounds__(256, MULTI ? 1 : 2)
-    gemm_wide_pass_kernel(GemmParams gu, GemmParams dn, RotParams rn, int nb_gu, int nb_dn,
-                          int g1, int g2, int slots, int32_t *q) {
+    gemm_wide_pass_kernel(GemmParams gu, GemmParams dn, int nb_gu, int nb_dn, int g1, int slots,
+                          int32_t *q) {
   constexpr int kBytes = WideLds<EPI_GATEUP>::kBytes > WideLds<EPI_DOWN>::kBytes
                              ? WideLds<EPI_GATEUP>::kBytes
                              : WideLds<EPI_DOWN>::kBytes;
   __shared__ __attribute__((aligned(16))) char smem[kBytes];
   int id = blockIdx.x;
-  auto wait_for = [&](const int32_t *cnt, int need) {
-    if (threadIdx.x == 0) {
-      int spins = 0;
-      while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-        if (++spins > (1 << 22)) {
-          atomicAdd(dn.ctrl + 2, 1);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(4);
-      }
-    }
-    __syncthreads();
-  };
   if (id < g1) {
     const int per = 8 * nb_gu, grp = id / per, r = id - grp * per;
     const int bx = 8 * grp + (r & 7);
     if (bx >= slots || !wide_item<EPI_GATEUP, MULTI, true>(gu, smem, bx, r >> 3)) return;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's a~ stores
     __syncthreads();                                     // ... and every wave's
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0)
       __hip_atomic_fetch_add(q + bx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(q + slots, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  id -= g1;
+  const int per = 8 * nb_dn, grp = id / per, r = id - grp * per;
+  const int ntiles = min(uload_i32(dn.plan_ntiles), slots);
+  const int bx = ntiles - 1 - (8 * grp + (r & 7));
+  if (bx < 0) return;
+  if (threadIdx.x == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(q + bx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nb_gu) {
+      if (++spins > (1 << 22)) {
+        atomicAdd(dn.ctrl + 2, 1);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
     }
+  }
+  __syncthreads();
+  wide_item<EPI_DOWN, MULTI, true>(dn, smem, bx, r >> 3);
+}
+
+hipError_t launch_gemm_wide_pass(const GemmParams &gu, const GemmParams &dn, int tiles,
+                                 int slots, int nb_gu, int nb_dn, int32_t *q, hipStream_t s) {
+  if (tiles <= 0 || nb_gu <= 0 || nb_dn <= 0) return hipSuccess;
+  const bool multi = gu.proj[0].num_stages > 1 || gu.proj[1].num_stages > 1 ||
+                     dn.proj[0].num_stages > 1;
+  const int t8 = (tiles + 7) / 8 * 8;
+  const int g1 = t8 * nb_gu;
+  const dim3 grid((unsigned)(g1 + t8 * nb_dn));
+  if (multi)
+    hipLaunchKernelGGL(gemm_wide_pass_kernel<true>, grid, dim3(256), 0, s, gu, dn, nb_gu, nb_dn,
+                       g1, slots, q);
+  else
+    hipLaunchKernelGGL(gemm_wide_pass_kernel<false>, grid, dim3(256), 0, s, gu, dn, nb_gu, nb_dn,
+                       g1, slots, q);
+  return hipGetLastError();
+}
+
+// Routed experts over several passes, software-pipelined across launches:
+// launch k holds the gate/up items of pass k, the down items of pass k - 1,
+// the rotation of pass k + 1 and the combine of pass k - 2. x~, a~ and d have
+// two buffers each (by pass parity), so within one launch no item reads what
+// another writes (gate/up reads x~[k] and writes a~[k]; down reads a~[k-1]
+// and writes d[k-1]; the rotation writes x~[k+1]; the combine reads d[k-2] =
+// d[k]), and every value an item reads was written by an earlier launch. No
+// item waits for another: the launch fills the machine with whatever work is
+// left of four passes, instead of idling through one pass's stragglers.
+// Items, in dispatch order (longest first): gate/up (tile x 128-column
+// block, heavy tiles first), down (tile x 256-column block), rotation
+// (kRotPerItem x 16 (position, 128-block) units), combine (one position).
+constexpr int kRotPerItem = 4;
+
+template <bool MULTI>
+__global__ void __launch_bounds__(256, MULTI ? 1 : 2)
+    gemm_wide_pipe_kernel(GemmParams gu, GemmParams dn, RotParams rn, CombineParams cb,
+                          int nb_gu, int nb_dn, int g1, int g2, int g3) {
+  constexpr int kBytes = WideLds<EPI_GATEUP>::kBytes > WideLds<EPI_DOWN>::kBytes
+                             ? WideLds<EPI_GATEUP>::kBytes
+                             : WideLds<EPI_DOWN>::kBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kBytes];
+  int id = blockIdx.x;
+  if (id < g1) {
+    const int per = 8 * nb_gu, grp = id / per, r = id - grp * per;
+    wide_item<EPI_GATEUP, MULTI>(gu, smem, 8 * grp + (r & 7), r >> 3);
     return;
   }
   id -= g1;
   if (id < g2) {
-    // tiles in reverse plan order: the plan puts heavy tiles first, so the
-    // first down items dispatched belong to tiles that finish gate/up early
     const int per = 8 * nb_dn, grp = id / per, r = id - grp * per;
-    const int ntiles = min(uload_i32(dn.plan_ntiles), slots);
-    const int bx = ntiles - 1 - (8 * grp + (r & 7));
-    if (bx < 0) return;
-    wait_for(q + bx, nb_gu);
-    wide_item<EPI_DOWN, MULTI, true>(dn, smem, bx, r >> 3);
+    wide_item<EPI_DOWN, MULTI>(dn, smem, 8 * grp + (r & 7), r >> 3);
     return;
   }
   id -= g2;
-  wait_for(q + slots, min(uload_i32(gu.plan_ntiles), slots) * nb_gu);
-  const int nrot = (int)gridDim.x - g1 - g2;
-  for (int i = id * 256 + (int)threadIdx.x; i < rn.nzero; i += nrot * 256) rn.zero[i] = 0;
-  rotate_unit(rn, (int64_t)id * 16 + (threadIdx.x >> 4), threadIdx.x & 15);
+  if (id < g3) {
+#pragma unroll 1
+    for (int u = 0; u < kRotPerItem; ++u)
+      rotate_unit(rn, ((int64_t)id * kRotPerItem + u) * 16 + (threadIdx.x >> 4), threadIdx.x & 15);
+    return;
+  }
+  combine_position(cb, id - g3);
 }
 
-hipError_t launch_gemm_wide_pass(const GemmParams &gu, const GemmParams &dn, const RotParams &rn,
-                                 int tiles, int slots, int nb_gu, int nb_dn, int32_t *q,
-                                 hipStream_t s) {
-  if (tiles <= 0 || nb_gu <= 0 || nb_dn <= 0) return hipSuccess;
+hipError_t launch_gemm_wide_pipe(const GemmParams &gu, int tiles_gu, const GemmParams &dn,
+                                 int tiles_dn, const RotParams &rn, const CombineParams &cb,
+                                 int npos_cb, int nb_gu, int nb_dn, hipStream_t s) {
   if (rn.nitems > 0 && (rn.nproj < 1 || rn.nproj > 2)) return hipErrorInvalidValue;
-  const bool multi = gu.proj[0].num_stages > 1 || gu.proj[1].num_stages > 1 ||
-                     dn.proj[0].num_stages > 1;
-  const int t8 = (tiles + 7) / 8 * 8;
-  const int g1 = t8 * nb_gu, g2 = t8 * nb_dn;
-  const int64_t units = (int64_t)rn.nitems * (rn.H >> 7);
-  const int g3 = (int)((units + 15) / 16);
-  const dim3 grid((unsigned)(g1 + g2 + g3));
+  const bool multi = (tiles_gu > 0 && (gu.proj[0].num_stages > 1 || gu.proj[1].num_stages > 1)) ||
+                     (tiles_dn > 0 && dn.proj[0].num_stages > 1);
+  const int g1 = tiles_gu > 0 ? (tiles_gu + 7) / 8 * 8 * nb_gu : 0;
+  const int g2 = tiles_dn > 0 ? (tiles_dn + 7) / 8 * 8 * nb_dn : 0;
+  const int64_t units = rn.nitems > 0 ? (int64_t)rn.nitems * (rn.H >> 7) : 0;
+  const int g3 = (int)((units + 16 * kRotPerItem - 1) / (16 * kRotPerItem));
+  const int g4 = npos_cb > 0 ? npos_cb : 0;
+  const int64_t total = (int64_t)g1 + g2 + g3 + g4;
+  if (total <= 0) return hipSuccess;
+  const dim3 grid((unsigned)total);
   if (multi)
-    hipLaunchKernelGGL(gemm_wide_pass_kernel<true>, grid, dim3(256), 0, s, gu, dn, rn, nb_gu,
-                       nb_dn, g1, g2, slots, q);
+    hipLaunchKernelGGL(gemm_wide_pipe_kernel<true>, grid, dim3(256), 0, s, gu, dn, rn, cb, nb_gu,
+                       nb_dn, g1, g2, g3);
   else
-    hipLaunchKernelGGL(gemm_wide_pass_kernel<false>, grid, dim3(256), 0, s, gu, dn, rn, nb_gu,
-                       nb_dn, g1, g2, slots, q);
+    hipLaunchKernelGGL(gemm_wide_pipe_kernel<false>, grid, dim3(256), 0, s, gu, dn, rn, cb, nb_gu,
+                       nb_dn, g1, g2, g3);
   return hipGetLastError();
 }
 

@@ -120,7 +120,8 @@ struct MoeLayout {
   size_t ctrl, count, offset, pair_of_pos, weight_of_pos, pos_of_pair, num_active, status;
   size_t expert_of_pos, plan, xt, at, d, yacc, nacc, ncnt, total;
   int passes, slots, cap, ncnt_ints;
-  bool wide;
+  bool wide, pipe;
+  size_t xt_bytes, at_bytes, d_bytes;  // one buffer each (pipe: two of each)
 };
 
 MoeLayout moe_layout(int32_t rows, int32_t topk, int32_t E, int32_t H, int32_t I,
@@ -147,16 +148,21 @@ MoeLayout moe_layout(int32_t rows, int32_t topk, int32_t E, int32_t H, int32_t I
   L.status = take(4);
   L.expert_of_pos = take(4 * (size_t)P);
   L.plan = take(4 * (size_t)L.passes * (1 + 3 * (size_t)L.slots));
-  L.xt = take(2 * (size_t)C * 2 * H);
-  L.at = take(2 * (size_t)C * I);
-  L.d = take(4 * (size_t)C * H);
-  L.yacc = take(4 * (size_t)rows * H);
-  // 16-row tiles: pre-rotation sums and completion counts of the GEMMs
   L.wide = P > 0 && moe_wide(P, E);
+  // 128-row tiles over several passes run pipelined across launches, with
+  // two buffers (by pass parity) of x~, a~ and d
+  L.pipe = L.wide && L.passes >= 2;
+  const size_t nbuf = L.pipe ? 2 : 1;
+  L.xt_bytes = align_up(2 * (size_t)C * 2 * H);
+  L.at_bytes = align_up(2 * (size_t)C * I);
+  L.d_bytes = align_up(4 * (size_t)C * H);
+  L.xt = take(nbuf * L.xt_bytes);
+  L.at = take(nbuf * L.at_bytes);
+  L.d = take(nbuf * L.d_bytes);
+  L.yacc = take(4 * (size_t)rows * H);
   // 16-row tiles: per (tile, 128-column block) completion counts; 128-row
-  // tiles: two sets (alternate passes) of per-tile finished gate/up items
-  // and their total
-  L.ncnt_ints = L.wide ? 2 * (L.slots + 1) : L.slots * (std::max(I, H) / 128);
+  // tiles in one pass: per tile, the finished gate/up items
+  L.ncnt_ints = L.pipe ? 0 : L.wide ? L.slots : L.slots * (std::max(I, H) / 128);
   L.nacc = take(L.wide ? 0 : 4 * (size_t)C * std::max(2 * I, H));
   L.ncnt = take(4 * (size_t)L.ncnt_ints);
   L.total = o;
@@ -213,9 +219,21 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
   int32_t *ctrl = at<int32_t>(ws, L.ctrl);
   const bool wide = L.wide;
   const int bm = wide ? kBMWide : kBM;
-  // rotation of the inputs of one pass
-  auto rot_params = [&](int pass) {
-    const int pb = pass * L.cap;
+  auto npos_of = [&](int pass) { return (int)std::min<int64_t>(L.cap, P - (int64_t)pass * L.cap); };
+  auto tiles_of = [&](int pass) {
+    const int npos = npos_of(pass);
+    return std::min(E, npos) + (npos + bm - 1) / bm;
+  };
+  auto plan_of = [&](int pass) {
+    return at<int32_t>(ws, L.plan) + (size_t)pass * (1 + 3 * (size_t)L.slots);
+  };
+  uint16_t *xt0 = at<uint16_t>(ws, L.xt), *at0 = at<uint16_t>(ws, L.at);
+  float *d0 = at<float>(ws, L.d);
+  auto xt_buf = [&](int b) { return (uint16_t *)((char *)xt0 + (size_t)b * L.xt_bytes); };
+  auto at_buf = [&](int b) { return (uint16_t *)((char *)at0 + (size_t)b * L.at_bytes); };
+  auto d_buf = [&](int b) { return (float *)((char *)d0 + (size_t)b * L.d_bytes); };
+  // rotation of the inputs of one pass into x~ buffer b
+  auto rot_params = [&](int pass, int b) {
     RotParams rp{};
     rp.x = x;
     rp.H = H;
@@ -226,87 +244,58 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     rp.pair_of_pos = pair_of_pos;
     rp.expert_of_pos = at<int32_t>(ws, L.expert_of_pos);
     rp.total_valid = total_valid;
-    rp.pass_base = pb;
+    rp.pass_base = pass * L.cap;
     rp.pairs = (int)P;
-    rp.nitems = (int)std::min<int64_t>(L.cap, P - pb);
-    rp.xt = at<uint16_t>(ws, L.xt);
+    rp.nitems = npos_of(pass);
+    rp.xt = xt_buf(b);
     rp.ctrl_clear = nullptr;
     return rp;
   };
-  // 128-row tiles: two sets of pass-kernel counts (slots + 1 ints each), the
-  // set of pass p + 1 zeroed by the rotation items of pass p's kernel
-  const int nq = L.slots + 1;
-  auto qset = [&](int pass) { return at<int32_t>(ws, L.ncnt) + (size_t)(pass & 1) * nq; };
-  for (int pass = 0; pass < L.passes; ++pass) {
-    const int pb = pass * L.cap;
-    const int npos = (int)std::min<int64_t>(L.cap, P - pb);
-    const int tiles = std::min(E, npos) + (npos + bm - 1) / bm;
-    const int32_t *plan = at<int32_t>(ws, L.plan) + (size_t)pass * (1 + 3 * (size_t)L.slots);
-
-    if (!wide || pass == 0) {  // later passes of 128-row tiles: rotated by the previous launch
-      RotParams rp = rot_params(pass);
-      if (wide) {
-        rp.zero = qset(0);
-        rp.nzero = nq;
-      }
-      ProfScope ps(st, EXL3_K_ROTATE);
-      if (launch_rotate(rp, st) != hipSuccess) return EXL3_E_LAUNCH;
-    }
-
+  // gate/up of one pass: x~ buffer b in, a~ buffer b out
+  auto gu_params = [&](int pass, int b) {
+    const int32_t *plan = plan_of(pass);
     GemmParams g{};
     g.proj[0] = to_dev(gate);
     g.proj[1] = to_dev(up);
     g.E = E;
     g.in_f = H;
     g.out_f = I;
-    g.A = at<uint16_t>(ws, L.xt);
+    g.A = xt_buf(b);
     g.lda = 2 * (int64_t)H;
     g.a_proj_stride = H;
     g.plan_ntiles = plan;
     g.plan_tiles = plan + 1;
     g.suh_down = down->suh;
-    g.out_h = at<uint16_t>(ws, L.at);
+    g.out_h = at_buf(b);
     g.ldo = I;
     g.ctrl = ctrl;
     g.nacc = at<float>(ws, L.nacc);
     g.ncnt = at<int32_t>(ws, L.ncnt);
-    if (!wide) {
-      ProfScope ps(st, EXL3_K_GATEUP);
-      if (launch_gemm(EPI_GATEUP, g, tiles, I / 128, st, wide) != hipSuccess) return EXL3_E_LAUNCH;
-    }
-
+    return g;
+  };
+  // down of one pass: a~ buffer b in, d buffer b out
+  auto dn_params = [&](int pass, int b) {
+    const int32_t *plan = plan_of(pass);
     GemmParams dn{};
     dn.proj[0] = to_dev(down);
     dn.E = E;
     dn.in_f = I;
     dn.out_f = H;
-    dn.A = at<uint16_t>(ws, L.at);
+    dn.A = at_buf(b);
     dn.lda = I;
     dn.plan_ntiles = plan;
     dn.plan_tiles = plan + 1;
-    dn.out_f32 = at<float>(ws, L.d);
+    dn.out_f32 = d_buf(b);
     dn.ldo = H;
     dn.weight_of_pos = weight_of_pos;
-    dn.pass_base = pb;
+    dn.pass_base = pass * L.cap;
     dn.ctrl = ctrl;
     dn.nacc = at<float>(ws, L.nacc);
     dn.ncnt = at<int32_t>(ws, L.ncnt);
-    if (wide) {
-      RotParams rn{};
-      if (pass + 1 < L.passes) {
-        rn = rot_params(pass + 1);
-        rn.zero = qset(pass + 1);
-        rn.nzero = nq;
-      }
-      ProfScope ps(st, EXL3_K_EXPERTS);
-      if (launch_gemm_wide_pass(g, dn, rn, tiles, L.slots, I / 128, (H + 255) / 256, qset(pass),
-                                st) != hipSuccess)
-        return EXL3_E_LAUNCH;
-    } else {
-      ProfScope ps(st, EXL3_K_DOWN);
-      if (launch_gemm(EPI_DOWN, dn, tiles, H / 128, st, wide) != hipSuccess) return EXL3_E_LAUNCH;
-    }
-
+    return dn;
+  };
+  // combine of one pass: d buffer b in
+  auto cb_params = [&](int pass, int b) {
     CombineParams cp{};
     cp.rows = rows;
     cp.topk = topk;
@@ -315,12 +304,67 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     cp.pair_of_pos = pair_of_pos;
     cp.pos_of_pair = pos_of_pair;
     cp.total_valid = total_valid;
-    cp.pass_base = pb;
-    cp.pass_end = pb + L.cap;
-    cp.d = at<float>(ws, L.d);
+    cp.pass_base = pass * L.cap;
+    cp.pass_end = pass * L.cap + L.cap;
+    cp.d = d_buf(b);
     cp.yacc = at<float>(ws, L.yacc);
     cp.out = out;
     cp.out_f32 = out_dtype == EXL3_F32;
+    return cp;
+  };
+
+  if (L.pipe) {
+    // launch k: gate/up of pass k, down of k - 1, rotation of k + 1, combine
+    // of k - 2; pass q uses the buffers of parity q & 1
+    {
+      ProfScope ps(st, EXL3_K_ROTATE);
+      if (launch_rotate(rot_params(0, 0), st) != hipSuccess) return EXL3_E_LAUNCH;
+    }
+    for (int k = 0; k <= L.passes + 1; ++k) {
+      const bool has_gu = k < L.passes, has_dn = k >= 1 && k <= L.passes;
+      const bool has_rn = k + 1 < L.passes, has_cb = k >= 2;
+      const GemmParams g = has_gu ? gu_params(k, k & 1) : GemmParams{};
+      const GemmParams dn = has_dn ? dn_params(k - 1, (k - 1) & 1) : GemmParams{};
+      const RotParams rn = has_rn ? rot_params(k + 1, (k + 1) & 1) : RotParams{};
+      const CombineParams cp = has_cb ? cb_params(k - 2, k & 1) : CombineParams{};
+      ProfScope ps(st, EXL3_K_EXPERTS);
+      if (launch_gemm_wide_pipe(g, has_gu ? tiles_of(k) : 0, dn, has_dn ? tiles_of(k - 1) : 0, rn,
+                                cp, has_cb ? npos_of(k - 2) : 0, I / 128, (H + 255) / 256,
+                                st) != hipSuccess)
+        return EXL3_E_LAUNCH;
+    }
+    return EXL3_OK;
+  }
+
+  // otherwise: pass by pass (128-row tiles: a single pass)
+  for (int pass = 0; pass < L.passes; ++pass) {
+    const int npos = npos_of(pass);
+    const int tiles = tiles_of(pass);
+    {
+      RotParams rp = rot_params(pass, 0);
+      if (wide) {  // the pass kernel's per-tile counts start at zero
+        rp.zero = at<int32_t>(ws, L.ncnt);
+        rp.nzero = L.ncnt_ints;
+      }
+      ProfScope ps(st, EXL3_K_ROTATE);
+      if (launch_rotate(rp, st) != hipSuccess) return EXL3_E_LAUNCH;
+    }
+    const GemmParams g = gu_params(pass, 0);
+    if (!wide) {
+      ProfScope ps(st, EXL3_K_GATEUP);
+      if (launch_gemm(EPI_GATEUP, g, tiles, I / 128, st, wide) != hipSuccess) return EXL3_E_LAUNCH;
+    }
+    const GemmParams dn = dn_params(pass, 0);
+    if (wide) {
+      ProfScope ps(st, EXL3_K_EXPERTS);
+      if (launch_gemm_wide_pass(g, dn, tiles, L.slots, I / 128, (H + 255) / 256,
+                                at<int32_t>(ws, L.ncnt), st) != hipSuccess)
+        return EXL3_E_LAUNCH;
+    } else {
+      ProfScope ps(st, EXL3_K_DOWN);
+      if (launch_gemm(EPI_DOWN, dn, tiles, H / 128, st, wide) != hipSuccess) return EXL3_E_LAUNCH;
+    }
+    const CombineParams cp = cb_params(pass, 0);
     {
       ProfScope ps(st, EXL3_K_COMBINE);
       const hipError_t err =

@@ -100,13 +100,18 @@ hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks,
 hipError_t launch_gemm_wide(int epi, const GemmParams &p, int tiles, int nblocks,
                             hipStream_t s);
 // One pass of 128-row routed experts: gate/up and down in one launch, a
-// tile's down work starting once its own gate/up items are done, then the
-// input rotation of the next pass (rn; rn.nitems == 0: none), which also
-// zeroes rn.zero. `q` holds slots + 1 ints, zero at launch (slots >= plan
-// tiles of the pass).
-hipError_t launch_gemm_wide_pass(const GemmParams &gu, const GemmParams &dn, const RotParams &rn,
-                                 int tiles, int slots, int nb_gu, int nb_dn, int32_t *q,
-                                 hipStream_t s);
+// tile's down work starting once its own gate/up items are done. `q` holds
+// `slots` ints, zero at launch (slots >= plan tiles of the pass).
+hipError_t launch_gemm_wide_pass(const GemmParams &gu, const GemmParams &dn, int tiles,
+                                 int slots, int nb_gu, int nb_dn, int32_t *q, hipStream_t s);
+// Several passes of 128-row routed experts, pipelined across launches: one
+// launch runs gate/up of pass k (gu, tiles_gu), down of pass k - 1 (dn,
+// tiles_dn), the rotation of pass k + 1 (rn) and the combine of pass k - 2
+// (cb, npos_cb positions); an absent part has 0 tiles / items. The caller
+// gives each pass's x~, a~ and d the buffer of its parity.
+hipError_t launch_gemm_wide_pipe(const GemmParams &gu, int tiles_gu, const GemmParams &dn,
+                                 int tiles_dn, const RotParams &rn, const CombineParams &cb,
+                                 int npos_cb, int nb_gu, int nb_dn, hipStream_t s);
 hipError_t launch_rotate(const RotParams &p, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int npos, hipStream_t s);
 hipError_t launch_combine_rows(const CombineParams &p, hipStream_t s);
