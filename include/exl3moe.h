@@ -216,6 +216,10 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t rows, int32_t topk,
  *   xt          fp16 [C][2][hidden]  rotated gate/up inputs of the pass
  *   at          fp16 [C][intermediate] rotated down inputs a~ of the pass
  *   d           fp32 [C][hidden]     weighted per-pair down outputs
+ *               (xt, at and d each hold two such buffers, the second one
+ *               256-byte aligned after the first, when the call runs several
+ *               passes on 128-row tiles (rows * topk >= 64 * num_experts and
+ *               capacity < rows * topk): pass p uses buffer p % 2)
  *   yacc        fp32 [rows][hidden]  running row sums across passes
  *   (then private scratch of the 16-row tile path, used when rows * topk <
  *   64 * num_experts: pre-rotation fp32 sums [C][max(2 intermediate,
