@@ -289,8 +289,8 @@ def main():
     roof = {"bound": "mfma", "kernel": dom, "achieved": pre["achieved_tflops"],
             "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": pre["achieved_tflops"] / MFMA_F16_PEAK_TFLOPS, "traffic": traffic,
-            "per_launch": "%.4g flops (2 x pairs_in_pass x in x out summed over the "
-                          "projections of the launch: gate, up and down)" % pre["per_launch_flops"]}
+            "per_launch": "%.4g flops: the layer's 2 x pairs x in x out over gate, up "
+                          "and down, divided by its launches of this kernel" % pre["per_launch_flops"]}
     cpu = None
     if not args.no_cpu:
         _log("cpu baseline (oracle)")
