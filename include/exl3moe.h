@@ -257,7 +257,8 @@ int32_t exl3_decode_tiles(const uint16_t *words, int32_t ntiles, int32_t K,
 enum exl3_kernel_id {
   EXL3_K_PACK = 1, EXL3_K_ROTATE = 2, EXL3_K_GATEUP = 3, EXL3_K_DOWN = 4,
   EXL3_K_COMBINE = 5, EXL3_K_LINEAR = 6, EXL3_K_DECODE = 7,
-  EXL3_K_EXPERTS = 8 /* gate/up and down of one pass in one launch (128-row tiles) */
+  EXL3_K_EXPERTS = 8 /* 128-row tiles: gate/up and down of a single pass in one launch, or one
+                        launch of the passes pipelined across launches */
 };
 int32_t exl3_profile_begin(int32_t max_launches);
 int32_t exl3_profile_end(int32_t *kernel_ids /* host */, float *ms /* host */,
