@@ -296,6 +296,47 @@ def test_moe_wide_capacity_invariance():
         assert torch.equal(y.view(torch.int32), base.view(torch.int32)), cap
 
 
+def test_moe_wide_pipelined_edge_cases():
+    """Several passes on 128-row tiles (capacity 100 of 600 pairs: 6 passes,
+    pipelined across launches) with dropped IDs and a fully dropped row,
+    fp16 output equal to RNE(fp32), and an extra zero-scale stage (with and
+    without a trellis pointer) equal to no stage."""
+    wl = _wide_wl()
+    ids_np = wl.ids.copy()
+    ids_np[7, :] = [-3, 4]        # row 7 fully dropped -> zeros
+    ids_np[150, 0] = 99           # one dropped pair
+    wl.ids = ids_np
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    lay = exl3.moe_layout(wl.rows, wl.topk, wl.num_experts, wl.hidden, wl.intermediate, 100)
+    assert lay.passes == 6
+    out = torch.full((wl.rows, wl.hidden), 7.0, dtype=torch.float32, device=DEV)
+    y = exl3.exl3_moe_forward(x, ids, w, gate, up, down, 100, torch.float32, out=out)
+    y16 = exl3.exl3_moe_forward(x, ids, w, gate, up, down, 100, torch.float16)
+    y1 = exl3.exl3_moe_forward(x, ids, w, gate, up, down, 10 ** 6, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(y[7] == 0)
+    assert torch.equal(y.view(torch.int32), y1.view(torch.int32))
+    assert np.array_equal(_fp16_of(y).view(np.uint16), y16.cpu().numpy().view(np.uint16))
+    ref = omoe.moe_forward(wl.x, ids_np, wl.weights_f64, wl.gate, wl.up, wl.down, "R")
+    assert _rel_err(y.cpu().double().numpy(), ref) <= TOL
+
+    def with_zero_stage(pr, null):
+        n3 = synth.words_per_tensor(pr.in_features, pr.out_features, 3)
+        words = pr.words + [[None if null else np.full(n3, 0x1234, np.uint16)
+                             for e in range(pr.num_experts)]]
+        return synth.Proj(pr.in_features, pr.out_features, pr.num_experts, words,
+                          np.concatenate([pr.scale, np.zeros((1, pr.num_experts), np.float32)]),
+                          np.concatenate([pr.bits, np.full((1, pr.num_experts), 3, np.int32)]),
+                          pr.suh, pr.svh, pr.chscale)
+
+    for null in (False, True):
+        g2, u2, d2 = (exl3.DeviceProj(with_zero_stage(pr, null), DEV)
+                      for pr in (wl.gate, wl.up, wl.down))
+        y2 = exl3.exl3_moe_forward(x, ids, w, g2, u2, d2, 100, torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(y2.view(torch.int32), y.view(torch.int32)), null
+
+
 def test_linear_wide_multistage_parity():
     # 1024 rows x 8192 out selects 128-row tiles; three stages, one zero
     p, x = _linear_case(256, 8192, ((3, 1.0), (2, 0.25), (4, 0.0)), 1024, seed=9)
