@@ -15,14 +15,20 @@
 //
 // Tile: 128 rows x 256 columns per workgroup of 4 waves. Wave w owns 64
 // output columns (4 strips of 16) over all 128 rows (8 MFMA row blocks): 32
-// 16x16 fp32 accumulator blocks, held in AGPRs. GATEUP: waves 0-1 compute gate
-// and waves 2-3 compute up (128 columns each), so the epilogue has both
-// halves of SwiGLU in one workgroup.
+// 16x16 fp32 accumulator blocks (in VGPRs; the multi-stage variant keeps a
+// second set in AGPRs). GATEUP: waves 0-1 compute gate and waves 2-3 compute
+// up (128 columns each), so the epilogue has both halves of SwiGLU in one
+// workgroup.
 //
 // Two workgroups share a CU (80 KB of LDS and at most 256 registers per wave
-// each). On gfx950 a wave's VALU work and its own MFMAs do not overlap, while
-// the VALU decode of one wave does run under the MFMAs of the other wave on
-// the same SIMD.
+// each). On gfx950 a wave's own VALU work hides under its MFMAs only in part
+// (about two VALU instructions per 16x16x32 MFMA); the VALU decode of one
+// wave also runs under the MFMAs of the other wave on the same SIMD.
+//
+// Launch forms: gemm_wide_kernel (one projection kind per launch: linear
+// calls), gemm_wide_pass_kernel (gate/up and down of a single pass in one
+// launch) and gemm_wide_pipe_kernel (several passes pipelined across
+// launches), all built from wide_item below.
 //
 // Pipeline over 32-input stages (one MFMA k-step; 2 trellis tiles along k):
 //  - A (rotated activations) is copied global->LDS by DMA into a ring of 3
