@@ -107,6 +107,92 @@ __device__ __forceinline__ uint64_t match_key(int key, uint64_t live, int nb) {
 
 constexpr int kPackBatch = 8;  // rounds whose loads are issued together
 
+// a4 for one pass, by one wave: the row tiles of every expert's sub-span
+// inside the pass; only the experts overlapping the pass are visited.
+// Order: full tiles (bm rows) first, in expert order, then the partial
+// tiles (at most one per expert: the end of its span); for 128-row tiles
+// and at most 128 experts in the pass those go by rows descending, ties in
+// expert order, otherwise in expert order. Heavy tiles so come first in
+// dispatch order, where each gets a CU of its own before the light ones
+// fill the second slots; the order never changes a result. s_off: the
+// expert offsets (E + 1, nondecreasing), kept = s_off[E].
+__device__ void plan_one_pass(const PackParams &p, const int *s_off, int E, int kept, int pass,
+                              int lane) {
+  const int pb = pass * p.capacity;
+  const int pe = (int)min((int64_t)pb + p.capacity, (int64_t)kept);
+  int32_t *plan = p.plan + (int64_t)pass * (1 + 3 * p.slots);
+  int total = 0;
+  if (pb < pe) {
+    const int e_lo = expert_at(s_off, E, pb), e_hi = expert_at(s_off, E, pe - 1);
+    const int bm = p.bm;
+    auto span = [&](int e, int &lo, int &hi) {
+      lo = max(s_off[e], pb);
+      hi = min(s_off[e + 1], pe);
+    };
+    for (int eb = e_lo; eb <= e_hi; eb += 64) {  // full tiles
+      const int e = eb + lane;
+      int lo = 0, hi = 0, nf = 0;
+      if (e <= e_hi) {
+        span(e, lo, hi);
+        nf = hi > lo ? (hi - lo) / bm : 0;
+      }
+      int x = nf;  // inclusive scan over the wave
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+      }
+      const int slot0 = total + x - nf;
+      for (int t = 0; t < nf; ++t) {
+        int32_t *d = plan + 1 + 3 * (slot0 + t);
+        d[0] = e;
+        d[1] = lo - pb + t * bm;
+        d[2] = bm;
+      }
+      total += __shfl(x, 63, 64);
+    }
+    // partial rows of the experts e_lo + lane and e_lo + 64 + lane
+    int prow[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int e = e_lo + 64 * c + lane;
+      int lo = 0, hi = 0;
+      if (e <= e_hi) span(e, lo, hi);
+      prow[c] = hi > lo ? (hi - lo) % bm : 0;
+    }
+    const bool sort = bm == kBMWide && e_hi - e_lo < 128;
+    const int nfull = total;
+    int npart = 0;
+    for (int eb = e_lo; eb <= e_hi; eb += 64) {  // partial tiles
+      const int e = eb + lane, c = (eb - e_lo) >> 6;
+      int lo = 0, hi = 0;
+      if (e <= e_hi) span(e, lo, hi);
+      const int rows = (c < 2) ? prow[c & 1] : (hi > lo ? (hi - lo) % bm : 0);
+      const uint64_t has = __ballot(rows > 0);
+      int rank = npart + __popcll(has & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+      if (sort) {  // rows descending, then expert order, over both chunks
+        rank = 0;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+          for (int l = 0; l < 64; ++l) {
+            const int r2 = __shfl(prow[c2], l, 64);
+            const int e2 = e_lo + 64 * c2 + l;
+            rank += (r2 > rows || (r2 == rows && e2 < e)) ? 1 : 0;
+          }
+      }
+      if (rows > 0) {
+        int32_t *d = plan + 1 + 3 * (nfull + rank);
+        d[0] = e;
+        d[1] = lo - pb + (hi - lo) / bm * bm;
+        d[2] = rows;
+      }
+      npart += __popcll(has);
+    }
+    total = nfull + npart;
+  }
+  if (lane == 0) plan[0] = total;
+}
+
 __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
   __shared__ int s_wc[kPackWaves][kMaxE];  // per wave: count, then next position
   __shared__ int s_off[kMaxE + 1];
@@ -241,89 +327,8 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
     for (int pos = a + lane; pos < b; pos += 64) p.expert_of_pos[pos] = e;
   }
 
-  // a4: per pass (one wave each), the row tiles of every expert's sub-span
-  // inside the pass; only the experts overlapping the pass are visited.
-  // Order: full tiles (bm rows) first, in expert order, then the partial
-  // tiles (at most one per expert: the end of its span); for 128-row tiles
-  // and at most 128 experts in the pass those go by rows descending, ties in
-  // expert order, otherwise in expert order. Heavy tiles so come first in dispatch order,
-  // where each gets a CU of its own before the light ones fill the second
-  // slots; the order never changes a result.
-  for (int pass = w; pass < p.passes; pass += kPackWaves) {
-    const int pb = pass * p.capacity;
-    const int pe = (int)min((int64_t)pb + p.capacity, (int64_t)kept);
-    int32_t *plan = p.plan + (int64_t)pass * (1 + 3 * p.slots);
-    int total = 0;
-    if (pb < pe) {
-      const int e_lo = expert_at(s_off, E, pb), e_hi = expert_at(s_off, E, pe - 1);
-      const int bm = p.bm;
-      auto span = [&](int e, int &lo, int &hi) {
-        lo = max(s_off[e], pb);
-        hi = min(s_off[e + 1], pe);
-      };
-      for (int eb = e_lo; eb <= e_hi; eb += 64) {  // full tiles
-        const int e = eb + lane;
-        int lo = 0, hi = 0, nf = 0;
-        if (e <= e_hi) {
-          span(e, lo, hi);
-          nf = hi > lo ? (hi - lo) / bm : 0;
-        }
-        int x = nf;  // inclusive scan over the wave
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int y = __shfl_up(x, d, 64);
-          if (lane >= d) x += y;
-        }
-        const int slot0 = total + x - nf;
-        for (int t = 0; t < nf; ++t) {
-          int32_t *d = plan + 1 + 3 * (slot0 + t);
-          d[0] = e;
-          d[1] = lo - pb + t * bm;
-          d[2] = bm;
-        }
-        total += __shfl(x, 63, 64);
-      }
-      // partial rows of the experts e_lo + lane and e_lo + 64 + lane
-      int prow[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int e = e_lo + 64 * c + lane;
-        int lo = 0, hi = 0;
-        if (e <= e_hi) span(e, lo, hi);
-        prow[c] = hi > lo ? (hi - lo) % bm : 0;
-      }
-      const bool sort = bm == kBMWide && e_hi - e_lo < 128;
-      const int nfull = total;
-      int npart = 0;
-      for (int eb = e_lo; eb <= e_hi; eb += 64) {  // partial tiles
-        const int e = eb + lane, c = (eb - e_lo) >> 6;
-        int lo = 0, hi = 0;
-        if (e <= e_hi) span(e, lo, hi);
-        const int rows = (c < 2) ? prow[c & 1] : (hi > lo ? (hi - lo) % bm : 0);
-        const uint64_t has = __ballot(rows > 0);
-        int rank = npart + __popcll(has & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-        if (sort) {  // rows descending, then expert order, over both chunks
-          rank = 0;
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2)
-            for (int l = 0; l < 64; ++l) {
-              const int r2 = __shfl(prow[c2], l, 64);
-              const int e2 = e_lo + 64 * c2 + l;
-              rank += (r2 > rows || (r2 == rows && e2 < e)) ? 1 : 0;
-            }
-        }
-        if (rows > 0) {
-          int32_t *d = plan + 1 + 3 * (nfull + rank);
-          d[0] = e;
-          d[1] = lo - pb + (hi - lo) / bm * bm;
-          d[2] = rows;
-        }
-        npart += __popcll(has);
-      }
-      total = nfull + npart;
-    }
-    if (lane == 0) plan[0] = total;
-  }
+  // a4: one wave per pass
+  for (int pass = w; pass < p.passes; pass += kPackWaves) plan_one_pass(p, s_off, E, kept, pass, lane);
 
   // rows whose pairs were all dropped produce zeros: one row per thread to
   // find them (rare), then the row is cleared by that thread. A pack that
@@ -343,8 +348,124 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
   }
 }
 
+// The same pack and one-pass plan for at most kSmallPairs pairs, by a single
+// wave and without barriers (decode-size calls, where the big kernel's
+// barriers and phases are most of its time; with more pairs the wave's
+// serial chunks cost more than the barriers save). Lane l holds pairs l +
+// 64 i; they are counted per expert with LDS atomics, the counts scanned over
+// the experts by the wave, and positions handed out chunk by chunk in pair
+// order (ballot ranks inside a chunk, a per-expert cursor in LDS across
+// chunks): the same positions as the big kernel.
+constexpr int kSmallPairs = 64;
+
+__global__ void __launch_bounds__(64) pack_small_kernel(PackParams p) {
+  __shared__ int s_cur[kMaxE];       // count, then next position per expert
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_rowhit[kSmallPairs];
+  const int lane = threadIdx.x;
+  const int E = p.E;
+  const int pairs = p.rows * p.topk;
+  const int nb = 32 - __clz(E);  // bits of the keys 0 .. E
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  constexpr int kChunks = kSmallPairs / 64;
+
+  int ev[kChunks];
+  float wv[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int q = 64 * i + lane;
+    const bool in = q < pairs;
+    ev[i] = in ? load_expert(p.ids, p.ids_i64, q, E) : -2;
+    wv[i] = in ? load_weight(p.w, p.w_dtype, q) : 0.0f;
+  }
+  for (int e = lane; e < E; e += 64) s_cur[e] = 0;
+  int dropped = 0;
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    if (ev[i] >= 0) atomicAdd(&s_cur[ev[i]], 1);  // counts are order-free
+    dropped += __popcll(__ballot(ev[i] == -1));
+  }
+  // a2: exclusive scan of the counts over the experts
+  int run = 0, nact = 0;
+  for (int eb = 0; eb < E; eb += 64) {
+    const int e = eb + lane;
+    const int c = (e < E) ? s_cur[e] : 0;
+    int x = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    const int ex = run + x - c;
+    if (e < E) {
+      s_off[e] = ex;
+      s_cur[e] = ex;
+      p.count[e] = c;
+      p.offset[e] = ex;
+    }
+    nact += __popcll(__ballot(e < E && c > 0));
+    run += __shfl(x, 63, 64);
+  }
+  const int kept = run;
+  if (lane == 0) {
+    s_off[E] = kept;
+    p.offset[E] = kept;
+    *p.num_active = nact;
+    *p.status = dropped;
+    if (p.ctrl) p.ctrl[0] = dropped;
+  }
+  // a3: positions in pair order
+  if (p.do_plan)
+    for (int r = lane; r < p.rows; r += 64) s_rowhit[r] = 0;
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    if (64 * i >= pairs) break;  // uniform
+    const int q = 64 * i + lane;
+    const int e = ev[i];
+    const bool valid = e >= 0;
+    const uint64_t m = match_key(valid ? e : E, __ballot(valid), nb);
+    if (valid) {
+      const int rank = __popcll(m & lt_mask);
+      const int base = s_cur[e];
+      const int pos = base + rank;
+      if (rank == 0) s_cur[e] = base + __popcll(m);
+      p.pair_of_pos[pos] = q;
+      p.weight_of_pos[pos] = wv[i];
+      p.pos_of_pair[q] = pos;
+      if (p.do_plan) {
+        p.expert_of_pos[pos] = e;
+        s_rowhit[q / p.topk] = 1;
+      }
+    } else if (e == -1) {
+      p.pos_of_pair[q] = -1;
+    }
+  }
+  for (int pos = kept + lane; pos < pairs; pos += 64) {
+    p.pair_of_pos[pos] = -1;
+    p.weight_of_pos[pos] = 0.0f;
+  }
+  if (!p.do_plan) return;
+  if (lane == 0 && p.ctrl) p.ctrl[1] = 0;  // bad stage entries
+  for (int i = lane; i < p.nzero; i += 64) p.zero[i] = 0;
+  plan_one_pass(p, s_off, E, kept, 0, lane);  // one pass: capacity >= pairs
+  // rows whose pairs were all dropped produce zeros
+  if (p.out && dropped > 0) {
+    for (int r = 0; r < p.rows; ++r) {
+      if (s_rowhit[r]) continue;  // uniform
+      for (int c = lane; c < p.H; c += 64) {
+        if (p.out_f32) ((float *)p.out)[(int64_t)r * p.H + c] = 0.0f;
+        else ((uint16_t *)p.out)[(int64_t)r * p.H + c] = 0;
+      }
+    }
+  }
+}
+
 hipError_t launch_pack(const PackParams &p, hipStream_t s) {
-  hipLaunchKernelGGL(pack_plan_kernel, dim3(1), dim3(kPackThreads), 0, s, p);
+  const int64_t pairs = (int64_t)p.rows * p.topk;
+  if (p.do_pack && pairs <= kSmallPairs && (!p.do_plan || p.passes == 1))
+    hipLaunchKernelGGL(pack_small_kernel, dim3(1), dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL(pack_plan_kernel, dim3(1), dim3(kPackThreads), 0, s, p);
   return hipGetLastError();
 }
 
