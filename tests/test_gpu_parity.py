@@ -224,13 +224,16 @@ def test_dropped_ids_and_unrouted_rows():
     ids_np[5, 1] = 8               # one dropped pair
     wl.ids = ids_np
     gate, up, down, x, ids, w = _moe_inputs(wl)
-    for dt in (torch.float32, torch.float16):
-        out = torch.full((8, wl.hidden), 7.0, dtype=dt, device=DEV)
-        y = exl3.exl3_moe_forward(x, ids, w, gate, up, down, 5, dt, out=out)
-        torch.cuda.synchronize()
-        ref = omoe.moe_forward(wl.x, ids_np, wl.weights_f64, wl.gate, wl.up, wl.down, "R")
-        assert torch.all(y[3] == 0)
-        assert _rel_err(y.cpu().double().numpy(), ref) <= (TOL if dt == torch.float32 else 5e-3)
+    ref = omoe.moe_forward(wl.x, ids_np, wl.weights_f64, wl.gate, wl.up, wl.down, "R")
+    # capacity 5: several passes; 10**6: one pass (pack, plan and rotation in
+    # one launch for so few pairs)
+    for cap in (5, 10 ** 6):
+        for dt in (torch.float32, torch.float16):
+            out = torch.full((8, wl.hidden), 7.0, dtype=dt, device=DEV)
+            y = exl3.exl3_moe_forward(x, ids, w, gate, up, down, cap, dt, out=out)
+            torch.cuda.synchronize()
+            assert torch.all(y[3] == 0), (cap, dt)
+            assert _rel_err(y.cpu().double().numpy(), ref) <= (TOL if dt == torch.float32 else 5e-3)
 
 
 # ---------------------------------------------------- full-size workloads

@@ -212,7 +212,7 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
                     const exl3_proj *down, void *out, int32_t out_dtype,
                     const MoeLayout &L, void *ws, const int32_t *pair_of_pos,
                     const int32_t *pos_of_pair, const float *weight_of_pos,
-                    const int32_t *offset, hipStream_t st) {
+                    const int32_t *offset, hipStream_t st, const PackParams *fused_pack = nullptr) {
   const int H = gate->in_features, I = gate->out_features, E = gate->num_experts;
   const int64_t P = (int64_t)rows * topk;
   const int32_t *total_valid = offset + E;
@@ -340,7 +340,11 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
   for (int pass = 0; pass < L.passes; ++pass) {
     const int npos = npos_of(pass);
     const int tiles = tiles_of(pass);
-    {
+    if (fused_pack && pass == 0) {  // pack, plan and this rotation in one launch
+      ProfScope ps(st, EXL3_K_PACK);
+      if (launch_pack_rotate(*fused_pack, rot_params(0, 0), st) != hipSuccess)
+        return EXL3_E_LAUNCH;
+    } else {
       RotParams rp = rot_params(pass, 0);
       if (wide) {  // the pass kernel's per-tile counts start at zero
         rp.zero = at<int32_t>(ws, L.ncnt);
@@ -606,12 +610,14 @@ int32_t exl3_moe_forward(const uint16_t *x, int32_t rows, const void *ids, int32
   p.ctrl = at<int32_t>(ws, L.ctrl);
   p.zero = L.ncnt_ints ? at<int32_t>(ws, L.ncnt) : nullptr;
   p.nzero = L.ncnt_ints;
-  {
+  // few pairs in one pass: the pack runs inside the first rotation's launch
+  const bool fuse = !L.pipe && pack_rotate_fits((int64_t)rows * topk, L.passes);
+  if (!fuse) {
     ProfScope ps(st, EXL3_K_PACK);
     if (launch_pack(p, st) != hipSuccess) return EXL3_E_LAUNCH;
   }
   return run_experts(x, rows, topk, gate, up, down, out, out_dtype, L, ws, p.pair_of_pos,
-                     p.pos_of_pair, p.weight_of_pos, p.offset, st);
+                     p.pos_of_pair, p.weight_of_pos, p.offset, st, fuse ? &p : nullptr);
 }
 
 int32_t exl3_moe_additive(const uint16_t *x, int32_t rows, int32_t topk,

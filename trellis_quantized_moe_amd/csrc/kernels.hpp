@@ -116,6 +116,10 @@ hipError_t launch_rotate(const RotParams &p, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int npos, hipStream_t s);
 hipError_t launch_combine_rows(const CombineParams &p, hipStream_t s);
 hipError_t launch_pack(const PackParams &p, hipStream_t s);
+// Pack, one-pass plan and the rotation of that pass in one launch, for calls
+// where pack_rotate_fits (few pairs, one pass). rp: the pass's rotation.
+bool pack_rotate_fits(int64_t pairs, int passes);
+hipError_t launch_pack_rotate(const PackParams &p, const RotParams &rp, hipStream_t s);
 hipError_t launch_decode_tiles(const uint16_t *words, int ntiles, int K,
                                uint16_t *out, hipStream_t s);
 

@@ -13,29 +13,14 @@
 
 namespace exl3 {
 
-// Unit gid = item * (H / 128) + block. Lane i (0..15 of the group) loads
-// entries 8i..8i+7 (16 bytes) of the x block once, transforms it for every
-// projection, and stores each result as one 16-byte run in the kSigma order:
-// slots 0..7 of its half-group hold entries {0,4,1,5,2,6,3,7} of the lane's
-// 8. Every lane of the group must call this with the same gid.
-__device__ __forceinline__ void rotate_unit(const RotParams &p, int64_t gid, int i) {
-  const int nblk = p.H >> 7;
-  if (gid >= (int64_t)p.nitems * nblk) return;
-  const int item = (int)(gid / nblk);
-  const int blk = (int)(gid - (int64_t)item * nblk);
-
-  int row, e;
-  if (p.pair_of_pos != nullptr) {
-    const int pos = p.pass_base + item;
-    if (pos >= min(*p.total_valid, p.pairs)) return;  // uniform per group
-    const int q = p.pair_of_pos[pos];
-    if (q < 0 || q >= p.pairs) return;  // inconsistent metadata: drop
-    row = q / p.topk;
-    e = p.expert_of_pos[pos];
-  } else {
-    row = item;
-    e = 0;
-  }
+// One (item, 128-block) unit whose source row and expert are known. Lane i
+// (0..15 of the group) loads entries 8i..8i+7 (16 bytes) of the x block
+// once, transforms it for every projection, and stores each result as one
+// 16-byte run in the kSigma order: slots 0..7 of its half-group hold entries
+// {0,4,1,5,2,6,3,7} of the lane's 8. Every lane of the group must call this
+// with the same unit.
+__device__ __forceinline__ void rotate_block(const RotParams &p, int item, int blk, int row, int e,
+                                             int i) {
   const int64_t col = blk * 128 + 8 * i;
   const u32x4 xv = *(const u32x4 *)(p.x + (int64_t)row * p.H + col);
   u32x4 sv[2];
@@ -62,6 +47,28 @@ __device__ __forceinline__ void rotate_unit(const RotParams &p, int64_t gid, int
                      (uint32_t)h[2] | ((uint32_t)h[6] << 16), (uint32_t)h[3] | ((uint32_t)h[7] << 16)};
     *(u32x4 *)(p.xt + ((int64_t)item * p.nproj + pj) * p.H + col) = o;
   }
+}
+
+// Unit gid = item * (H / 128) + block: the row and expert of the item come
+// from the pack (MoE) or are the item itself (linear).
+__device__ __forceinline__ void rotate_unit(const RotParams &p, int64_t gid, int i) {
+  const int nblk = p.H >> 7;
+  if (gid >= (int64_t)p.nitems * nblk) return;
+  const int item = (int)(gid / nblk);
+  const int blk = (int)(gid - (int64_t)item * nblk);
+  int row, e;
+  if (p.pair_of_pos != nullptr) {
+    const int pos = p.pass_base + item;
+    if (pos >= min(*p.total_valid, p.pairs)) return;  // uniform per group
+    const int q = p.pair_of_pos[pos];
+    if (q < 0 || q >= p.pairs) return;  // inconsistent metadata: drop
+    row = q / p.topk;
+    e = p.expert_of_pos[pos];
+  } else {
+    row = item;
+    e = 0;
+  }
+  rotate_block(p, item, blk, row, e, i);
 }
 
 }  // namespace exl3

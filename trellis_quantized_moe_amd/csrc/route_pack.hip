@@ -14,6 +14,7 @@
 // follow pair order exactly without atomics on the positions.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "rotate_dev.hpp"
 
 namespace exl3 {
 
@@ -351,43 +352,35 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
 // The same pack and one-pass plan for at most kSmallPairs pairs, by a single
 // wave and without barriers (decode-size calls, where the big kernel's
 // barriers and phases are most of its time; with more pairs the wave's
-// serial chunks cost more than the barriers save). Lane l holds pairs l +
-// 64 i; they are counted per expert with LDS atomics, the counts scanned over
-// the experts by the wave, and positions handed out chunk by chunk in pair
-// order (ballot ranks inside a chunk, a per-expert cursor in LDS across
-// chunks): the same positions as the big kernel.
+// serial work costs more than the barriers save). Lane l holds pair l; the
+// pairs are counted per expert with LDS atomics, the counts scanned over the
+// experts by the wave, and each pair's rank among the earlier pairs of its
+// expert found with ballots: the same positions as the big kernel.
 constexpr int kSmallPairs = 64;
 
-__global__ void __launch_bounds__(64) pack_small_kernel(PackParams p) {
-  __shared__ int s_cur[kMaxE];       // count, then next position per expert
-  __shared__ int s_off[kMaxE + 1];
-  __shared__ int s_rowhit[kSmallPairs];
-  const int lane = threadIdx.x;
+struct SmallPairs {
+  int e;      // expert of the lane's pair; -1 dropped, -2 no pair
+  float w;    // its route weight (when loaded)
+  int pos;    // its position, -1 if none
+  int kept, dropped, nact;
+};
+
+// Positions of the (at most 64) pairs by one wave. s_cur and s_off hold E
+// and E + 1 ints of LDS; s_off ends as the expert offsets. With `meta` the
+// weights are loaded and the counts and offsets written.
+__device__ SmallPairs small_positions(const PackParams &p, int *s_cur, int *s_off, bool meta) {
+  const int lane = threadIdx.x & 63;
   const int E = p.E;
   const int pairs = p.rows * p.topk;
-  const int nb = 32 - __clz(E);  // bits of the keys 0 .. E
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  constexpr int kChunks = kSmallPairs / 64;
-
-  int ev[kChunks];
-  float wv[kChunks];
-#pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    const int q = 64 * i + lane;
-    const bool in = q < pairs;
-    ev[i] = in ? load_expert(p.ids, p.ids_i64, q, E) : -2;
-    wv[i] = in ? load_weight(p.w, p.w_dtype, q) : 0.0f;
-  }
+  SmallPairs r;
+  const bool in = lane < pairs;
+  r.e = in ? load_expert(p.ids, p.ids_i64, lane, E) : -2;
+  r.w = (in && meta) ? load_weight(p.w, p.w_dtype, lane) : 0.0f;
   for (int e = lane; e < E; e += 64) s_cur[e] = 0;
-  int dropped = 0;
-#pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    if (ev[i] >= 0) atomicAdd(&s_cur[ev[i]], 1);  // counts are order-free
-    dropped += __popcll(__ballot(ev[i] == -1));
-  }
-  // a2: exclusive scan of the counts over the experts
+  if (r.e >= 0) atomicAdd(&s_cur[r.e], 1);  // counts are order-free
+  r.dropped = __popcll(__ballot(r.e == -1));
   int run = 0, nact = 0;
-  for (int eb = 0; eb < E; eb += 64) {
+  for (int eb = 0; eb < E; eb += 64) {  // exclusive scan over the experts
     const int e = eb + lane;
     const int c = (e < E) ? s_cur[e] : 0;
     int x = c;
@@ -400,65 +393,115 @@ __global__ void __launch_bounds__(64) pack_small_kernel(PackParams p) {
     if (e < E) {
       s_off[e] = ex;
       s_cur[e] = ex;
-      p.count[e] = c;
-      p.offset[e] = ex;
+      if (meta) {
+        p.count[e] = c;
+        p.offset[e] = ex;
+      }
     }
     nact += __popcll(__ballot(e < E && c > 0));
     run += __shfl(x, 63, 64);
   }
-  const int kept = run;
+  r.kept = run;
+  r.nact = nact;
+  if (lane == 0) s_off[E] = run;
+  const bool valid = r.e >= 0;
+  const uint64_t m = match_key(valid ? r.e : E, __ballot(valid), 32 - __clz(E));
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  r.pos = valid ? s_cur[r.e] + __popcll(m & lt_mask) : -1;
+  return r;
+}
+
+// Pack (and with do_plan the one-pass plan) of at most kSmallPairs pairs by
+// the first wave of the block; the other waves return.
+__device__ void pack_small(const PackParams &p) {
+  __shared__ int s_cur[kMaxE];
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_rowhit[kSmallPairs];
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const int pairs = p.rows * p.topk;
+  const SmallPairs r = small_positions(p, s_cur, s_off, true);
   if (lane == 0) {
-    s_off[E] = kept;
-    p.offset[E] = kept;
-    *p.num_active = nact;
-    *p.status = dropped;
-    if (p.ctrl) p.ctrl[0] = dropped;
+    p.offset[p.E] = r.kept;
+    *p.num_active = r.nact;
+    *p.status = r.dropped;
+    if (p.ctrl) p.ctrl[0] = r.dropped;
   }
-  // a3: positions in pair order
   if (p.do_plan)
-    for (int r = lane; r < p.rows; r += 64) s_rowhit[r] = 0;
-#pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    if (64 * i >= pairs) break;  // uniform
-    const int q = 64 * i + lane;
-    const int e = ev[i];
-    const bool valid = e >= 0;
-    const uint64_t m = match_key(valid ? e : E, __ballot(valid), nb);
-    if (valid) {
-      const int rank = __popcll(m & lt_mask);
-      const int base = s_cur[e];
-      const int pos = base + rank;
-      if (rank == 0) s_cur[e] = base + __popcll(m);
-      p.pair_of_pos[pos] = q;
-      p.weight_of_pos[pos] = wv[i];
-      p.pos_of_pair[q] = pos;
-      if (p.do_plan) {
-        p.expert_of_pos[pos] = e;
-        s_rowhit[q / p.topk] = 1;
-      }
-    } else if (e == -1) {
-      p.pos_of_pair[q] = -1;
+    for (int row = lane; row < p.rows; row += 64) s_rowhit[row] = 0;
+  if (r.e >= 0) {
+    p.pair_of_pos[r.pos] = lane;
+    p.weight_of_pos[r.pos] = r.w;
+    p.pos_of_pair[lane] = r.pos;
+    if (p.do_plan) {
+      p.expert_of_pos[r.pos] = r.e;
+      s_rowhit[lane / p.topk] = 1;
     }
+  } else if (r.e == -1) {
+    p.pos_of_pair[lane] = -1;
   }
-  for (int pos = kept + lane; pos < pairs; pos += 64) {
+  for (int pos = r.kept + lane; pos < pairs; pos += 64) {
     p.pair_of_pos[pos] = -1;
     p.weight_of_pos[pos] = 0.0f;
   }
   if (!p.do_plan) return;
   if (lane == 0 && p.ctrl) p.ctrl[1] = 0;  // bad stage entries
   for (int i = lane; i < p.nzero; i += 64) p.zero[i] = 0;
-  plan_one_pass(p, s_off, E, kept, 0, lane);  // one pass: capacity >= pairs
+  plan_one_pass(p, s_off, p.E, r.kept, 0, lane);  // one pass: capacity >= pairs
   // rows whose pairs were all dropped produce zeros
-  if (p.out && dropped > 0) {
-    for (int r = 0; r < p.rows; ++r) {
-      if (s_rowhit[r]) continue;  // uniform
+  if (p.out && r.dropped > 0) {
+    for (int row = 0; row < p.rows; ++row) {
+      if (s_rowhit[row]) continue;  // uniform
       for (int c = lane; c < p.H; c += 64) {
-        if (p.out_f32) ((float *)p.out)[(int64_t)r * p.H + c] = 0.0f;
-        else ((uint16_t *)p.out)[(int64_t)r * p.H + c] = 0;
+        if (p.out_f32) ((float *)p.out)[(int64_t)row * p.H + c] = 0.0f;
+        else ((uint16_t *)p.out)[(int64_t)row * p.H + c] = 0;
       }
     }
   }
 }
+
+__global__ void __launch_bounds__(64) pack_small_kernel(PackParams p) { pack_small(p); }
+
+// Pack, plan and the rotation of the one pass in a single launch (at most
+// kSmallPairs pairs): block 0 packs; every other block recomputes the same
+// positions with one wave (no block waits for another) and rotates its 16
+// (position, 128-block) units.
+__global__ void __launch_bounds__(256) pack_rotate_small_kernel(PackParams p, RotParams rp) {
+  if (blockIdx.x == 0) {
+    pack_small(p);
+    return;
+  }
+  __shared__ int s_cur[kMaxE];
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_q[kSmallPairs], s_e[kSmallPairs];
+  __shared__ int s_kept;
+  if (threadIdx.x < 64) {
+    const SmallPairs r = small_positions(p, s_cur, s_off, false);
+    if (r.e >= 0) {
+      s_q[r.pos] = threadIdx.x;
+      s_e[r.pos] = r.e;
+    }
+    if (threadIdx.x == 0) s_kept = r.kept;
+  }
+  __syncthreads();
+  const int nblk = rp.H >> 7;
+  const int gid = (blockIdx.x - 1) * 16 + (threadIdx.x >> 4);
+  const int item = gid / nblk, blk = gid - item * nblk;
+  if (item < s_kept) rotate_block(rp, item, blk, s_q[item] / p.topk, s_e[item], threadIdx.x & 15);
+}
+
+hipError_t launch_pack_rotate(const PackParams &p, const RotParams &rp, hipStream_t s) {
+  const int64_t pairs = (int64_t)p.rows * p.topk;
+  if (!p.do_pack || !p.do_plan || p.passes != 1 || pairs > kSmallPairs || rp.nproj < 1 ||
+      rp.nproj > 2 || rp.pass_base != 0 || rp.nitems < pairs)
+    return hipErrorInvalidValue;
+  const int64_t units = pairs * (rp.H >> 7);
+  hipLaunchKernelGGL(pack_rotate_small_kernel, dim3((unsigned)(1 + (units + 15) / 16)), dim3(256),
+                     0, s, p, rp);
+  return hipGetLastError();
+}
+
+bool pack_rotate_fits(int64_t pairs, int passes) { return pairs <= kSmallPairs && passes == 1; }
 
 hipError_t launch_pack(const PackParams &p, hipStream_t s) {
   const int64_t pairs = (int64_t)p.rows * p.topk;
