@@ -48,7 +48,7 @@ extern "C" {
 /* Exact-match compatibility contract [p1 API contract]: bumped on any
  * incompatible signature, pointer-layout, workspace, residual-encoding or
  * overflow-semantics change. Consumers must require an exact value. */
-#define EXL3_ABI_VERSION 1
+#define EXL3_ABI_VERSION 2
 
 enum exl3_dtype {
   EXL3_F16 = 1, EXL3_BF16 = 2, EXL3_F32 = 3, EXL3_I32 = 4, EXL3_I64 = 5
@@ -153,7 +153,10 @@ int32_t exl3_route_pack(const void *ids, int32_t ids_dtype, const void *w,
 
 /*
  * Plain EXL3 linear [p2 What this changes: row-invariant linear; prompt rows
- * in blocks]. x: [rows][in] fp16; out: [rows][out] fp16 (RNE) or fp32.
+ * in blocks]. x: [rows][in], x_dtype EXL3_F16 or EXL3_BF16 (read exactly; the
+ * rotated rows are rounded to fp16 either way); out: [rows][out], out_dtype
+ * EXL3_F16 or EXL3_BF16 (round to nearest even of the fp32 result) or
+ * EXL3_F32.
  * A row's output bytes do not depend on rows or on how rows are chunked.
  * ws: device workspace of at least exl3_linear_workspace_size() bytes (the
  * rotated rows, plus pre-rotation sums and completion counts for small row
@@ -161,9 +164,9 @@ int32_t exl3_route_pack(const void *ids, int32_t ids_dtype, const void *w,
  */
 size_t exl3_linear_workspace_size(int32_t rows, int32_t in_features,
                                   int32_t out_features);
-int32_t exl3_linear(const uint16_t *x, int32_t rows, const exl3_proj *proj,
-                    void *out, int32_t out_dtype, void *ws, size_t ws_bytes,
-                    void *stream);
+int32_t exl3_linear(const uint16_t *x, int32_t x_dtype, int32_t rows,
+                    const exl3_proj *proj, void *out, int32_t out_dtype, void *ws,
+                    size_t ws_bytes, void *stream);
 
 /*
  * Routed-experts layer. Per kept pair (r, j), e = ids[r][j], w = weight:
@@ -179,15 +182,18 @@ int32_t exl3_linear(const uint16_t *x, int32_t rows, const exl3_proj *proj,
  * bit-identical for every capacity [p1 Summary, API contract].
  * num_active_hint: launch-size hint only; never changes results (pass <= 0
  * for "unknown") [p1 API contract].
- * x: [rows][hidden] fp16; out: [rows][hidden] fp16 (RNE) or fp32.
+ * x: [rows][hidden], x_dtype EXL3_F16 or EXL3_BF16 (read exactly; the rotated
+ * inputs x~ are rounded to fp16 either way, since the decoded weights are
+ * fp16 values); out: [rows][hidden], out_dtype EXL3_F16 or EXL3_BF16 (round
+ * to nearest even of the fp32 result) or EXL3_F32.
  */
 size_t exl3_moe_workspace_size(int32_t rows, int32_t topk, int32_t num_experts,
                                int32_t hidden, int32_t intermediate,
                                int32_t capacity);
 
 /* Stable route pack + experts in one call [p1 Summary: fused variant]. */
-int32_t exl3_moe_forward(const uint16_t *x, int32_t rows, const void *ids,
-                         int32_t ids_dtype, const void *w, int32_t w_dtype,
+int32_t exl3_moe_forward(const uint16_t *x, int32_t x_dtype, int32_t rows,
+                         const void *ids, int32_t ids_dtype, const void *w, int32_t w_dtype,
                          int32_t topk, const exl3_proj *gate,
                          const exl3_proj *up, const exl3_proj *down, void *out,
                          int32_t out_dtype, int32_t capacity,
@@ -196,7 +202,7 @@ int32_t exl3_moe_forward(const uint16_t *x, int32_t rows, const void *ids,
 
 /* Experts only, for callers that already hold route metadata (from
  * exl3_route_pack or equivalent) [p1 Summary: exl3_moe_additive]. */
-int32_t exl3_moe_additive(const uint16_t *x, int32_t rows, int32_t topk,
+int32_t exl3_moe_additive(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t topk,
                           const exl3_route_meta *meta, const exl3_proj *gate,
                           const exl3_proj *up, const exl3_proj *down,
                           void *out, int32_t out_dtype, int32_t capacity,

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert exl3.abi_version() == 1
+    assert exl3.abi_version() == 2
     L = exl3.lib()
     for s in range(0, -9, -1):
         msg = L.exl3_status_string(s).decode()
@@ -62,20 +62,21 @@ def _proj(**kw):
 
 
 def _fwd(gate=None, up=None, down=None, rows=4, topk=2, capacity=8, out_dtype=exl3.F32,
-         ids=4096, ids_dtype=exl3.I32, w=8192, w_dtype=exl3.F32, x=16384, out=32768,
+         x_dtype=exl3.F16, ids=4096, ids_dtype=exl3.I32, w=8192, w_dtype=exl3.F32, x=16384, out=32768,
          ws=65536, ws_bytes=1 << 40):
     gate = gate or _proj()
     up = up or _proj()
     down = down or _proj(in_features=512, out_features=256)
     return exl3.lib().exl3_moe_forward(
-        ctypes.c_void_p(x), rows, ctypes.c_void_p(ids), ids_dtype, ctypes.c_void_p(w),
+        ctypes.c_void_p(x), x_dtype, rows, ctypes.c_void_p(ids), ids_dtype, ctypes.c_void_p(w),
         w_dtype, topk, ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down),
         ctypes.c_void_p(out), out_dtype, capacity, -1, ctypes.c_void_p(ws), ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=0), -1), (dict(ids=0), -1), (dict(ws=0), -1),
-    (dict(ids_dtype=exl3.F16), -2), (dict(w_dtype=exl3.I32), -2), (dict(out_dtype=exl3.BF16), -2),
+    (dict(ids_dtype=exl3.F16), -2), (dict(w_dtype=exl3.I32), -2), (dict(out_dtype=exl3.I32), -2),
+    (dict(x_dtype=exl3.F32), -2), (dict(x_dtype=0), -2),
     (dict(gate=_proj(in_features=200)), -3), (dict(up=_proj(out_features=384)), -3),
     (dict(down=_proj(in_features=512, out_features=128)), -3),
     (dict(up=_proj(num_experts=7)), -3),
@@ -90,6 +91,13 @@ def test_forward_rejects_bad_arguments_before_device_work(kw, code):
 
 def test_rows_zero_is_a_noop():
     assert _fwd(rows=0, x=0, ws=0) == 0
+
+
+@pytest.mark.parametrize("xdt,odt", [(exl3.BF16, exl3.F32), (exl3.F16, exl3.BF16),
+                                     (exl3.BF16, exl3.BF16)])
+def test_bf16_activations_and_outputs_pass_validation(xdt, odt):
+    # accepted dtypes get as far as the device-pointer check (-5)
+    assert _fwd(x_dtype=xdt, out_dtype=odt) == -5
 
 
 def test_host_pointers_are_rejected_as_not_device():

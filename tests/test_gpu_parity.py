@@ -353,6 +353,76 @@ def test_linear_wide_multistage_parity():
     assert torch.equal(y_small.view(torch.int32), y[:5].view(torch.int32))
 
 
+# ------------------------------------------- bf16 activations and outputs
+def _bf16_x(shape, seed):
+    """Seeded bf16 activations: device tensor and the exact values (float64)."""
+    v = np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+    v[np.abs(v) < 2.0 ** -14] = 0.0  # every value then also exact in fp16
+    bits = synth.f32_to_bf16_bits(v)
+    t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return t, synth.bf16_bits_to_f64(bits)
+
+
+def _check_out16(y32, y16, dtype):
+    """A 16-bit output equals torch's CPU round-to-nearest-even of the fp32 one."""
+    want = y32.cpu().to(dtype).view(torch.int16).numpy()
+    assert np.array_equal(y16.cpu().view(torch.int16).numpy(), want), dtype
+
+
+@pytest.mark.parametrize("fin,fout,stages,rows", [
+    (256, 384, ((3, 1.0), (2, 0.37)), 33), (256, 8192, ((4, 1.0),), 1024)])
+def test_linear_bf16_activations_and_outputs(fin, fout, stages, rows):
+    """bf16 x is read exactly (the rotated rows still round to fp16); bf16
+    and fp16 outputs are the fp32 output rounded to nearest even."""
+    _say("linear bf16", fin, fout, rows)
+    p, _ = _linear_case(fin, fout, stages, rows, seed=fin + fout + rows)
+    xd, xv = _bf16_x((rows, fin), seed=rows)
+    dp = exl3.DeviceProj(p, DEV)
+    y32 = exl3.exl3_linear(xd, dp, torch.float32)
+    yb = exl3.exl3_linear(xd, dp, torch.bfloat16)
+    yh = exl3.exl3_linear(xd, dp, torch.float16)
+    torch.cuda.synchronize()
+    sample = list(range(rows)) if rows <= 64 else [0, 5, rows - 1]
+    ref = olinear.linear(xv[sample], p, "R")
+    assert _rel_err(y32.cpu().double().numpy()[sample], ref) <= TOL
+    _check_out16(y32, yb, torch.bfloat16)
+    _check_out16(y32, yh, torch.float16)
+    # an fp16 x holding the same values gives the same bytes
+    xh = torch.from_numpy(xv.astype(np.float16)).to(DEV)
+    assert np.array_equal(xh.cpu().double().numpy(), xv)
+    assert torch.equal(exl3.exl3_linear(xh, dp, torch.float32).view(torch.int32),
+                       y32.view(torch.int32))
+
+
+@pytest.mark.parametrize("case", ["tiny", "one_row", "wide", "wide_pipelined"])
+def test_moe_bf16_activations_and_outputs(case):
+    """bf16 x through every launch form (16-row tiles, the one-launch decode
+    pack + rotation, 128-row tiles in one pass and pipelined over 6 passes);
+    bf16 output equal to RNE of the fp32 output."""
+    _say("moe bf16", case)
+    if case == "tiny":
+        wl, cap = _tiny(K=(2, 3, 5, 8)), None
+    elif case == "one_row":
+        wl, cap = _tiny(rows=1, topk=8, E=16, K=(3, 4)), None
+    else:
+        wl, cap = _wide_wl(), (100 if case == "wide_pipelined" else 10 ** 6)
+    cap = wl.capacity if cap is None else cap
+    gate, up, down, _, ids, w = _moe_inputs(wl)
+    xd, xv = _bf16_x((wl.rows, wl.hidden), seed=len(case))
+    y32 = exl3.exl3_moe_forward(xd, ids, w, gate, up, down, cap, torch.float32)
+    yb = exl3.exl3_moe_forward(xd, ids, w, gate, up, down, cap, torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = omoe.moe_forward(xv, wl.ids, wl.weights_f64, wl.gate, wl.up, wl.down, "R")
+    assert _rel_err(y32.cpu().double().numpy(), ref) <= TOL
+    _check_out16(y32, yb, torch.bfloat16)
+    if case == "wide_pipelined":
+        y1 = exl3.exl3_moe_forward(xd, ids, w, gate, up, down, 10 ** 6, torch.float32)
+        assert torch.equal(y1.view(torch.int32), y32.view(torch.int32))
+        meta = exl3.exl3_route_pack(ids, w, wl.num_experts)
+        ya = exl3.exl3_moe_additive(xd, wl.topk, meta, gate, up, down, cap, torch.bfloat16)
+        assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
+
+
 # ------------------------------------------ prefill workload at full scale
 def _ulp_dist(a16, b16):
     """Distance in fp16 ulps between two fp16 arrays (ordered bit patterns)."""

@@ -67,8 +67,10 @@ __device__ __forceinline__ void combine_position(const CombineParams &p, int ite
     } else if (p.out_f32) {
       *(f32x4 *)((float *)p.out + rowoff + c) = acc;
     } else {
-      const uint32_t lo = (uint32_t)f32_to_f16_bits(acc[0]) | ((uint32_t)f32_to_f16_bits(acc[1]) << 16);
-      const uint32_t hi = (uint32_t)f32_to_f16_bits(acc[2]) | ((uint32_t)f32_to_f16_bits(acc[3]) << 16);
+      const uint32_t lo = (uint32_t)f32_to_out16(acc[0], p.out_bf16) |
+                           ((uint32_t)f32_to_out16(acc[1], p.out_bf16) << 16);
+      const uint32_t hi = (uint32_t)f32_to_out16(acc[2], p.out_bf16) |
+                           ((uint32_t)f32_to_out16(acc[3], p.out_bf16) << 16);
       *(uint2 *)((uint16_t *)p.out + rowoff + c) = make_uint2(lo, hi);
     }
   };

@@ -340,5 +340,19 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
 }
+// bfloat16 = the upper 16 bits of an fp32, rounded to nearest even (add
+// 0x7FFF plus the lowest kept bit, then truncate); a NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+// A 16-bit output value: bf16 or fp16, both round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_out16(float x, int bf16) {
+  return bf16 ? f32_to_bf16_bits(x) : f32_to_f16_bits(x);
+}
 
 }  // namespace exl3

@@ -102,7 +102,7 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, float *T, int ld, 
           p.out_f32[o] = y * wt;
         } else {
           if (p.out_f32) p.out_f32[o] = y;
-          else p.out_h[o] = f32_to_f16_bits(y);
+          else p.out_h[o] = f32_to_out16(y, p.out_bf16);
         }
       }
     }

@@ -105,7 +105,8 @@ ProjDev to_dev(const exl3_proj *p) {
   return d;
 }
 
-bool out_dtype_ok(int32_t t) { return t == EXL3_F16 || t == EXL3_F32; }
+bool out_dtype_ok(int32_t t) { return t == EXL3_F16 || t == EXL3_BF16 || t == EXL3_F32; }
+bool x_dtype_ok(int32_t t) { return t == EXL3_F16 || t == EXL3_BF16; }
 
 // Tile shape choice (never changes results: both tile shapes run the same
 // per-element MFMA chain and the same epilogue code). Wide 128-row tiles pay
@@ -175,7 +176,7 @@ T *at(void *ws, size_t off) {
   return (T *)((char *)ws + off);
 }
 
-int32_t validate_moe_common(const uint16_t *x, int32_t rows, int32_t topk,
+int32_t validate_moe_common(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t topk,
                             const exl3_proj *gate, const exl3_proj *up,
                             const exl3_proj *down, void *out, int32_t out_dtype,
                             int32_t capacity, void *ws) {
@@ -183,7 +184,7 @@ int32_t validate_moe_common(const uint16_t *x, int32_t rows, int32_t topk,
   if (!x || !out || !ws) return EXL3_E_NULL;
   for (const exl3_proj *p : {gate, up, down})
     if (int32_t s = check_proj_host(p)) return s;
-  if (!out_dtype_ok(out_dtype)) return EXL3_E_DTYPE;
+  if (!x_dtype_ok(x_dtype) || !out_dtype_ok(out_dtype)) return EXL3_E_DTYPE;
   if (topk < 1 || topk > EXL3_MAX_TOPK) return EXL3_E_ARG;
   if (capacity < 1) return EXL3_E_ARG;
   const int H = gate->in_features, I = gate->out_features, E = gate->num_experts;
@@ -207,7 +208,7 @@ int32_t validate_moe_device(const uint16_t *x, const exl3_proj *gate,
 }
 
 // Passes over the packed positions: rotate, gate/up, down, combine.
-int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
+int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t topk,
                     const exl3_proj *gate, const exl3_proj *up,
                     const exl3_proj *down, void *out, int32_t out_dtype,
                     const MoeLayout &L, void *ws, const int32_t *pair_of_pos,
@@ -236,6 +237,7 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
   auto rot_params = [&](int pass, int b) {
     RotParams rp{};
     rp.x = x;
+    rp.x_bf16 = x_dtype == EXL3_BF16;
     rp.H = H;
     rp.topk = topk;
     rp.suh[0] = gate->suh;
@@ -310,6 +312,7 @@ int32_t run_experts(const uint16_t *x, int32_t rows, int32_t topk,
     cp.yacc = at<float>(ws, L.yacc);
     cp.out = out;
     cp.out_f32 = out_dtype == EXL3_F32;
+    cp.out_bf16 = out_dtype == EXL3_BF16;
     return cp;
   };
 
@@ -424,14 +427,14 @@ size_t exl3_linear_workspace_size(int32_t rows, int32_t in_features, int32_t out
   return lin_layout(rows, in_features, out_features).total;
 }
 
-int32_t exl3_linear(const uint16_t *x, int32_t rows, const exl3_proj *proj, void *out,
-                    int32_t out_dtype, void *ws, size_t ws_bytes, void *stream) {
+int32_t exl3_linear(const uint16_t *x, int32_t x_dtype, int32_t rows, const exl3_proj *proj,
+                    void *out, int32_t out_dtype, void *ws, size_t ws_bytes, void *stream) {
   if (rows < 0) return EXL3_E_ARG;
   if (rows == 0) return EXL3_OK;
   if (!x || !out || !ws) return EXL3_E_NULL;
   if (int32_t s = check_proj_host(proj)) return s;
   if (proj->num_experts != 1) return EXL3_E_ARG;
-  if (!out_dtype_ok(out_dtype)) return EXL3_E_DTYPE;
+  if (!x_dtype_ok(x_dtype) || !out_dtype_ok(out_dtype)) return EXL3_E_DTYPE;
   if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return EXL3_E_ALIGN;
   if (ws_bytes < exl3_linear_workspace_size(rows, proj->in_features, proj->out_features))
     return EXL3_E_WORKSPACE;
@@ -445,6 +448,7 @@ int32_t exl3_linear(const uint16_t *x, int32_t rows, const exl3_proj *proj, void
   uint16_t *xt = at<uint16_t>(ws, LL.xt);
   RotParams rp{};
   rp.x = x;
+  rp.x_bf16 = x_dtype == EXL3_BF16;
   rp.H = proj->in_features;
   rp.suh[0] = proj->suh;
   rp.nproj = 1;
@@ -469,6 +473,7 @@ int32_t exl3_linear(const uint16_t *x, int32_t rows, const exl3_proj *proj, void
   g.ldo = proj->out_features;
   if (out_dtype == EXL3_F32) g.out_f32 = (float *)out;
   else g.out_h = (uint16_t *)out;
+  g.out_bf16 = out_dtype == EXL3_BF16;
   g.ctrl = ctrl;
   g.nacc = at<float>(ws, LL.nacc);
   g.ncnt = at<int32_t>(ws, LL.ncnt);
@@ -558,7 +563,8 @@ int32_t exl3_route_pack(const void *ids, int32_t ids_dtype, const void *w, int32
   return launch_pack(p, (hipStream_t)stream) == hipSuccess ? EXL3_OK : EXL3_E_LAUNCH;
 }
 
-int32_t exl3_moe_forward(const uint16_t *x, int32_t rows, const void *ids, int32_t ids_dtype,
+int32_t exl3_moe_forward(const uint16_t *x, int32_t x_dtype, int32_t rows, const void *ids,
+                         int32_t ids_dtype,
                          const void *w, int32_t w_dtype, int32_t topk, const exl3_proj *gate,
                          const exl3_proj *up, const exl3_proj *down, void *out,
                          int32_t out_dtype, int32_t capacity, int32_t num_active_hint,
@@ -566,7 +572,8 @@ int32_t exl3_moe_forward(const uint16_t *x, int32_t rows, const void *ids, int32
   (void)num_active_hint;
   if (rows < 0) return EXL3_E_ARG;
   if (rows == 0) return EXL3_OK;
-  if (int32_t s = validate_moe_common(x, rows, topk, gate, up, down, out, out_dtype, capacity, ws))
+  if (int32_t s = validate_moe_common(x, x_dtype, rows, topk, gate, up, down, out, out_dtype,
+                                      capacity, ws))
     return s;
   if (!ids || !w) return EXL3_E_NULL;
   if (ids_dtype != EXL3_I32 && ids_dtype != EXL3_I64) return EXL3_E_DTYPE;
@@ -616,11 +623,11 @@ int32_t exl3_moe_forward(const uint16_t *x, int32_t rows, const void *ids, int32
     ProfScope ps(st, EXL3_K_PACK);
     if (launch_pack(p, st) != hipSuccess) return EXL3_E_LAUNCH;
   }
-  return run_experts(x, rows, topk, gate, up, down, out, out_dtype, L, ws, p.pair_of_pos,
+  return run_experts(x, x_dtype, rows, topk, gate, up, down, out, out_dtype, L, ws, p.pair_of_pos,
                      p.pos_of_pair, p.weight_of_pos, p.offset, st, fuse ? &p : nullptr);
 }
 
-int32_t exl3_moe_additive(const uint16_t *x, int32_t rows, int32_t topk,
+int32_t exl3_moe_additive(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t topk,
                           const exl3_route_meta *meta, const exl3_proj *gate,
                           const exl3_proj *up, const exl3_proj *down, void *out,
                           int32_t out_dtype, int32_t capacity, int32_t num_active_hint,
@@ -628,7 +635,8 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t rows, int32_t topk,
   (void)num_active_hint;
   if (rows < 0) return EXL3_E_ARG;
   if (rows == 0) return EXL3_OK;
-  if (int32_t s = validate_moe_common(x, rows, topk, gate, up, down, out, out_dtype, capacity, ws))
+  if (int32_t s = validate_moe_common(x, x_dtype, rows, topk, gate, up, down, out, out_dtype,
+                                      capacity, ws))
     return s;
   if (!meta) return EXL3_E_NULL;
   void *mp[] = {meta->expert_offset, meta->pair_of_pos, meta->weight_of_pos, meta->pos_of_pair};
@@ -668,7 +676,8 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t rows, int32_t topk,
     ProfScope ps(st, EXL3_K_PACK);
     if (launch_pack(p, st) != hipSuccess) return EXL3_E_LAUNCH;
   }
-  return run_experts(x, rows, topk, gate, up, down, out, out_dtype, L, ws, meta->pair_of_pos,
+  return run_experts(x, x_dtype, rows, topk, gate, up, down, out, out_dtype, L, ws,
+                     meta->pair_of_pos,
                      meta->pos_of_pair, meta->weight_of_pos, meta->expert_offset, st);
 }
 

@@ -31,7 +31,8 @@ struct GemmParams {
   const int32_t *plan_tiles;
   // Epilogue.
   const uint16_t *suh_down;  // GATEUP: [E][I] (down input signs)
-  uint16_t *out_h;           // GATEUP: a~ [C][I]; LINEAR fp16 output
+  uint16_t *out_h;           // GATEUP: a~ [C][I]; LINEAR 16-bit output
+  int out_bf16;              // LINEAR: out_h holds bf16 (else fp16)
   float *out_f32;            // DOWN: d [C][H]; LINEAR fp32 output
   int64_t ldo;
   const float *weight_of_pos;  // DOWN
@@ -44,7 +45,8 @@ struct GemmParams {
 };
 
 struct RotParams {
-  const uint16_t *x;  // [rows][H] fp16
+  const uint16_t *x;  // [rows][H] fp16, or bf16 if x_bf16
+  int x_bf16;
   int H, topk;
   const uint16_t *suh[2];  // [E][H] per projection (suh[1] may be null)
   int nproj;
@@ -68,7 +70,8 @@ struct CombineParams {
   const float *d;  // [C][H]
   float *yacc;     // [rows][H]
   void *out;
-  int out_f32;     // 1: fp32 out, 0: fp16
+  int out_f32;     // 1: fp32 out, 0: 16-bit out
+  int out_bf16;    // 16-bit out is bf16 (else fp16)
 };
 
 struct PackParams {

@@ -1,4 +1,5 @@
-// Input rotation of one (item, 128-block) by one 16-lane group, shared by the
+// Input rotation of one (item, 128-block) by one 16-lane group (x in fp16 or
+// bf16, read exactly; x~ always rounded to fp16), shared by the
 // rotate kernel and the per-pass expert kernel (which rotates the next pass's
 // inputs while its own down work finishes).
 // x~ = fp16_rne(H128(x * suh) / sqrt(128)) for the GEMM A operands, stored in
@@ -36,8 +37,12 @@ __device__ __forceinline__ void rotate_block(const RotParams &p, int item, int b
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t xw = xv[j], sw = sv[pj][j];
-      v[2 * j] = f16_bits_to_f32((uint16_t)(xw & 0xFFFFu)) * f16_bits_to_f32((uint16_t)(sw & 0xFFFFu));
-      v[2 * j + 1] = f16_bits_to_f32((uint16_t)(xw >> 16)) * f16_bits_to_f32((uint16_t)(sw >> 16));
+      const float x0 = p.x_bf16 ? bf16_bits_to_f32((uint16_t)(xw & 0xFFFFu))
+                                : f16_bits_to_f32((uint16_t)(xw & 0xFFFFu));
+      const float x1 = p.x_bf16 ? bf16_bits_to_f32((uint16_t)(xw >> 16))
+                                : f16_bits_to_f32((uint16_t)(xw >> 16));
+      v[2 * j] = x0 * f16_bits_to_f32((uint16_t)(sw & 0xFFFFu));
+      v[2 * j + 1] = x1 * f16_bits_to_f32((uint16_t)(sw >> 16));
     }
     fwht128_lane8(v);
     uint16_t h[8];

@@ -17,7 +17,12 @@ LIB_PATH = os.path.join(_HERE, "libexl3moe.so")
 F16, BF16, F32, I32, I64 = 1, 2, 3, 4, 5
 _DT = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32,
        torch.int32: I32, torch.int64: I64}
-_OUT = {F16: torch.float16, F32: torch.float32}
+_OUT = {F16: torch.float16, BF16: torch.bfloat16, F32: torch.float32}
+
+
+def _dt(t):
+    """Library dtype code of a tensor; 0 (rejected by the library) if it has none."""
+    return _DT.get(t.dtype, 0)
 
 
 class Exl3Error(RuntimeError):
@@ -52,13 +57,14 @@ _SIGS = {
     "exl3_route_pack": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                ctypes.POINTER(MetaC), _vp]),
     "exl3_linear_workspace_size": (_sz, [_i32, _i32, _i32]),
-    "exl3_linear": (_i32, [_vp, _i32, ctypes.POINTER(ProjC), _vp, _i32, _vp, _sz, _vp]),
+    "exl3_linear": (_i32, [_vp, _i32, _i32, ctypes.POINTER(ProjC), _vp, _i32, _vp, _sz,
+                           _vp]),
     "exl3_moe_workspace_size": (_sz, [_i32] * 6),
-    "exl3_moe_forward": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _i32,
+    "exl3_moe_forward": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32,
                                 ctypes.POINTER(ProjC), ctypes.POINTER(ProjC),
                                 ctypes.POINTER(ProjC), _vp, _i32, _i32, _i32, _vp, _sz,
                                 _vp]),
-    "exl3_moe_additive": (_i32, [_vp, _i32, _i32, ctypes.POINTER(MetaC),
+    "exl3_moe_additive": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(MetaC),
                                  ctypes.POINTER(ProjC), ctypes.POINTER(ProjC),
                                  ctypes.POINTER(ProjC), _vp, _i32, _i32, _i32, _vp, _sz,
                                  _vp]),
@@ -204,8 +210,8 @@ def exl3_linear(x, proj, out_dtype=torch.float32, out=None, ws=None):
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     pc = proj.cstruct()
-    _check(lib().exl3_linear(_p(x), rows, ctypes.byref(pc), _p(out), _DT[out.dtype], _p(ws),
-                             ws.numel(), _stream()))
+    _check(lib().exl3_linear(_p(x), _dt(x), rows, ctypes.byref(pc), _p(out), _DT[out.dtype],
+                             _p(ws), ws.numel(), _stream()))
     return out
 
 
@@ -231,9 +237,10 @@ def exl3_moe_forward(x, ids, w, gate, up, down, capacity, out_dtype=torch.float3
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
-    _check(lib().exl3_moe_forward(_p(x), rows, _p(ids), _DT[ids.dtype], _p(w), _DT[w.dtype],
-                                  topk, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
-                                  _p(out), _DT[out.dtype], capacity, num_active_hint,
+    _check(lib().exl3_moe_forward(_p(x), _dt(x), rows, _p(ids), _DT[ids.dtype], _p(w),
+                                  _DT[w.dtype], topk, ctypes.byref(g), ctypes.byref(u),
+                                  ctypes.byref(d), _p(out), _DT[out.dtype], capacity,
+                                  num_active_hint,
                                   _p(ws), ws.numel(), _stream()))
     return out
 
@@ -249,9 +256,9 @@ def exl3_moe_additive(x, topk, meta, gate, up, down, capacity, out_dtype=torch.f
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
     mc = _meta_c(meta)
-    _check(lib().exl3_moe_additive(_p(x), rows, topk, ctypes.byref(mc), ctypes.byref(g),
-                                   ctypes.byref(u), ctypes.byref(d), _p(out), _DT[out.dtype],
-                                   capacity, num_active_hint, _p(ws), ws.numel(), _stream()))
+    _check(lib().exl3_moe_additive(_p(x), _dt(x), rows, topk, ctypes.byref(mc),
+                                   ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), _p(out),
+                                   _DT[out.dtype], capacity, num_active_hint, _p(ws), ws.numel(), _stream()))
     return out
 
 
