@@ -85,10 +85,12 @@ static_assert(WideLds<EPI_GATEUP>::kBytes <= 80 * 1024, "two workgroups per CU")
 static_assert(WideLds<EPI_LINEAR>::kBytes <= 80 * 1024, "two workgroups per CU");
 
 // 16-byte chunk swizzle of A row r (0..15 inside its 16-row block); a row is
-// 64 bytes (4 chunks). The 8 lanes that read (rows 0..7 or 8..15, one chunk
-// index) hit 8 distinct 16-byte groups of a 128-byte bank window, and the 16
-// lanes of rows 0..15 hit 16 distinct groups of a 256-byte window.
-__device__ __forceinline__ int a_swizzle(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// 64 bytes (4 chunks), and lane (g, r) of an A-fragment read takes chunk g of
+// row r. gfx950 serves a 64-lane ds_read_b128 as 4 groups of 16 lanes over 64
+// four-byte banks; with this swizzle the LDS bank-conflict counter reads zero
+// for the fragment reads (without it, or with (r>>1)^(r>>3), every read costs
+// 4 extra cycles).
+__device__ __forceinline__ int a_swizzle(int r) { return (r >> 1) & 3; }
 
 // 16-byte-per-lane global->LDS copy: lane L reads sbase + voff and writes
 // LDS byte m0 + 16 L. The wave's LDS destination goes through m0.
