@@ -203,7 +203,7 @@ def cpu_baseline(wl, synth, rows=(0, 1)):
 
 
 KERNEL_SOURCES = ("gemm_wide.hip", "gemm_shared.hpp", "common.hpp", "kernels.hpp",
-                  "rotate_dev.hpp")
+                  "rotate_dev.hpp", "combine_dev.hpp")
 
 
 def kernel_source_sha():
