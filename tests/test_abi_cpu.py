@@ -104,3 +104,38 @@ def test_host_pointers_are_rejected_as_not_device():
     # everything valid on the host side; the device check must fail (no GPU
     # here, or host memory on a GPU machine) without launching anything
     assert _fwd() == -5
+
+
+def _lin(x_dtype=exl3.F16, out_dtype=exl3.F32, proj=None, rows=3, x=16384, out=32768,
+         ws=65536, ws_bytes=1 << 40):
+    proj = proj or _proj(num_experts=1)
+    return exl3.lib().exl3_linear(ctypes.c_void_p(x), x_dtype, rows, ctypes.byref(proj),
+                                  ctypes.c_void_p(out), out_dtype, ctypes.c_void_p(ws),
+                                  ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x_dtype=exl3.F32), -2), (dict(x_dtype=exl3.I64), -2), (dict(out_dtype=exl3.I32), -2),
+    (dict(x=0), -1), (dict(proj=_proj(num_experts=2)), -7), (dict(x=16386), -4),
+    (dict(ws_bytes=1), -6), (dict(rows=-2), -7),
+    # accepted dtypes reach the device check (host pointers here)
+    (dict(x_dtype=exl3.BF16, out_dtype=exl3.BF16), -5), (dict(out_dtype=exl3.F16), -5),
+])
+def test_linear_validates_dtypes_and_arguments_on_the_host(kw, code):
+    assert _lin(**kw) == code
+
+
+def _add(x_dtype=exl3.F16, out_dtype=exl3.F32, meta_ptr=8192):
+    g, u, d = _proj(), _proj(), _proj(in_features=512, out_features=256)
+    mc = exl3.MetaC(*([ctypes.c_void_p(meta_ptr)] * len(exl3.MetaC._fields_)))
+    return exl3.lib().exl3_moe_additive(
+        ctypes.c_void_p(16384), x_dtype, 4, 2, ctypes.byref(mc), ctypes.byref(g),
+        ctypes.byref(u), ctypes.byref(d), ctypes.c_void_p(32768), out_dtype, 8, -1,
+        ctypes.c_void_p(65536), 1 << 40, None)
+
+
+@pytest.mark.parametrize("xdt,odt,code", [
+    (exl3.F32, exl3.F32, -2), (0, exl3.F32, -2), (exl3.F16, exl3.I64, -2),
+    (exl3.BF16, exl3.F32, -5), (exl3.BF16, exl3.BF16, -5), (exl3.F16, exl3.F16, -5)])
+def test_additive_validates_dtypes_on_the_host(xdt, odt, code):
+    assert _add(xdt, odt) == code
