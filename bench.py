@@ -6,7 +6,10 @@ already resident in HBM. The headline workload is the mixed-width prefill
 layer (192 experts, top-8, hidden 6144, intermediate 2048, K per expert in
 {3,4,5,6,8}, 3072 rows, Zipf(1.2) routing, capacity 2048 pairs). The decode
 layer (128 experts, top-8, hidden 4096, intermediate 1536, K=4) at 1 and 32
-rows is reported alongside, timed by hipGraph replay over rotating routings.
+rows is reported alongside, timed by hipGraph replay over rotating routings,
+and so are the additive layer (256 experts, base K=3 plus a K=2 residual
+stage, 128 rows) and the plain 4096 -> 4096 linear at K = 2, 3, 4, 8 and 1,
+32, 2048 rows, both with cold weights.
 
 Prints one JSON line. ``--gpus N`` with N > 1 is refused: this build runs on
 one GPU.
@@ -176,6 +179,97 @@ def run_decode(args, torch, exl3, synth, M, groups=16, **over):
     }
 
 
+def run_linear(args, torch, exl3, synth, Ks=(2, 3, 4, 8), Ms=(1, 32, 2048), reps=48):
+    """The plain linear 4096 -> 4096 (exl3_linear: rotation + GEMM launch) at
+    each width K and row count M, weights cold: calls rotate over enough
+    copies of the trellis (>= 600 MB) that none is cache-resident. Bytes are
+    the trellis plus fp16 rows in and out; flops 2 x M x in x out."""
+    res = {}
+    for K in Ks:
+        p, x = synth.linear_workload(K, max(Ms))
+        tbytes = p.in_features * p.out_features * K // 8
+        ncopy = max(2, -(-600_000_000 // tbytes))
+        copies = [exl3.DeviceProj(p, "cuda") for _ in range(ncopy)]
+        xd = exl3.f16_tensor(x)
+        for M in Ms:
+            out = torch.empty(M, p.out_features, dtype=torch.float16, device="cuda")
+            ws = torch.empty(max(256, exl3.linear_workspace_size(M, p.in_features,
+                                                                 p.out_features)),
+                             dtype=torch.uint8, device="cuda")
+            for c in copies[:4]:
+                exl3.exl3_linear(xd[:M], c, out=out, ws=ws)
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(reps):
+                exl3.exl3_linear(xd[:M], copies[i % ncopy], out=out, ws=ws)
+            b.record()
+            torch.cuda.synchronize()
+            us = 1000.0 * a.elapsed_time(b) / reps
+            nbytes = tbytes + M * (p.in_features + p.out_features) * 2
+            flops = 2.0 * M * p.in_features * p.out_features
+            res["K%d_M%d" % (K, M)] = {
+                "us": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+                "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                "tflops": flops / (us * 1e-6) / 1e12,
+                "mfma_frac": flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS}
+        del copies
+        torch.cuda.empty_cache()
+    return res
+
+
+def run_additive(args, torch, exl3, synth, reps=20):
+    """The additive layer (256 experts, top-8, 4096/2048, 128 rows, base K=3
+    plus one K=2 residual stage per projection, 30% of the residual scales
+    zero): exl3_moe_additive on a route pack made once. Its trellis (over
+    3 GB) exceeds every cache. Bytes are the trellis of the stages that run
+    (active experts, nonzero scales) plus rows in, a~ and d traffic."""
+    wl = synth.moe_workload("additive", materialize=False)
+    gate, up, down = (exl3.DeviceProj(p, "cuda", words_fn=synth.realize_words)
+                      for p in (wl.gate, wl.up, wl.down))
+    x, ids, w = exl3.device_inputs(wl, "cuda")
+    meta = exl3.exl3_route_pack(ids, w, wl.num_experts)
+    cap = wl.rows * wl.topk
+    out = torch.empty(wl.rows, wl.hidden, dtype=torch.float16, device="cuda")
+    ws = torch.empty(exl3.moe_workspace_size(wl.rows, wl.topk, wl.num_experts, wl.hidden,
+                                             wl.intermediate, cap),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        exl3.exl3_moe_additive(x, wl.topk, meta, gate, up, down, cap, out=out, ws=ws)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * a.elapsed_time(b) / reps
+    with exl3.Profile(max_launches=8 * 4) as prof:
+        for _ in range(4):
+            call()
+        torch.cuda.synchronize()
+    kst = _kernel_stats(prof.records)
+    active = np.unique(wl.ids[(wl.ids >= 0) & (wl.ids < wl.num_experts)])
+    tbytes = 0
+    for pr in (wl.gate, wl.up, wl.down):
+        for t in range(len(pr.words)):
+            for e in active:
+                if float(pr.scale[t][e]) != 0.0:
+                    tbytes += pr.in_features * pr.out_features * int(pr.bits[t][e]) // 8
+    P = int(np.sum((wl.ids >= 0) & (wl.ids < wl.num_experts)))
+    nbytes = tbytes + wl.rows * wl.hidden * 2 + P * (wl.intermediate * 2 * 2 + wl.hidden * 4 * 2)
+    return {"rows": wl.rows, "us": us, "tokens_per_s": wl.rows / (us * 1e-6),
+            "kernels": kst, "algorithmic_bytes": nbytes, "trellis_bytes": tbytes,
+            "layer_GBps": nbytes / (us * 1e-6) / 1e9,
+            "layer_hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
 def cpu_baseline(wl, synth, rows=(0, 1)):
     """The float64 oracle on a bounded sample of the prefill workload: whole
     tokens (rows 0 and 1, all 8 routed pairs each) through the layer, expert
@@ -266,6 +360,10 @@ def main():
         for M in (1, 32):
             _log("decode M=%d" % M)
             extra["decode_M%d" % M] = run_decode(args, torch, exl3, synth, M)
+        _log("additive layer")
+        extra["additive"] = run_additive(args, torch, exl3, synth)
+        _log("linear 4096 -> 4096")
+        extra["linear"] = run_linear(args, torch, exl3, synth)
     if not args.no_tp:
         # one GPU's share under 4-way tensor parallelism: intermediate / 4
         _log("tp4 shard: decode M=32, intermediate 384")
