@@ -297,12 +297,13 @@ def cpu_baseline(wl, synth, rows=(0, 1)):
 
 
 KERNEL_SOURCES = ("gemm_wide.hip", "gemm_shared.hpp", "common.hpp", "kernels.hpp",
-                  "rotate_dev.hpp", "combine_dev.hpp")
+                  "rotate_dev.hpp", "combine_dev.hpp", "route_pack.hip", "host.cpp")
 
 
 def kernel_source_sha():
     """SHA-256 over the sources of the 128-row GEMM (the prefill's dominant
-    kernel): a committed counter summary applies only to this exact code."""
+    kernel), its plan builder and the host code that decides what one launch
+    holds: a committed counter summary applies only to this exact code."""
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:

@@ -218,14 +218,22 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t x_dtype, int32_t rows, int3
  *   meta        forward only: count[E], offset[E+1], pair_of_pos[P],
  *               weight_of_pos[P], pos_of_pair[P], num_active[1] (P = pairs)
  *   expert_of_pos int32[P]
- *   plan        per pass: int32 ntiles + tiles of {expert, start, len}
- *   xt          fp16 [C][2][hidden]  rotated gate/up inputs of the pass
- *   at          fp16 [C][intermediate] rotated down inputs a~ of the pass
- *   d           fp32 [C][hidden]     weighted per-pair down outputs
+ *   Passes are grouped into launch units of G = plan_group passes when the
+ *   call runs several passes on 128-row tiles (rows * topk >= 64 *
+ *   num_experts): G = 4 from 8 passes, 2 from 4 passes, else 1. A unit
+ *   covers packed positions [u G C, (u + 1) G C); spans are still cut every
+ *   C positions. The scratch for such calls is therefore 2 G C rows of xt,
+ *   at and d (about 1 GB for 3072 rows x top-8, hidden 6144, intermediate
+ *   2048 at C = 2048).
+ *   plan        per unit: int32 ntiles + tiles of {expert, start, len}
+ *               (start relative to the unit; slots: G * plan_slots)
+ *   xt          fp16 [G C][2][hidden]  rotated gate/up inputs of the unit
+ *   at          fp16 [G C][intermediate] rotated down inputs a~ of the unit
+ *   d           fp32 [G C][hidden]     weighted per-pair down outputs
  *               (xt, at and d each hold two such buffers, the second one
  *               256-byte aligned after the first, when the call runs several
  *               passes on 128-row tiles (rows * topk >= 64 * num_experts and
- *               capacity < rows * topk): pass p uses buffer p % 2)
+ *               capacity < rows * topk): unit u uses buffer u % 2)
  *   yacc        fp32 [rows][hidden]  running row sums across passes
  *   (then private scratch of the 16-row tile path, used when rows * topk <
  *   64 * num_experts: pre-rotation fp32 sums [C][max(2 intermediate,
@@ -236,7 +244,7 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t x_dtype, int32_t rows, int3
  */
 typedef struct exl3_moe_layout_t {
   size_t ctrl, meta, expert_of_pos, plan, xt, at, d, yacc, total;
-  int32_t passes, plan_slots;
+  int32_t passes, plan_slots, plan_group;
 } exl3_moe_layout_t;
 int32_t exl3_moe_layout(int32_t rows, int32_t topk, int32_t num_experts,
                         int32_t hidden, int32_t intermediate, int32_t capacity,

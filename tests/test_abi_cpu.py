@@ -42,15 +42,24 @@ def test_workspace_sizes():
     a = L.exl3_moe_workspace_size(3072, 8, 192, 6144, 2048, 2048)
     b = L.exl3_moe_workspace_size(3072, 8, 192, 6144, 2048, 4096)
     c = L.exl3_moe_workspace_size(3072, 8, 192, 6144, 2048, 10 ** 6)
-    assert 0 < a < b <= c
+    assert 0 < a and 0 < b and 0 < c
     # capacity beyond rows*topk does not grow the workspace
     assert c == L.exl3_moe_workspace_size(3072, 8, 192, 6144, 2048, 24576)
     assert L.exl3_moe_workspace_size(4, 2, 8, 200, 512, 8) == 0  # not a multiple of 128
     lay = exl3.moe_layout(3072, 8, 192, 6144, 2048, 2048)
-    assert lay.passes == 12
+    assert lay.passes == 12 and lay.plan_group == 4
     offs = [lay.ctrl, lay.meta, lay.expert_of_pos, lay.plan, lay.xt, lay.at, lay.d, lay.yacc]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.total == a
+    # two buffers (by unit parity) of group * capacity rows each
+    rows = lay.plan_group * 2048
+    assert lay.at - lay.xt >= 2 * rows * 2 * 6144 * 2
+    assert lay.d - lay.at >= 2 * rows * 2048 * 2
+    assert lay.yacc - lay.d >= 2 * rows * 6144 * 4
+    # a single pass needs a single buffer of every pair
+    one = exl3.moe_layout(3072, 8, 192, 6144, 2048, 10 ** 6)
+    assert (one.passes, one.plan_group) == (1, 1)
+    assert one.at - one.xt >= 24576 * 2 * 6144 * 2
     assert L.exl3_linear_workspace_size(7, 4096, 4096) >= 7 * 4096 * 2
 
 
@@ -139,3 +148,20 @@ def _add(x_dtype=exl3.F16, out_dtype=exl3.F32, meta_ptr=8192):
     (exl3.BF16, exl3.F32, -5), (exl3.BF16, exl3.BF16, -5), (exl3.F16, exl3.F16, -5)])
 def test_additive_validates_dtypes_on_the_host(xdt, odt, code):
     assert _add(xdt, odt) == code
+
+
+@pytest.mark.parametrize("rows,cap,passes,group", [
+    (3072, 2048, 12, 4), (3072, 10 ** 6, 1, 1), (3072, 12288, 2, 1), (3072, 8192, 3, 1),
+    (3072, 6144, 4, 2), (3072, 4916, 5, 2), (3072, 3511, 7, 2), (3072, 3072, 8, 4)])
+def test_pipelined_passes_are_grouped_per_launch_unit(rows, cap, passes, group):
+    # 128-row tiles (rows * topk >= 64 * experts): 4 passes share a launch
+    # unit from 8 passes on, 2 from 4 (one plan, buffers of group * capacity)
+    lay = exl3.moe_layout(rows, 8, 192, 6144, 2048, cap)
+    assert (lay.passes, lay.plan_group) == (passes, group)
+    one = exl3.moe_layout(rows, 8, 192, 6144, 2048, cap if group == 1 else 10 ** 6)
+    assert lay.total > 0 and one.total > 0
+
+
+def test_small_tiles_never_group_passes():
+    lay = exl3.moe_layout(64, 8, 128, 4096, 1536, 16)  # 16-row tiles, 32 passes
+    assert lay.passes == 32 and lay.plan_group == 1

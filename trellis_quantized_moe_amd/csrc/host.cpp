@@ -121,6 +121,10 @@ struct MoeLayout {
   size_t ctrl, count, offset, pair_of_pos, weight_of_pos, pos_of_pair, num_active, status;
   size_t expert_of_pos, plan, xt, at, d, yacc, nacc, ncnt, total;
   int passes, slots, cap, ncnt_ints;
+  // A launch unit is `group` consecutive passes (on the pipelined path 4
+  // with 8+ passes, 2 with 4-7, else 1): one plan, one buffer set of
+  // gcap = group * cap rows. Spans are still cut every `cap` pairs.
+  int group, units, gcap;
   bool wide, pipe;
   size_t xt_bytes, at_bytes, d_bytes;  // one buffer each (pipe: two of each)
 };
@@ -148,15 +152,23 @@ MoeLayout moe_layout(int32_t rows, int32_t topk, int32_t E, int32_t H, int32_t I
   L.num_active = take(4);
   L.status = take(4);
   L.expert_of_pos = take(4 * (size_t)P);
-  L.plan = take(4 * (size_t)L.passes * (1 + 3 * (size_t)L.slots));
   L.wide = P > 0 && moe_wide(P, E);
   // 128-row tiles over several passes run pipelined across launches, with
-  // two buffers (by pass parity) of x~, a~ and d
+  // two buffers (by unit parity) of x~, a~ and d. A launch unit holds 4
+  // passes from 8 passes on, 2 from 4: more work per launch to spread over
+  // the CUs and fewer launch tails, for buffers of group * capacity rows
+  // (measured on the 3072-row prefill at capacity 2048: 4.37 / 4.20 / 4.05
+  // ms per layer with 1 / 2 / 4 passes per unit)
   L.pipe = L.wide && L.passes >= 2;
+  L.group = !L.pipe ? 1 : L.passes >= 8 ? 4 : L.passes >= 4 ? 2 : 1;
+  L.units = (L.passes + L.group - 1) / L.group;
+  L.gcap = L.group * L.cap;
+  L.plan = take(4 * (size_t)L.units * (1 + 3 * (size_t)L.group * L.slots));
   const size_t nbuf = L.pipe ? 2 : 1;
-  L.xt_bytes = align_up(2 * (size_t)C * 2 * H);
-  L.at_bytes = align_up(2 * (size_t)C * I);
-  L.d_bytes = align_up(4 * (size_t)C * H);
+  const size_t G = (size_t)L.gcap;
+  L.xt_bytes = align_up(2 * G * 2 * H);
+  L.at_bytes = align_up(2 * G * I);
+  L.d_bytes = align_up(4 * G * H);
   L.xt = take(nbuf * L.xt_bytes);
   L.at = take(nbuf * L.at_bytes);
   L.d = take(nbuf * L.d_bytes);
@@ -220,13 +232,23 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
   int32_t *ctrl = at<int32_t>(ws, L.ctrl);
   const bool wide = L.wide;
   const int bm = wide ? kBMWide : kBM;
-  auto npos_of = [&](int pass) { return (int)std::min<int64_t>(L.cap, P - (int64_t)pass * L.cap); };
-  auto tiles_of = [&](int pass) {
-    const int npos = npos_of(pass);
-    return std::min(E, npos) + (npos + bm - 1) / bm;
+  // Launch units of L.group passes (see MoeLayout): u covers packed
+  // positions [u * gcap, (u + 1) * gcap), with spans still cut every cap.
+  auto npos_of = [&](int u) {
+    return (int)std::min<int64_t>(L.gcap, P - (int64_t)u * L.gcap);
   };
-  auto plan_of = [&](int pass) {
-    return at<int32_t>(ws, L.plan) + (size_t)pass * (1 + 3 * (size_t)L.slots);
+  auto tiles_of = [&](int u) {  // bound on the unit's plan tiles
+    int t = 0;
+    for (int j = 0; j < L.group; ++j) {
+      const int64_t pass = (int64_t)u * L.group + j;
+      if (pass >= L.passes) break;
+      const int np = (int)std::min<int64_t>(L.cap, P - pass * L.cap);
+      t += std::min(E, np) + (np + bm - 1) / bm;
+    }
+    return t;
+  };
+  auto plan_of = [&](int u) {
+    return at<int32_t>(ws, L.plan) + (size_t)u * (1 + 3 * (size_t)L.group * L.slots);
   };
   uint16_t *xt0 = at<uint16_t>(ws, L.xt), *at0 = at<uint16_t>(ws, L.at);
   float *d0 = at<float>(ws, L.d);
@@ -246,7 +268,7 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
     rp.pair_of_pos = pair_of_pos;
     rp.expert_of_pos = at<int32_t>(ws, L.expert_of_pos);
     rp.total_valid = total_valid;
-    rp.pass_base = pass * L.cap;
+    rp.pass_base = pass * L.gcap;
     rp.pairs = (int)P;
     rp.nitems = npos_of(pass);
     rp.xt = xt_buf(b);
@@ -290,7 +312,7 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
     dn.out_f32 = d_buf(b);
     dn.ldo = H;
     dn.weight_of_pos = weight_of_pos;
-    dn.pass_base = pass * L.cap;
+    dn.pass_base = pass * L.gcap;
     dn.ctrl = ctrl;
     dn.nacc = at<float>(ws, L.nacc);
     dn.ncnt = at<int32_t>(ws, L.ncnt);
@@ -306,8 +328,8 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
     cp.pair_of_pos = pair_of_pos;
     cp.pos_of_pair = pos_of_pair;
     cp.total_valid = total_valid;
-    cp.pass_base = pass * L.cap;
-    cp.pass_end = pass * L.cap + L.cap;
+    cp.pass_base = pass * L.gcap;
+    cp.pass_end = pass * L.gcap + L.gcap;
     cp.d = d_buf(b);
     cp.yacc = at<float>(ws, L.yacc);
     cp.out = out;
@@ -317,15 +339,15 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
   };
 
   if (L.pipe) {
-    // launch k: gate/up of pass k, down of k - 1, rotation of k + 1, combine
-    // of k - 2; pass q uses the buffers of parity q & 1
+    // launch k: gate/up of unit k, down of k - 1, rotation of k + 1, combine
+    // of k - 2; unit q uses the buffers of parity q & 1
     {
       ProfScope ps(st, EXL3_K_ROTATE);
       if (launch_rotate(rot_params(0, 0), st) != hipSuccess) return EXL3_E_LAUNCH;
     }
-    for (int k = 0; k <= L.passes + 1; ++k) {
-      const bool has_gu = k < L.passes, has_dn = k >= 1 && k <= L.passes;
-      const bool has_rn = k + 1 < L.passes, has_cb = k >= 2;
+    for (int k = 0; k <= L.units + 1; ++k) {
+      const bool has_gu = k < L.units, has_dn = k >= 1 && k <= L.units;
+      const bool has_rn = k + 1 < L.units, has_cb = k >= 2;
       const GemmParams g = has_gu ? gu_params(k, k & 1) : GemmParams{};
       const GemmParams dn = has_dn ? dn_params(k - 1, (k - 1) & 1) : GemmParams{};
       const RotParams rn = has_rn ? rot_params(k + 1, (k + 1) & 1) : RotParams{};
@@ -339,8 +361,8 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
     return EXL3_OK;
   }
 
-  // otherwise: pass by pass (128-row tiles: a single pass)
-  for (int pass = 0; pass < L.passes; ++pass) {
+  // otherwise: pass by pass, one pass per unit (128-row tiles: a single pass)
+  for (int pass = 0; pass < L.units; ++pass) {
     const int npos = npos_of(pass);
     const int tiles = tiles_of(pass);
     if (fused_pack && pass == 0) {  // pack, plan and this rotation in one launch
@@ -506,6 +528,7 @@ int32_t exl3_moe_layout(int32_t rows, int32_t topk, int32_t num_experts, int32_t
   out->total = L.total;
   out->passes = L.passes;
   out->plan_slots = L.slots;
+  out->plan_group = L.group;
   return EXL3_OK;
 }
 
@@ -610,6 +633,7 @@ int32_t exl3_moe_forward(const uint16_t *x, int32_t x_dtype, int32_t rows, const
   p.passes = L.passes;
   p.capacity = L.cap;
   p.slots = L.slots;
+  p.group = L.group;
   p.bm = moe_wide((int64_t)rows * topk, E) ? kBMWide : kBM;
   p.out = out;
   p.out_f32 = out_dtype == EXL3_F32;
@@ -665,6 +689,7 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t x_dtype, int32_t rows, int3
   p.passes = L.passes;
   p.capacity = L.cap;
   p.slots = L.slots;
+  p.group = L.group;
   p.bm = moe_wide((int64_t)rows * topk, E) ? kBMWide : kBM;
   p.out = out;
   p.out_f32 = out_dtype == EXL3_F32;

@@ -87,8 +87,9 @@ struct PackParams {
   int do_pack, do_plan;
   // plan outputs
   int32_t *expert_of_pos;
-  int32_t *plan;  // per pass: [1 + 3 * slots]
+  int32_t *plan;  // per unit of `group` passes: [1 + 3 * group * slots]
   int passes, capacity, slots, bm;
+  int group;      // passes per plan (tiles of pass j of a unit start j * capacity rows in)
   // unrouted rows get zero output
   void *out;
   int out_f32, H;

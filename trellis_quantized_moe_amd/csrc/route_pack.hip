@@ -117,11 +117,13 @@ constexpr int kPackBatch = 8;  // rounds whose loads are issued together
 // dispatch order, where each gets a CU of its own before the light ones
 // fill the second slots; the order never changes a result. s_off: the
 // expert offsets (E + 1, nondecreasing), kept = s_off[E].
-__device__ void plan_one_pass(const PackParams &p, const int *s_off, int E, int kept, int pass,
-                              int lane) {
+// Tiles of one pass, appended to `plan` at tile index `base`, their first
+// rows offset by `roff` (the pass's place in its launch unit). Returns the
+// pass's tile count; the caller writes the unit's count.
+__device__ int plan_one_pass(const PackParams &p, const int *s_off, int E, int kept, int pass,
+                             int lane, int32_t *plan, int base, int roff) {
   const int pb = pass * p.capacity;
   const int pe = (int)min((int64_t)pb + p.capacity, (int64_t)kept);
-  int32_t *plan = p.plan + (int64_t)pass * (1 + 3 * p.slots);
   int total = 0;
   if (pb < pe) {
     const int e_lo = expert_at(s_off, E, pb), e_hi = expert_at(s_off, E, pe - 1);
@@ -143,11 +145,11 @@ __device__ void plan_one_pass(const PackParams &p, const int *s_off, int E, int 
         const int y = __shfl_up(x, d, 64);
         if (lane >= d) x += y;
       }
-      const int slot0 = total + x - nf;
+      const int slot0 = base + total + x - nf;
       for (int t = 0; t < nf; ++t) {
         int32_t *d = plan + 1 + 3 * (slot0 + t);
         d[0] = e;
-        d[1] = lo - pb + t * bm;
+        d[1] = roff + lo - pb + t * bm;
         d[2] = bm;
       }
       total += __shfl(x, 63, 64);
@@ -182,16 +184,30 @@ __device__ void plan_one_pass(const PackParams &p, const int *s_off, int E, int 
           }
       }
       if (rows > 0) {
-        int32_t *d = plan + 1 + 3 * (nfull + rank);
+        int32_t *d = plan + 1 + 3 * (base + nfull + rank);
         d[0] = e;
-        d[1] = lo - pb + (hi - lo) / bm * bm;
+        d[1] = roff + lo - pb + (hi - lo) / bm * bm;
         d[2] = rows;
       }
       npart += __popcll(has);
     }
     total = nfull + npart;
   }
-  if (lane == 0) plan[0] = total;
+  return total;
+}
+
+// Plans of every launch unit (p.group consecutive passes), one wave per unit.
+__device__ void plan_units(const PackParams &p, const int *s_off, int E, int kept, int w,
+                           int nw, int lane) {
+  const int G = max(p.group, 1);
+  const int units = (p.passes + G - 1) / G;
+  for (int u = w; u < units; u += nw) {
+    int32_t *plan = p.plan + (int64_t)u * (1 + 3 * (int64_t)G * p.slots);
+    int n = 0;
+    for (int j = 0; j < G && u * G + j < p.passes; ++j)
+      n += plan_one_pass(p, s_off, E, kept, u * G + j, lane, plan, n, j * p.capacity);
+    if (lane == 0) plan[0] = n;
+  }
 }
 
 __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
@@ -329,7 +345,7 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
   }
 
   // a4: one wave per pass
-  for (int pass = w; pass < p.passes; pass += kPackWaves) plan_one_pass(p, s_off, E, kept, pass, lane);
+  plan_units(p, s_off, E, kept, w, kPackWaves, lane);
 
   // rows whose pairs were all dropped produce zeros: one row per thread to
   // find them (rare), then the row is cleared by that thread. A pack that
@@ -447,7 +463,7 @@ __device__ void pack_small(const PackParams &p) {
   if (!p.do_plan) return;
   if (lane == 0 && p.ctrl) p.ctrl[1] = 0;  // bad stage entries
   for (int i = lane; i < p.nzero; i += 64) p.zero[i] = 0;
-  plan_one_pass(p, s_off, p.E, r.kept, 0, lane);  // one pass: capacity >= pairs
+  plan_units(p, s_off, p.E, r.kept, 0, 1, lane);  // one pass: capacity >= pairs
   // rows whose pairs were all dropped produce zeros
   if (p.out && r.dropped > 0) {
     for (int row = 0; row < p.rows; ++row) {

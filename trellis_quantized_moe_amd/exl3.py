@@ -46,7 +46,8 @@ class MetaC(ctypes.Structure):
 class LayoutC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("ctrl", "meta", "expert_of_pos", "plan", "xt", "at", "d", "yacc",
-                 "total")] + [("passes", ctypes.c_int32), ("plan_slots", ctypes.c_int32)]
+                 "total")] + [("passes", ctypes.c_int32), ("plan_slots", ctypes.c_int32),
+                              ("plan_group", ctypes.c_int32)]
 
 
 _lib = None
