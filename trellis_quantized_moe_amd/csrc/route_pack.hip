@@ -120,6 +120,8 @@ constexpr int kPackBatch = 8;  // rounds whose loads are issued together
 // Tiles of one pass, appended to `plan` at tile index `base`, their first
 // rows offset by `roff` (the pass's place in its launch unit). Returns the
 // pass's tile count; the caller writes the unit's count.
+// With WRITE false only the count is computed (no stores, no sort).
+template <bool WRITE = true>
 __device__ int plan_one_pass(const PackParams &p, const int *s_off, int E, int kept, int pass,
                              int lane, int32_t *plan, int base, int roff) {
   const int pb = pass * p.capacity;
@@ -146,7 +148,7 @@ __device__ int plan_one_pass(const PackParams &p, const int *s_off, int E, int k
         if (lane >= d) x += y;
       }
       const int slot0 = base + total + x - nf;
-      for (int t = 0; t < nf; ++t) {
+      for (int t = 0; WRITE && t < nf; ++t) {
         int32_t *d = plan + 1 + 3 * (slot0 + t);
         d[0] = e;
         d[1] = roff + lo - pb + t * bm;
@@ -173,7 +175,7 @@ __device__ int plan_one_pass(const PackParams &p, const int *s_off, int E, int k
       const int rows = (c < 2) ? prow[c & 1] : (hi > lo ? (hi - lo) % bm : 0);
       const uint64_t has = __ballot(rows > 0);
       int rank = npart + __popcll(has & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-      if (sort) {  // rows descending, then expert order, over both chunks
+      if (WRITE && sort) {  // rows descending, then expert order, over both chunks
         rank = 0;
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)
@@ -183,7 +185,7 @@ __device__ int plan_one_pass(const PackParams &p, const int *s_off, int E, int k
             rank += (r2 > rows || (r2 == rows && e2 < e)) ? 1 : 0;
           }
       }
-      if (rows > 0) {
+      if (WRITE && rows > 0) {
         int32_t *d = plan + 1 + 3 * (base + nfull + rank);
         d[0] = e;
         d[1] = roff + lo - pb + (hi - lo) / bm * bm;
@@ -194,6 +196,31 @@ __device__ int plan_one_pass(const PackParams &p, const int *s_off, int E, int k
     total = nfull + npart;
   }
   return total;
+}
+
+// Plans of every launch unit of p.group > 1 passes when the passes' tile
+// counts fit `cnt` (ncnt ints of LDS, free): every wave first counts the
+// tiles of its passes, then writes them after the earlier passes of their
+// unit, so all waves plan in parallel. Same plan as plan_units.
+__device__ void plan_units_parallel(const PackParams &p, const int *s_off, int E, int kept,
+                                    int w, int nw, int lane, int *cnt) {
+  const int G = p.group;
+  for (int pass = w; pass < p.passes; pass += nw) {
+    const int n = plan_one_pass<false>(p, s_off, E, kept, pass, lane, nullptr, 0, 0);
+    if (lane == 0) cnt[pass] = n;
+  }
+  __syncthreads();
+  for (int pass = w; pass < p.passes; pass += nw) {
+    const int u = pass / G, j = pass - u * G;
+    int32_t *plan = p.plan + (int64_t)u * (1 + 3 * (int64_t)G * p.slots);
+    int base = 0, n = 0;
+    for (int j2 = 0; j2 < G && u * G + j2 < p.passes; ++j2) {
+      base += (j2 < j) ? cnt[u * G + j2] : 0;
+      n += cnt[u * G + j2];
+    }
+    plan_one_pass(p, s_off, E, kept, pass, lane, plan, base, j * p.capacity);
+    if (j == 0 && lane == 0) plan[0] = n;
+  }
 }
 
 // Plans of every launch unit (p.group consecutive passes), one wave per unit.
@@ -344,8 +371,13 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
     for (int pos = a + lane; pos < b; pos += 64) p.expert_of_pos[pos] = e;
   }
 
-  // a4: one wave per pass
-  plan_units(p, s_off, E, kept, w, kPackWaves, lane);
+  // a4: one wave per pass (units of grouped passes: count, then write)
+  if (p.group > 1 && p.passes <= kPackWaves * kMaxE) {
+    __syncthreads();  // the per-wave position counters are free
+    plan_units_parallel(p, s_off, E, kept, w, kPackWaves, lane, &s_wc[0][0]);
+  } else {
+    plan_units(p, s_off, E, kept, w, kPackWaves, lane);
+  }
 
   // rows whose pairs were all dropped produce zeros: one row per thread to
   // find them (rare), then the row is cleared by that thread. A pack that
