@@ -340,6 +340,25 @@ def test_moe_wide_pipelined_edge_cases():
         assert torch.equal(y2.view(torch.int32), y.view(torch.int32)), null
 
 
+@pytest.mark.parametrize("cap,group", [(100, 2), (50, 4), (7, 4)])
+def test_moe_wide_grouped_passes_additive_equals_forward(cap, group):
+    """128-row tiles over several passes grouped into launch units (2 or 4
+    passes per plan and buffer set): exl3_moe_additive on the route pack
+    equals exl3_moe_forward, and both equal the one-pass result."""
+    wl = _wide_wl()
+    lay = exl3.moe_layout(wl.rows, wl.topk, wl.num_experts, wl.hidden, wl.intermediate, cap)
+    assert lay.plan_group == group, (lay.passes, lay.plan_group)
+    _say("wide grouped", cap, lay.passes, group)
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    one = exl3.exl3_moe_forward(x, ids, w, gate, up, down, 10 ** 6, torch.float32)
+    fwd = exl3.exl3_moe_forward(x, ids, w, gate, up, down, cap, torch.float32)
+    meta = exl3.exl3_route_pack(ids, w, wl.num_experts)
+    add = exl3.exl3_moe_additive(x, wl.topk, meta, gate, up, down, cap, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(fwd.view(torch.int32), one.view(torch.int32))
+    assert torch.equal(add.view(torch.int32), one.view(torch.int32))
+
+
 def test_linear_wide_multistage_parity():
     # 1024 rows x 8192 out selects 128-row tiles; three stages, one zero
     p, x = _linear_case(256, 8192, ((3, 1.0), (2, 0.25), (4, 0.0)), 1024, seed=9)
