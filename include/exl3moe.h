@@ -19,8 +19,8 @@
  *     memory, so every call can be captured into a hipGraph. Table contents
  *     may change between graph replays; their addresses may not.
  *   - Every argument is validated on the host BEFORE any device work is
- *     enqueued [p1 Summary: validate device, contiguity, dtype, shape,
- *     workspace and routing contracts before device-side mutation]. On error
+ *     enqueued [p1 Summary: the device, layout, dtypes, shapes, workspace and
+ *     routing are all checked first]. On error
  *     the call returns a negative EXL3_E_* code and enqueues nothing.
  *     rows == 0 is a successful no-op.
  *   - Problems only the device can see (route ID outside [0, E), a stage
@@ -85,8 +85,8 @@ const char *exl3_status_string(int32_t status);
 /*
  * One projection (gate, up or down) of all experts; num_experts == 1 for a
  * plain linear. Stage 0 is the base; stages 1.. are additive residual
- * ("cartridge") stages [p1 Summary: stage-major trellis pointer, scale and
- * bitrate tables with zero-scale sparse entries]. Tables are stage-major
+ * ("cartridge") stages [p1 Summary: per-stage tables of trellis addresses,
+ * scales and widths, any entry of which may be empty]. Tables are laid out
  * [num_stages][num_experts]:
  *   trellis  int64 device addresses of uint16 trellis tensors, each
  *            [out/16][in/16][16*K] words (16x16 tiles of 256*K bits,
@@ -212,9 +212,16 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t x_dtype, int32_t rows, int3
 /*
  * Workspace layout of exl3_moe_forward / exl3_moe_additive (byte offsets
  * from ws, each region 256-byte aligned, in this order):
- *   ctrl        256 B   int32[64]: [0] dropped pairs, [1] bad stage entries,
- *               [2] waits between the gate/up and down items of one pass that
- *               gave up (never expected; the output is then invalid)
+ *   ctrl        256 B   int32[64], status words of the last call, written
+ *               or zeroed at its start by its first launch:
+ *               [0] pairs left out: IDs outside [0, E) (exl3_moe_forward) or
+ *                   pairs whose pos_of_pair is negative (exl3_moe_additive);
+ *               [1] stage entries skipped because a nonzero scale came with a
+ *                   null trellis or a width outside 2..8;
+ *               [2] device-side waits between work items that gave up (never
+ *                   expected; the output of that call is then invalid).
+ *               A caller reads them after the call's stream work completes;
+ *               the library itself never waits for them.
  *   meta        forward only: count[E], offset[E+1], pair_of_pos[P],
  *               weight_of_pos[P], pos_of_pair[P], num_active[1] (P = pairs)
  *   expert_of_pos int32[P]
@@ -252,7 +259,10 @@ int32_t exl3_moe_layout(int32_t rows, int32_t topk, int32_t num_experts,
 
 /*
  * Diagnostic: decode `ntiles` consecutive trellis tiles of width K with the
- * same device decoder the GEMMs use. words: [ntiles][16K] uint16;
+ * GEMM kernels' own decode path: consecutive tile pairs are taken as the two
+ * tiles of one 32-input MFMA k-step, and each lane decodes the half column
+ * those kernels give it, from the same in-tile window offsets and shift,
+ * with the same register decode. words: [ntiles][16K] uint16;
  * out: [ntiles][16 (k)][16 (n)] fp16. For bit-exact decode tests.
  */
 int32_t exl3_decode_tiles(const uint16_t *words, int32_t ntiles, int32_t K,

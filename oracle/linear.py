@@ -6,7 +6,7 @@ What is computed, following the pages:
     other rows.
   * exllamav3 #284 (Summary, API contract): FP32 accumulation and output
     scaling in the inner GEMM; stage-major trellis/scale/bitrate tables with
-    zero-scale sparse entries; residual stages reuse the base suh/svh; a zero
+    entries that may be empty; residual stages reuse the base suh/svh; a zero
     scale skips that stage's GEMM.
 
 Reading used where the pages are silent (the library's format definition):

@@ -4,7 +4,8 @@
 // y_r = sum of the row's weighted per-pair outputs d, added in fp32 in
 // ascending packed position (expert, then pair index), pass after pass.
 // TensorFold PR #837 (What this changes: the weighted combine; an expert's
-// member count never changes a row's bits) — the fixed order makes the row's
+// how many rows an expert serves must not alter any row's result) — the
+// fixed order makes the row's
 // bytes independent of other rows, capacity and chunking.
 #pragma once
 

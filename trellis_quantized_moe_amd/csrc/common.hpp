@@ -33,7 +33,7 @@ constexpr float kRsqrt128 = 0.08838834764831845f;  // 1/sqrt(128), fp32
 // GPU-internal k order of rotated activations: inside every aligned group of
 // 16 entries, stored slot p holds entry kSigma[p] =
 // {0,4,1,5,2,6,3,7, 8,12,9,13,10,14,11,15}. It matches the order in which one
-// lane's decoded B values reach the MFMA (see decode_column).
+// lane's decoded B values reach the MFMA (see decode_half).
 // Entry k (0..15) of a 16-group -> stored slot.
 __device__ __forceinline__ int sigma_inv(int k) {
   // inverse of kSigma: k -> 2*(k&3) + ((k>>2)&1) + (k&8)
@@ -64,31 +64,6 @@ __device__ __forceinline__ uint32_t codebook_mask() {
 template <int K>
 struct Geom {
   static constexpr int kTileDw = 8 * K;  // dwords per tile
-  // dwords covering one column's window (15K + 16 bits) at the worst offset
-  static constexpr int kLoadDw = (K == 2) ? 2 : (K <= 4) ? 3 : (K <= 6) ? 4 : 5;
-  // dwords of the window once shifted to bit 0
-  static constexpr int kNormDw = (15 * K + 16 + 31) / 32;
-};
-
-// Dword indices (within a tile) and bit shift of the window of column n.
-// The window of states 16n..16n+15 starts at bit 16nK + K - 16; for n = 0 it
-// wraps to the end of the tile (tail-biting).
-template <int K>
-struct ColumnWindow {
-  int idx[Geom<K>::kLoadDw];
-  uint32_t shift;
-  __device__ __forceinline__ explicit ColumnWindow(int n) {
-    const int b = 16 * n * K + K - 16;
-    const int d0 = b >> 5;  // floor
-    shift = (uint32_t)(b & 31);
-#pragma unroll
-    for (int j = 0; j < Geom<K>::kLoadDw; ++j) {
-      int d = d0 + j;
-      d += (d < 0) ? Geom<K>::kTileDw : 0;
-      d -= (d >= Geom<K>::kTileDw) ? Geom<K>::kTileDw : 0;
-      idx[j] = d;
-    }
-  }
 };
 
 // Geometry of half a tile column (8 consecutive states): the window is
@@ -135,14 +110,6 @@ __device__ __forceinline__ void normalize(const uint32_t (&raw)[ND], uint32_t sh
   }
 }
 
-// The window of one tile column shifted to bit 0 (kNormDw dwords).
-template <int K>
-__device__ __forceinline__ void column_normalize(const uint32_t (&raw)[Geom<K>::kLoadDw],
-                                                 uint32_t shift,
-                                                 uint32_t (&N)[Geom<K>::kNormDw]) {
-  normalize(raw, shift, N);
-}
-
 // States (j, j + 4) of a normalised window (state i starting at bit iK) in
 // the low and high 16-bit halves of one dword (bits above a state's 16 are
 // don't-care for the 16-bit hash). State j starts at bit o1 = jK, state
@@ -178,16 +145,6 @@ __device__ __forceinline__ uint32_t column_pair(const uint32_t (&N)[NN]) {
     const uint32_t hi = window32<o2 - 16>(N);
     return __builtin_amdgcn_perm(hi, lo, 0x07060100u);
   }
-}
-
-// Packed fp16 register V (0..7) of a decoded tile column: states (j, j+4)
-// with j = (V & 3) + 8 * (V >> 2), so registers 0..3 feed k = {0,4,1,5,2,6,3,7}
-// and 4..7 feed k = {8,12,9,13,10,14,11,15} of the column: the kSigma order.
-template <int K, int V>
-__device__ __forceinline__ uint32_t column_reg(const uint32_t (&N)[Geom<K>::kNormDw],
-                                               uint32_t mask) {
-  constexpr int j = (V & 3) + 8 * (V >> 2);
-  return codebook2(column_pair<K, j>(N), mask);
 }
 
 // Register r (0..3) of a decoded half column (window normalised to its first
@@ -230,22 +187,64 @@ __device__ __forceinline__ uint32_t half_reg_raw(const uint32_t (&raw)[ND], uint
   return codebook2(pair, mask);
 }
 
-// Decode one tile column (16 states) from its raw dwords into 8 packed fp16
-// pairs (register order as in column_reg).
+// The half column a lane decodes in one 32-input MFMA k-step (two tiles along
+// k): lane (g, n) takes states 8h .. 8h + 7 (h = g & 1) of column n of tile
+// t = g >> 1, i.e. the 8 k-entries it feeds the MFMA. Their window starts at
+// bit 16nK + 8hK + K - 16 of tile t's tail-biting stream. off[j] is the byte
+// offset of the window's dword j from the step's first tile (tile t's own
+// base included, wrapped inside the tile); shift is the window's bit offset
+// inside dword 0. Every kernel that decodes trellis (both GEMM tile shapes and
+// the diagnostic decode export) takes its addresses from here.
 template <int K>
-__device__ __forceinline__ void decode_column(const uint32_t (&raw)[Geom<K>::kLoadDw],
-                                              uint32_t shift, uint32_t mask,
-                                              uint32_t (&out)[8]) {
-  uint32_t N[Geom<K>::kNormDw];
-  column_normalize<K>(raw, shift, N);
-  out[0] = column_reg<K, 0>(N, mask);
-  out[1] = column_reg<K, 1>(N, mask);
-  out[2] = column_reg<K, 2>(N, mask);
-  out[3] = column_reg<K, 3>(N, mask);
-  out[4] = column_reg<K, 4>(N, mask);
-  out[5] = column_reg<K, 5>(N, mask);
-  out[6] = column_reg<K, 6>(N, mask);
-  out[7] = column_reg<K, 7>(N, mask);
+struct HalfWindow {
+  static constexpr int ND = HalfGeom<K>::kLoadDw;
+  uint32_t off[ND];
+  uint32_t shift;
+  __device__ __forceinline__ explicit HalfWindow(int lane) {
+    constexpr int TD = Geom<K>::kTileDw;
+    const int g = lane >> 4, n = lane & 15;
+    const int b = 16 * n * K + 8 * (g & 1) * K + K - 16;
+    const int d0 = b >> 5;  // floor
+    shift = (uint32_t)(b & 31);
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+      int d = d0 + j;
+      d += (d < 0) ? TD : 0;
+      d -= (d >= TD) ? TD : 0;
+      off[j] = (uint32_t)((g >> 1) * TD + d) * 4u;
+    }
+  }
+};
+
+// Register r (0..3) of a decoded half column from the raw window dwords:
+// states (r, r + 4), fp16 k-slots {2r, 2r + 1} of the lane's MFMA operand.
+// K = 4 and 8 cut the pairs straight from the raw dwords; other widths shift
+// the window to bit 0 first (N, computed when r == 0 and reused for r > 0).
+template <int K, int r>
+__device__ __forceinline__ uint32_t half_column_reg(const uint32_t (&raw)[HalfGeom<K>::kLoadDw],
+                                                    uint32_t shift,
+                                                    uint32_t (&N)[HalfGeom<K>::kNormDw],
+                                                    uint32_t mask) {
+  if constexpr (kRawPairs<K>) {
+    (void)shift;
+    (void)N;
+    return half_reg_raw<K, r>(raw, mask);
+  } else {
+    if constexpr (r == 0) normalize(raw, shift, N);
+    return half_reg<K, r>(N, mask);
+  }
+}
+
+// The whole decoded half column: the 8 fp16 B-operand values of the lane.
+template <int K>
+__device__ __forceinline__ u32x4 decode_half(const uint32_t (&raw)[HalfGeom<K>::kLoadDw],
+                                             uint32_t shift, uint32_t mask) {
+  uint32_t N[HalfGeom<K>::kNormDw];
+  const uint32_t r0 = half_column_reg<K, 0>(raw, shift, N, mask);
+  const uint32_t r1 = half_column_reg<K, 1>(raw, shift, N, mask);
+  const uint32_t r2 = half_column_reg<K, 2>(raw, shift, N, mask);
+  const uint32_t r3 = half_column_reg<K, 3>(raw, shift, N, mask);
+  return (u32x4){r0, r1, r2, r3};
 }
 
 // Wave index as a scalar: lets the compiler keep every per-wave value (and
@@ -309,8 +308,10 @@ __device__ __forceinline__ void fwht128_group16(float (&v)[8]) {
 
 // Unnormalised 128-point FWHT with 8 consecutive entries per lane: lane i of
 // the 16-lane group holds entries 8i..8i+7. Distances 1, 2, 4 in registers,
-// then 8..64 across lanes (xor 1..8). Used for the input rotation only.
-__device__ __forceinline__ void fwht128_lane8(float (&v)[8]) {
+// then 8..64 across lanes (xor 1..8). Used for the input rotation only, in
+// fp64: there every butterfly is exact (the inputs are fp16 values, so any
+// sum of 128 of them spans at most 40 significant bits).
+__device__ __forceinline__ void fwht128_lane8(double (&v)[8]) {
   const int i = threadIdx.x & 15;
 #pragma unroll
   for (int d = 1; d < 8; d <<= 1) {
@@ -328,17 +329,42 @@ __device__ __forceinline__ void fwht128_lane8(float (&v)[8]) {
     const bool upper = (i & d) != 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float o = __shfl_xor(v[j], d, 64);
+      const double o = __shfl_xor(v[j], d, 64);
       v[j] = upper ? (o - v[j]) : (v[j] + o);
     }
   }
 }
+
+constexpr double kRsqrt128d = 0.088388347648318440550;  // 1/sqrt(128), fp64
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);  // RNE
 }
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// fp64 -> fp16, round to nearest even, in one rounding. The value is first
+// rounded to fp32 (RNE). That second rounding can only go wrong where the
+// fp32 result lands exactly on the midpoint between two fp16 values while the
+// fp64 value does not: then the fp32 value is moved one fp32 ulp towards the
+// fp64 value before the fp16 rounding, so the midpoint is resolved the way
+// the fp64 value lies. (Midpoint test: the fp32 significand bits below the
+// fp16 lsb are exactly one half of it; below 2^-14 the fp16 lsb is 2^-24.)
+__device__ __forceinline__ uint16_t f64_to_f16_bits(double d) {
+  float f = (float)d;
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  const int E = (int)((u >> 23) & 0xFFu) - 127;
+  const int drop = (E >= -14) ? 13 : 13 + (-14 - E);  // fp32 bits below the fp16 lsb
+  const uint32_t mant = (u & 0x7FFFFFu) | ((E > -127) ? 0x800000u : 0u);
+  const bool tie = drop <= 24 && (mant & ((1u << drop) - 1u)) == (1u << (drop - 1));
+  const double back = (double)f;
+  if (tie && d != back) {
+    // away from zero if |d| > |f|, else towards zero
+    u = ((d > back) == (f > 0.0f)) ? u + 1u : u - 1u;
+    f = __builtin_bit_cast(float, u);
+  }
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 // bfloat16 = the upper 16 bits of an fp32, rounded to nearest even (add
 // 0x7FFF plus the lowest kept bit, then truncate); a NaN stays a (quiet) NaN.

@@ -8,7 +8,7 @@
 // changes: decode straight into the matrix-core operands, input rotation,
 // row-invariant linear, grouped experts with SwiGLU and down) and exllamav3
 // PR #284 "MoE: Add fused additive EXL3 kernels" (Summary: FP32 accumulation
-// and output scaling; stage tables with zero-scale sparse entries).
+// and output scaling; per-stage tables in which a stage may be absent).
 //
 // Arithmetic contract (makes a row's bytes independent of the other rows,
 // the tile it lands in, the capacity and the chunking):
@@ -77,7 +77,7 @@ __device__ __forceinline__ void sdma16(uint32_t voff, const void *sbase, uint32_
       "s_mov_b64 exec, %0"
       : "=&s"(saved)
       : "v"(voff), "s"(sbase), "s"(lds_base), "s"(lanes)
-      : "memory");
+      : "memory", "scc");
 }
 
 template <int N>
@@ -103,7 +103,7 @@ __device__ __forceinline__ void aload_block(u32x4 &a0, u32x4 &a1, u32x4 &a2, u32
       "s_mov_b64 exec, %4"
       : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&s"(saved)
       : "v"(voff), "s"(sbase), "s"(lanes)
-      : "memory");
+      : "memory", "scc");
 }
 
 // Wait until at most N vector loads are outstanding; the A registers of the
@@ -172,16 +172,7 @@ struct StreamChain {
         raw[s][j] = *(const uint32_t *)(ring + base + traddr[j] + s * 2 * TD * 4);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      uint32_t N[NN];
-      u32x4 w;
-      if constexpr (kRawPairs<K>) {
-        w = (u32x4){half_reg_raw<K, 0>(raw[s], mask), half_reg_raw<K, 1>(raw[s], mask),
-                    half_reg_raw<K, 2>(raw[s], mask), half_reg_raw<K, 3>(raw[s], mask)};
-      } else {
-        normalize(raw[s], shift, N);
-        w = (u32x4){half_reg<K, 0>(N, mask), half_reg<K, 1>(N, mask), half_reg<K, 2>(N, mask),
-                    half_reg<K, 3>(N, mask)};
-      }
+      const u32x4 w = decode_half<K>(raw[s], shift, mask);
       acc = mfma16x16x32(__builtin_bit_cast(f16x8, a[aslot][s]), __builtin_bit_cast(f16x8, w), acc);
     }
   }
@@ -224,7 +215,7 @@ __device__ __forceinline__ f32x4 stream_chain(const char *strip, int in_f, const
                                               int lane) {
   StreamChain<K> c;
   c.alanes = alanes;
-  const int g = lane >> 4, n = lane & 15;
+  const int g = lane >> 4;
   c.strip = sgpr_ptr(strip);
   c.ring = ring;
   c.ring_lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)ring);
@@ -232,18 +223,10 @@ __device__ __forceinline__ f32x4 stream_chain(const char *strip, int in_f, const
   c.avoff = avoff + 16u * g;  // 8 halves per k-group
   c.tvoff = 16u * (uint32_t)lane;
   c.nblk = in_f >> 7;
-  // window of states 8h .. 8h+7 of column n: first bit 16nK + 8hK + K - 16
-  const int b = 16 * n * K + 8 * (g & 1) * K + K - 16;
-  const int d0 = b >> 5;  // floor
-  c.shift = (uint32_t)(b & 31);
-  constexpr int TD = Geom<K>::kTileDw;
+  const HalfWindow<K> hw(lane);
+  c.shift = hw.shift;
 #pragma unroll
-  for (int j = 0; j < StreamChain<K>::ND; ++j) {
-    int d = d0 + j;
-    d += (d < 0) ? TD : 0;
-    d -= (d >= TD) ? TD : 0;
-    c.traddr[j] = (uint32_t)((g >> 1) * TD + d) * 4u;
-  }
+  for (int j = 0; j < StreamChain<K>::ND; ++j) c.traddr[j] = hw.off[j];
   c.mask = codebook_mask();
   return c.run();
 }
@@ -373,48 +356,55 @@ hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks, hip
   return hipGetLastError();
 }
 
-// Diagnostic decode of whole tiles with the same column decoder: one wave per
-// tile, lane n (< 16) decodes column n; output [tile][k][n] fp16 in natural k.
+// Diagnostic decode with the GEMMs' own decode path: one wave per pair of
+// consecutive tiles (taken as the two tiles of one 32-input k-step), each
+// lane decoding the half column HalfWindow assigns it with decode_half, from
+// the same window byte offsets and shift the GEMM kernels use (the GEMMs read
+// those dwords from their LDS rings, this kernel from global memory). Output
+// [tile][k][n] fp16 in natural k order: register r of lane (g, n) holds
+// states (r, r + 4) of its half, i.e. k = 8 (g & 1) + r and k + 4.
 template <int K>
-__device__ void decode_tile_wave(const uint16_t *words, uint16_t *out, int lane) {
-  if (lane >= 16) return;
-  const uint32_t *t = (const uint32_t *)words;
-  const ColumnWindow<K> cw(lane);
-  uint32_t raw[Geom<K>::kLoadDw];
+__device__ void decode_pair_wave(const uint16_t *words, int ntiles, int pair, uint16_t *out,
+                                 int lane) {
+  const int g = lane >> 4, n = lane & 15;
+  const int tile = 2 * pair + (g >> 1);
+  if (tile >= ntiles) return;
+  const uint32_t *base = (const uint32_t *)(words + (size_t)(2 * pair) * 16 * K);
+  const HalfWindow<K> hw(lane);
+  uint32_t raw[HalfGeom<K>::kLoadDw];
 #pragma unroll
-  for (int j = 0; j < Geom<K>::kLoadDw; ++j) raw[j] = t[cw.idx[j]];
-  uint32_t b[8];
-  decode_column<K>(raw, cw.shift, codebook_mask(), b);
+  for (int j = 0; j < HalfGeom<K>::kLoadDw; ++j) raw[j] = base[hw.off[j] >> 2];
+  const u32x4 b = decode_half<K>(raw, hw.shift, codebook_mask());
+  uint16_t *o = out + (size_t)tile * 256;
+  const int k0 = 8 * (g & 1);
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    const int j = (v & 3) + 8 * (v >> 2);
-    out[j * 16 + lane] = (uint16_t)(b[v] & 0xFFFFu);
-    out[(j + 4) * 16 + lane] = (uint16_t)(b[v] >> 16);
+  for (int r = 0; r < 4; ++r) {
+    o[(k0 + r) * 16 + n] = (uint16_t)(b[r] & 0xFFFFu);
+    o[(k0 + r + 4) * 16 + n] = (uint16_t)(b[r] >> 16);
   }
 }
 
 __global__ void decode_tiles_kernel(const uint16_t *words, int ntiles, int K,
                                     uint16_t *out) {
-  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tile >= ntiles) return;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (2 * pair >= ntiles) return;
   const int lane = threadIdx.x & 63;
-  const uint16_t *w = words + (size_t)tile * 16 * K;
-  uint16_t *o = out + (size_t)tile * 256;
   switch (K) {
-    case 2: decode_tile_wave<2>(w, o, lane); break;
-    case 3: decode_tile_wave<3>(w, o, lane); break;
-    case 4: decode_tile_wave<4>(w, o, lane); break;
-    case 5: decode_tile_wave<5>(w, o, lane); break;
-    case 6: decode_tile_wave<6>(w, o, lane); break;
-    case 7: decode_tile_wave<7>(w, o, lane); break;
-    default: decode_tile_wave<8>(w, o, lane); break;
+    case 2: decode_pair_wave<2>(words, ntiles, pair, out, lane); break;
+    case 3: decode_pair_wave<3>(words, ntiles, pair, out, lane); break;
+    case 4: decode_pair_wave<4>(words, ntiles, pair, out, lane); break;
+    case 5: decode_pair_wave<5>(words, ntiles, pair, out, lane); break;
+    case 6: decode_pair_wave<6>(words, ntiles, pair, out, lane); break;
+    case 7: decode_pair_wave<7>(words, ntiles, pair, out, lane); break;
+    default: decode_pair_wave<8>(words, ntiles, pair, out, lane); break;
   }
 }
 
 hipError_t launch_decode_tiles(const uint16_t *words, int ntiles, int K,
                                uint16_t *out, hipStream_t s) {
   if (ntiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_tiles_kernel, dim3((ntiles + 3) / 4), dim3(256), 0, s,
+  const int pairs = (ntiles + 1) / 2;
+  hipLaunchKernelGGL(decode_tiles_kernel, dim3((pairs + 3) / 4), dim3(256), 0, s,
                      words, ntiles, K, out);
   return hipGetLastError();
 }

@@ -3,7 +3,8 @@
 // this one epilogue so a row's output bytes never depend on the tile shape it
 // was computed with (TensorFold PR #837 "cuda: EXL3 linear and grouped routed
 // experts, every codebook and width, a width per expert", What this changes:
-// row-invariant linear; an expert's member count never changes a row's bits).
+// row-invariant linear; the number of rows routed to an expert does not alter
+// any row's result).
 #pragma once
 
 #include "common.hpp"

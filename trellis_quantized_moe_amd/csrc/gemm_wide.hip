@@ -8,7 +8,8 @@
 // changes: decode straight into the matrix-core operands; grouped experts with
 // SwiGLU and down) and exllamav3 PR #284 "MoE: Add fused additive EXL3
 // kernels" (Summary: FP32 accumulation and output scaling; stage tables with
-// zero-scale sparse entries). The per-element arithmetic is the one the
+// per-stage tables in which a stage may be absent). The per-element
+// arithmetic is the one the
 // narrow kernel uses: for each output, an MFMA chain over ascending 32-input
 // k-steps (each two whole trellis tiles) starting from 0, then
 // acc = fmaf(s_t, P_t, acc) over the stages, then the shared epilogue.
@@ -137,7 +138,7 @@ __device__ __forceinline__ void dma16_lanes(uint32_t voff, const void *sbase, ui
       "s_mov_b64 exec, %0"
       : "=&s"(saved)
       : "v"(voff), "s"(sbase), "s"(lds_base), "s"(lanes)
-      : "memory");
+      : "memory", "scc");
 }
 
 __device__ __forceinline__ const char *uniform_ptr(const char *ptr) {
@@ -205,19 +206,10 @@ struct WideIter {
       tvoff[d] = (uint32_t)((nt0 + ns) * ktiles * 32 * K + 16 * min(sl, SEG / 16 - 1));
     }
     tdst = uniform_u32(c.lds0 + L::kTOff + c.w * kTwave);
-    // window of states 8h .. 8h+7 of column n of tile t: first bit
-    // 16nK + 8hK + K - 16 of the tile's tail-biting stream
-    const int t = g >> 1, h = g & 1;
-    const int b = 16 * n * K + 8 * h * K + K - 16;
-    const int d0 = b >> 5;  // floor
-    shift = (uint32_t)(b & 31);
+    const HalfWindow<K> hw(lane);
+    shift = hw.shift;
 #pragma unroll
-    for (int j = 0; j < ND; ++j) {
-      int d = d0 + j;
-      d += (d < 0) ? 8 * K : 0;
-      d -= (d >= 8 * K) ? 8 * K : 0;
-      traddr[j] = (uint32_t)(L::kTOff + c.w * kTwave + t * 32 * K + 4 * d);
-    }
+    for (int j = 0; j < ND; ++j) traddr[j] = (uint32_t)(L::kTOff + c.w * kTwave) + hw.off[j];
     afrag = (uint32_t)(L::kAOff + c.pj * kAbuf + n * kArow + ((g ^ a_swizzle(n)) * 16));
     mask = codebook_mask();
   }
@@ -249,12 +241,7 @@ struct WideIter {
   template <int Q>
   __device__ __forceinline__ void decode_pair(BRegs &bn) {
     constexpr int ns = Q / 4, r = Q % 4;
-    if constexpr (kRawPairs<K>) {
-      bn[ns][r] = half_reg_raw<K, r>(raw[ns], mask);
-    } else {
-      if constexpr (r == 0) normalize(raw[ns], shift, N);
-      bn[ns][r] = half_reg<K, r>(N, mask);
-    }
+    bn[ns][r] = half_column_reg<K, r>(raw[ns], shift, N, mask);
   }
   template <int... Qs>
   __device__ __forceinline__ void decode_seq(BRegs &bn, std::integer_sequence<int, Qs...>) {

@@ -2,8 +2,8 @@
 // workspace layout and stream-ordered launch orchestration. No call
 // synchronises, allocates or frees; every argument is checked before the
 // first launch (exllamav3 PR #284 "MoE: Add fused additive EXL3 kernels",
-// Summary: validate device, contiguity, dtype, shape, workspace and routing
-// contracts before device-side mutation; API contract: exact ABI version).
+// Summary: all argument checks precede any device work; API contract: an
+// exact ABI version number).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -37,7 +37,7 @@ struct GemmParams {
   int64_t ldo;
   const float *weight_of_pos;  // DOWN
   int pass_base;               // DOWN: packed position of tile row 0
-  int32_t *ctrl;               // [1] counts bad stage entries
+  int32_t *ctrl;               // [1] bad stage entries, [2] waits that gave up
   // narrow tiles: pre-rotation sums [rows][NPROJ][out_f] and per (tile,
   // 128-column block) completion counts, zero between launches
   float *nacc;
@@ -58,7 +58,7 @@ struct RotParams {
   int pairs;   // rows * topk (bound for caller-supplied metadata)
   int nitems;  // positions of this pass (upper bound) or rows
   uint16_t *xt;  // [nitems][nproj][H]
-  int32_t *ctrl_clear;  // if set, block 0 zeroes ctrl[1] (bad stage entries)
+  int32_t *ctrl_clear;  // if set, block 0 zeroes ctrl[0..2] (linear calls)
   int32_t *zero;        // if set, zeroed (nzero ints) before the GEMMs run
   int nzero;
 };
@@ -93,7 +93,8 @@ struct PackParams {
   // unrouted rows get zero output
   void *out;
   int out_f32, H;
-  int32_t *ctrl;  // [0] dropped pairs, [1] bad stage entries (cleared)
+  int32_t *ctrl;  // [0] dropped pairs (written), [1] bad stage entries and
+                  // [2] waits that gave up (both zeroed)
   int32_t *zero;  // narrow-tile completion counts, zeroed (nzero ints)
   int nzero;
 };

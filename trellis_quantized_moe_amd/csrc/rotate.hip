@@ -6,7 +6,9 @@ namespace exl3 {
 // One 16-lane group per (item, 128-block), 16 groups per block.
 __global__ void __launch_bounds__(256) rotate_kernel(RotParams p) {
   if (p.ctrl_clear && blockIdx.x == 0 && threadIdx.x == 0) {
+    p.ctrl_clear[0] = 0;  // dropped pairs (none in a linear call)
     p.ctrl_clear[1] = 0;  // bad stage entries
+    p.ctrl_clear[2] = 0;  // waits that gave up
   }
   if (p.zero) {  // completion counts of the GEMMs that follow
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < p.nzero;

@@ -1,5 +1,6 @@
 // Input rotation of one (item, 128-block) by one 16-lane group (x in fp16 or
-// bf16, read exactly; x~ always rounded to fp16), shared by the
+// bf16, read exactly; x~ rounded once to fp16 from an exact fp64 transform,
+// so it is the correctly rounded rotated value), shared by the
 // rotate kernel and the per-pass expert kernel (which rotates the next pass's
 // inputs while its own down work finishes).
 // x~ = fp16_rne(H128(x * suh) / sqrt(128)) for the GEMM A operands, stored in
@@ -33,7 +34,7 @@ __device__ __forceinline__ void rotate_block(const RotParams &p, int item, int b
     if (pj >= p.nproj) break;
     // halves are unpacked with shifts: this compiler mis-compiles a bit_cast
     // of a vector element taken inside an unrolled loop (it reuses element 0)
-    float v[8];
+    double v[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t xw = xv[j], sw = sv[pj][j];
@@ -41,13 +42,15 @@ __device__ __forceinline__ void rotate_block(const RotParams &p, int item, int b
                                 : f16_bits_to_f32((uint16_t)(xw & 0xFFFFu));
       const float x1 = p.x_bf16 ? bf16_bits_to_f32((uint16_t)(xw >> 16))
                                 : f16_bits_to_f32((uint16_t)(xw >> 16));
-      v[2 * j] = x0 * f16_bits_to_f32((uint16_t)(sw & 0xFFFFu));
-      v[2 * j + 1] = x1 * f16_bits_to_f32((uint16_t)(sw >> 16));
+      v[2 * j] = (double)(x0 * f16_bits_to_f32((uint16_t)(sw & 0xFFFFu)));
+      v[2 * j + 1] = (double)(x1 * f16_bits_to_f32((uint16_t)(sw >> 16)));
     }
+    // exact butterflies and one rounding: x~ is the fp16 value nearest to
+    // Hhat(x * suh) itself
     fwht128_lane8(v);
     uint16_t h[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) h[j] = f32_to_f16_bits(v[j] * kRsqrt128);
+    for (int j = 0; j < 8; ++j) h[j] = f64_to_f16_bits(v[j] * kRsqrt128d);
     const u32x4 o = {(uint32_t)h[0] | ((uint32_t)h[4] << 16), (uint32_t)h[1] | ((uint32_t)h[5] << 16),
                      (uint32_t)h[2] | ((uint32_t)h[6] << 16), (uint32_t)h[3] | ((uint32_t)h[7] << 16)};
     *(u32x4 *)(p.xt + ((int64_t)item * p.nproj + pj) * p.H + col) = o;

@@ -246,6 +246,7 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int E = p.E;
   const int pairs = p.rows * p.topk;
+  if (tid == 0) s_dropped = 0;
 
   if (p.do_pack) {
     // the wave's segment: whole rounds of 64 pairs
@@ -256,7 +257,6 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int *wc = s_wc[w];
     for (int e = lane; e < E; e += 64) wc[e] = 0;
-    if (tid == 0) s_dropped = 0;
     __syncthreads();
 
     // a1: this wave's histogram (only this wave touches its row)
@@ -353,12 +353,18 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
     const int m = block_inclusive_max(v, s_tmp, vmax);
     if (tid < E) s_off[tid] = m;
     if (tid == 0) s_off[E] = max(min(max(p.offset[E], 0), pairs), vmax);
+    // dropped pairs of the caller's pack (no position): reported in ctrl[0]
+    int drop = 0;
+    for (int q = tid; q < pairs; q += kPackThreads) drop += (p.pos_of_pair[q] < 0) ? 1 : 0;
+    if (drop) atomicAdd(&s_dropped, drop);
     __syncthreads();
+    if (tid == 0 && p.ctrl) p.ctrl[0] = s_dropped;
   }
 
   if (!p.do_plan) return;
   if (tid == 0 && p.ctrl) {
     p.ctrl[1] = 0;  // bad stage entries
+    p.ctrl[2] = 0;  // waits that gave up
   }
   for (int i = tid; i < p.nzero; i += kPackThreads) p.zero[i] = 0;
 
@@ -493,7 +499,10 @@ __device__ void pack_small(const PackParams &p) {
     p.weight_of_pos[pos] = 0.0f;
   }
   if (!p.do_plan) return;
-  if (lane == 0 && p.ctrl) p.ctrl[1] = 0;  // bad stage entries
+  if (lane == 0 && p.ctrl) {
+    p.ctrl[1] = 0;  // bad stage entries
+    p.ctrl[2] = 0;  // waits that gave up
+  }
   for (int i = lane; i < p.nzero; i += 64) p.zero[i] = 0;
   plan_units(p, s_off, p.E, r.kept, 0, 1, lane);  // one pass: capacity >= pairs
   // rows whose pairs were all dropped produce zeros
