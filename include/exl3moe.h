@@ -48,7 +48,7 @@ extern "C" {
 /* Exact-match compatibility contract [p1 API contract]: bumped on any
  * incompatible signature, pointer-layout, workspace, residual-encoding or
  * overflow-semantics change. Consumers must require an exact value. */
-#define EXL3_ABI_VERSION 2
+#define EXL3_ABI_VERSION 3
 
 enum exl3_dtype {
   EXL3_F16 = 1, EXL3_BF16 = 2, EXL3_F32 = 3, EXL3_I32 = 4, EXL3_I64 = 5
@@ -69,7 +69,9 @@ enum exl3_status {
   EXL3_E_WORKSPACE = -6, /* workspace NULL or smaller than *_workspace_size */
   EXL3_E_ARG = -7,       /* scalar argument out of range (topk, stages,
                             capacity, experts, rows) */
-  EXL3_E_LAUNCH = -8     /* a kernel launch failed */
+  EXL3_E_LAUNCH = -8,    /* a kernel launch failed */
+  EXL3_E_SCRATCH = -9    /* exl3_moe_forward_static: the call needs more
+                            workspace than EXL3_STATIC_SCRATCH_BYTES */
 };
 
 /* Limits checked by validation. */
@@ -199,6 +201,29 @@ int32_t exl3_moe_forward(const uint16_t *x, int32_t x_dtype, int32_t rows,
                          int32_t out_dtype, int32_t capacity,
                          int32_t num_active_hint, void *ws, size_t ws_bytes,
                          void *stream);
+
+/*
+ * exl3_moe_forward for callers that cannot allocate device memory (code under
+ * hipGraph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without ws / ws_bytes. The workspace is the library's
+ * own static device array of EXL3_STATIC_SCRATCH_BYTES (32 MiB), which every
+ * GPU the library runs on holds until the process ends; this call allocates
+ * and frees nothing. A call whose exl3_moe_workspace_size() exceeds it
+ * returns EXL3_E_SCRATCH and enqueues nothing (32 MiB holds, for example,
+ * 64 rows x top-8 at hidden 4096 / intermediate 1536 with capacity = pairs).
+ * Every call on one GPU uses that GPU's one array: calls that can overlap on
+ * a GPU (different streams, or different host threads without ordering)
+ * race and give wrong results; order them on one stream. The array keeps the
+ * last call's contents; each call clears what it needs cleared. The status
+ * words are not readable through this entry point.
+ */
+#define EXL3_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int32_t exl3_moe_forward_static(const uint16_t *x, int32_t x_dtype, int32_t rows,
+                                const void *ids, int32_t ids_dtype, const void *w,
+                                int32_t w_dtype, int32_t topk, const exl3_proj *gate,
+                                const exl3_proj *up, const exl3_proj *down, void *out,
+                                int32_t out_dtype, int32_t capacity,
+                                int32_t num_active_hint, void *stream);
 
 /* Experts only, for callers that already hold route metadata (from
  * exl3_route_pack or equivalent) [p1 Summary: exl3_moe_additive]. */

@@ -29,9 +29,9 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert exl3.abi_version() == 2
+    assert exl3.abi_version() == 3
     L = exl3.lib()
-    for s in range(0, -9, -1):
+    for s in range(0, -10, -1):
         msg = L.exl3_status_string(s).decode()
         assert msg and msg != "unknown status"
     assert L.exl3_status_string(123).decode() == "unknown status"

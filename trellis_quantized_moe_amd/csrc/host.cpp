@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/exl3moe.h"
 #include "kernels.hpp"
@@ -213,7 +214,7 @@ int32_t validate_moe_device(const uint16_t *x, const exl3_proj *gate,
                             const exl3_proj *up, const exl3_proj *down, void *out,
                             void *ws) {
   for (const void *q : {(const void *)x, (const void *)out, (const void *)ws})
-    if (int32_t s = check_device(q)) return s;
+    if (q && check_device(q)) return EXL3_E_DEVICE;
   for (const exl3_proj *p : {gate, up, down})
     if (int32_t s = check_proj_device(p)) return s;
   return EXL3_OK;
@@ -440,6 +441,9 @@ const char *exl3_status_string(int32_t s) {
     case EXL3_E_WORKSPACE: return "workspace missing or too small";
     case EXL3_E_ARG: return "argument out of range";
     case EXL3_E_LAUNCH: return "kernel launch failed";
+    case EXL3_E_SCRATCH:
+      return "call needs a larger workspace than the static scratch of exl3_moe_forward_static "
+             "(EXL3_STATIC_SCRATCH_BYTES = 32 MiB); use exl3_moe_forward with a workspace";
     default: return "unknown status";
   }
 }
@@ -586,13 +590,20 @@ int32_t exl3_route_pack(const void *ids, int32_t ids_dtype, const void *w, int32
   return launch_pack(p, (hipStream_t)stream) == hipSuccess ? EXL3_OK : EXL3_E_LAUNCH;
 }
 
-int32_t exl3_moe_forward(const uint16_t *x, int32_t x_dtype, int32_t rows, const void *ids,
-                         int32_t ids_dtype,
-                         const void *w, int32_t w_dtype, int32_t topk, const exl3_proj *gate,
-                         const exl3_proj *up, const exl3_proj *down, void *out,
-                         int32_t out_dtype, int32_t capacity, int32_t num_active_hint,
-                         void *ws, size_t ws_bytes, void *stream) {
-  (void)num_active_hint;
+}  // extern "C"
+
+namespace {
+
+// exl3_moe_forward with the workspace either the caller's (checked like any
+// other argument) or the library's own static scratch (ws_is_scratch: its
+// address comes from hipGetSymbolAddress, not from an allocation, so it is
+// not given to hipPointerGetAttributes). ws_bytes of 0 with ws_is_scratch
+// means "the call does not fit the scratch".
+int32_t moe_forward_impl(const uint16_t *x, int32_t x_dtype, int32_t rows, const void *ids,
+                         int32_t ids_dtype, const void *w, int32_t w_dtype, int32_t topk,
+                         const exl3_proj *gate, const exl3_proj *up, const exl3_proj *down,
+                         void *out, int32_t out_dtype, int32_t capacity, void *ws,
+                         size_t ws_bytes, void *stream, bool ws_is_scratch) {
   if (rows < 0) return EXL3_E_ARG;
   if (rows == 0) return EXL3_OK;
   if (int32_t s = validate_moe_common(x, x_dtype, rows, topk, gate, up, down, out, out_dtype,
@@ -605,8 +616,9 @@ int32_t exl3_moe_forward(const uint16_t *x, int32_t x_dtype, int32_t rows, const
     return EXL3_E_ALIGN;
   const int H = gate->in_features, I = gate->out_features, E = gate->num_experts;
   const MoeLayout L = moe_layout(rows, topk, E, H, I, capacity);
-  if (ws_bytes < L.total) return EXL3_E_WORKSPACE;
-  if (int32_t s = validate_moe_device(x, gate, up, down, out, ws)) return s;
+  if (ws_bytes < L.total) return ws_is_scratch ? EXL3_E_SCRATCH : EXL3_E_WORKSPACE;
+  if (int32_t s = validate_moe_device(x, gate, up, down, out, ws_is_scratch ? nullptr : ws))
+    return s;
   for (const void *q : {ids, w})
     if (int32_t s = check_device(q)) return s;
 
@@ -649,6 +661,66 @@ int32_t exl3_moe_forward(const uint16_t *x, int32_t x_dtype, int32_t rows, const
   }
   return run_experts(x, x_dtype, rows, topk, gate, up, down, out, out_dtype, L, ws, p.pair_of_pos,
                      p.pos_of_pair, p.weight_of_pos, p.offset, st, fuse ? &p : nullptr);
+}
+
+// ------------------------------------------------ static scratch workspace
+// The workspace of exl3_moe_forward_static: a file-scope device array, so
+// calls through that entry point allocate nothing. The runtime gives every
+// device that loads this library its own copy. In host code `scratch` names
+// a host-side stand-in, not device memory: its device address is taken once
+// per device with hipGetSymbolAddress (on that device's first call, with the
+// device current) and only that address is passed on.
+static __device__ __align__(256) char scratch[EXL3_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array, nullptr on failure.
+void *scratch_ptr(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      ptr = nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  });
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t exl3_moe_forward(const uint16_t *x, int32_t x_dtype, int32_t rows, const void *ids,
+                         int32_t ids_dtype,
+                         const void *w, int32_t w_dtype, int32_t topk, const exl3_proj *gate,
+                         const exl3_proj *up, const exl3_proj *down, void *out,
+                         int32_t out_dtype, int32_t capacity, int32_t num_active_hint,
+                         void *ws, size_t ws_bytes, void *stream) {
+  (void)num_active_hint;
+  return moe_forward_impl(x, x_dtype, rows, ids, ids_dtype, w, w_dtype, topk, gate, up, down,
+                          out, out_dtype, capacity, ws, ws_bytes, stream, false);
+}
+
+int32_t exl3_moe_forward_static(const uint16_t *x, int32_t x_dtype, int32_t rows,
+                                const void *ids, int32_t ids_dtype, const void *w,
+                                int32_t w_dtype, int32_t topk, const exl3_proj *gate,
+                                const exl3_proj *up, const exl3_proj *down, void *out,
+                                int32_t out_dtype, int32_t capacity, int32_t num_active_hint,
+                                void *stream) {
+  (void)num_active_hint;
+  if (rows < 0) return EXL3_E_ARG;
+  if (rows == 0) return EXL3_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return EXL3_E_DEVICE;
+  void *ws = scratch_ptr(dev);
+  if (!ws) return EXL3_E_DEVICE;
+  return moe_forward_impl(x, x_dtype, rows, ids, ids_dtype, w, w_dtype, topk, gate, up, down,
+                          out, out_dtype, capacity, ws, EXL3_STATIC_SCRATCH_BYTES, stream,
+                          true);
 }
 
 int32_t exl3_moe_additive(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t topk,

@@ -65,6 +65,9 @@ _SIGS = {
                                 ctypes.POINTER(ProjC), ctypes.POINTER(ProjC),
                                 ctypes.POINTER(ProjC), _vp, _i32, _i32, _i32, _vp, _sz,
                                 _vp]),
+    "exl3_moe_forward_static": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32,
+                                       ctypes.POINTER(ProjC), ctypes.POINTER(ProjC),
+                                       ctypes.POINTER(ProjC), _vp, _i32, _i32, _i32, _vp]),
     "exl3_moe_additive": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(MetaC),
                                  ctypes.POINTER(ProjC), ctypes.POINTER(ProjC),
                                  ctypes.POINTER(ProjC), _vp, _i32, _i32, _i32, _vp, _sz,
@@ -244,6 +247,23 @@ def exl3_moe_forward(x, ids, w, gate, up, down, capacity, out_dtype=torch.float3
                                   num_active_hint,
                                   _p(ws), ws.numel(), _stream()))
     return out
+
+
+def exl3_moe_forward_static(x, ids, w, gate, up, down, capacity, out_dtype=torch.float32,
+                            out=None, num_active_hint=-1):
+    """exl3_moe_forward on the library's static scratch (no workspace)."""
+    rows, topk = ids.shape
+    out = out if out is not None else torch.empty(rows, down.out_features, dtype=out_dtype,
+                                                  device=x.device)
+    g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
+    _check(lib().exl3_moe_forward_static(_p(x), _dt(x), rows, _p(ids), _DT[ids.dtype], _p(w),
+                                         _DT[w.dtype], topk, ctypes.byref(g), ctypes.byref(u),
+                                         ctypes.byref(d), _p(out), _DT[out.dtype], capacity,
+                                         num_active_hint, _stream()))
+    return out
+
+
+STATIC_SCRATCH_BYTES = 32 << 20
 
 
 def exl3_moe_additive(x, topk, meta, gate, up, down, capacity, out_dtype=torch.float32,
