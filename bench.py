@@ -5,7 +5,7 @@ SwiGLU, down GEMM, ordered combine) over one batch of synthetic input that is
 already resident in HBM. The headline workload is the mixed-width prefill
 layer (192 experts, top-8, hidden 6144, intermediate 2048, K per expert in
 {3,4,5,6,8}, 3072 rows, Zipf(1.2) routing, capacity 2048 pairs). The decode
-layer (128 experts, top-8, hidden 4096, intermediate 1536, K=4) at 1 and 32
+layer (128 experts, top-8, hidden 4096, intermediate 1536, K=4) at 1, 8 and 32
 rows is reported alongside, timed by hipGraph replay over rotating routings,
 and so are the additive layer (256 experts, base K=3 plus a K=2 residual
 stage, 128 rows) and the plain 4096 -> 4096 linear at K = 2, 3, 4, 8 and 1,
@@ -44,6 +44,18 @@ def _kernel_stats(records):
         s[1] += ms
     return {k: {"launches": n, "total_ms": t, "avg_us": 1000.0 * t / n}
             for k, (n, t) in st.items()}
+
+
+def check_status(ws, dropped, what):
+    """The library's status words of the last call on this workspace (ctrl[0]
+    pairs left out, ctrl[1] skipped stage entries, ctrl[2] device waits that
+    gave up) must read (dropped, 0, 0): otherwise the timed result is not a
+    valid layer output."""
+    import torch
+    torch.cuda.synchronize()
+    c = [int(v) for v in ws[:12].view(torch.int32).cpu()]
+    if c != [dropped, 0, 0]:
+        raise RuntimeError("%s: status words %s, expected [%d, 0, 0]" % (what, c, dropped))
 
 
 def prefill_step_flops(wl):
@@ -90,6 +102,7 @@ def run_prefill(args, torch, exl3, synth, **over):
         t_stop.record()
         torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_stop) / args.steps
+    check_status(ws, int(np.sum((wl.ids < 0) | (wl.ids >= wl.num_experts))), "prefill")
     _log("prefill: %.1f us per layer" % (1000 * ms))
     kstats = _kernel_stats(prof.records)
     flops = prefill_step_flops(wl)
@@ -110,6 +123,13 @@ def run_prefill(args, torch, exl3, synth, **over):
 
 
 def run_decode(args, torch, exl3, synth, M, groups=16, **over):
+    """The decode layer (128 experts, top-8, hidden 4096, intermediate 1536,
+    K=4) at M rows. `groups` routings are drawn; one captured graph holds one
+    layer call per routing, so a replay streams the experts of 16 different
+    routings (together about all 1.2 GB of weights, far more than the 256 MB
+    MALL) and the host's cost per graph replay is spread over 16 layers.
+    Layer time = replay time / 16. Per-kernel durations come from eager calls
+    over the same routings (HIP events around each launch)."""
     wl = synth.moe_workload("decode", rows=M, **over)
     gate, up, down = (exl3.DeviceProj(p, "cuda") for p in (wl.gate, wl.up, wl.down))
     x, _, _ = exl3.device_inputs(wl, "cuda")
@@ -130,27 +150,25 @@ def run_decode(args, torch, exl3, synth, M, groups=16, **over):
     for r in routings:
         call(r)
     torch.cuda.synchronize()
-    # one captured graph per routing: replays stream different experts
-    graphs = []
     side = torch.cuda.Stream()
-    for r in routings:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side, capture_error_mode="relaxed"):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side, capture_error_mode="relaxed"):
+        for r in routings:
             call(r)
-        graphs.append(g)
     torch.cuda.synchronize()
-    steps = max(args.steps, 4 * groups)
-    for i in range(groups):
-        graphs[i].replay()
+    reps = max(4, args.steps)
+    for _ in range(2):
+        g.replay()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
-    for i in range(steps):
-        graphs[i % groups].replay()
+    for _ in range(reps):
+        g.replay()
     b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+    ms = a.elapsed_time(b) / (reps * groups)
+    check_status(ws, 0, "decode M=%d" % M)
     # per-kernel durations from eager launches over the same routings
     with exl3.Profile(max_launches=16 * groups * 4) as prof:
         for _ in range(4):
@@ -158,25 +176,27 @@ def run_decode(args, torch, exl3, synth, M, groups=16, **over):
                 call(r)
         torch.cuda.synchronize()
     kst = _kernel_stats(prof.records)
-    # algorithmic HBM bytes of the gate/up GEMM: the trellis of every active
-    # expert's gate and up projection (read once: <= 16 pairs per expert),
-    # plus its rotated inputs and a~ outputs
+    # algorithmic HBM bytes: the trellis of every active expert's gate, up and
+    # down projection (each read once), the input rows, the rotated inputs
+    # x~ (written and read), a~ (written and read), d (written and read) and
+    # the output
     per_tensor = wl.hidden * wl.intermediate * 4 // 8
     act = [len(np.unique(r[0])) for r in routings]
-    gu_bytes = np.mean([2 * per_tensor * n for n in act]) + M * wl.topk * (
-        2 * wl.hidden * 2 + wl.intermediate * 2)
-    dn_bytes = np.mean([per_tensor * n for n in act]) + M * wl.topk * (
-        wl.intermediate * 2 + wl.hidden * 4)
-    layer_bytes = gu_bytes + dn_bytes
-    return {
-        "rows": M, "us": 1000 * ms, "tokens_per_s": M / (ms * 1e-3), "graph_replays": steps,
-        "kernels": kst,
-        "gemm_gateup_GBps": gu_bytes / (kst["gemm_gateup"]["avg_us"] * 1e-6) / 1e9,
-        "gemm_down_GBps": dn_bytes / (kst["gemm_down"]["avg_us"] * 1e-6) / 1e9,
+    P = M * wl.topk
+    trellis = np.mean([3 * per_tensor * n for n in act])
+    acts = (M * wl.hidden * 2 + P * (2 * wl.hidden * 2) * 2 + P * wl.intermediate * 2 * 2
+            + P * wl.hidden * 4 * 2 + M * wl.hidden * 2)
+    layer_bytes = trellis + acts
+    res = {
+        "rows": M, "us": 1000 * ms, "tokens_per_s": M / (ms * 1e-3),
+        "graph": "%d layer calls per replay, %d replays" % (groups, reps),
+        "kernels": kst, "algorithmic_bytes": layer_bytes, "trellis_bytes": trellis,
         "layer_GBps": layer_bytes / (ms * 1e-3) / 1e9,
         "layer_hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "algorithmic_bytes": {"gemm_gateup": gu_bytes, "gemm_down": dn_bytes},
     }
+    if "gemm_experts" in kst:
+        res["gemm_experts_GBps"] = trellis / (kst["gemm_experts"]["avg_us"] * 1e-6) / 1e9
+    return res
 
 
 def run_linear(args, torch, exl3, synth, Ks=(2, 3, 4, 8), Ms=(1, 32, 2048), reps=48):
@@ -250,6 +270,7 @@ def run_additive(args, torch, exl3, synth, reps=20):
     b.record()
     torch.cuda.synchronize()
     us = 1000.0 * a.elapsed_time(b) / reps
+    check_status(ws, int((meta["pos_of_pair"][:wl.rows * wl.topk] < 0).sum()), "additive")
     with exl3.Profile(max_launches=8 * 4) as prof:
         for _ in range(4):
             call()
@@ -334,6 +355,9 @@ def main():
                     help="skip the 4-way tensor-parallel shard shapes (intermediate / 4)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated parts to run, for profiling: prefill, decode1, "
+                         "decode8, decode32, additive, linear (no JSON line)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="JSON with measured HBM bytes per launch of the dominant kernel")
     args = ap.parse_args()
@@ -355,10 +379,25 @@ def main():
         copy_probe(torch)
         return
 
+    if args.only:
+        parts = set(args.only.split(","))
+        res = {}
+        if "prefill" in parts:
+            res["prefill"] = run_prefill(args, torch, exl3, synth)[1]
+        for M in (1, 8, 32):
+            if "decode%d" % M in parts:
+                res["decode_M%d" % M] = run_decode(args, torch, exl3, synth, M)
+        if "additive" in parts:
+            res["additive"] = run_additive(args, torch, exl3, synth)
+        if "linear" in parts:
+            res["linear"] = run_linear(args, torch, exl3, synth)
+        print(json.dumps({"only": sorted(parts), "results": res}), flush=True)
+        return
+
     wl, pre = run_prefill(args, torch, exl3, synth)
     extra = {"prefill": pre}
     if not args.no_decode:
-        for M in (1, 32):
+        for M in (1, 8, 32):
             _log("decode M=%d" % M)
             extra["decode_M%d" % M] = run_decode(args, torch, exl3, synth, M)
         _log("additive layer")

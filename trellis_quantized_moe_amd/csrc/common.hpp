@@ -253,18 +253,23 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
-// Loads of per-workgroup / per-wave table entries, forced into SGPRs.
-__device__ __forceinline__ int uload_i32(const int32_t *a) {
-  return __builtin_amdgcn_readfirstlane(*a);
+// Loads of per-workgroup / per-wave table entries (plan tiles, stage
+// tables) as scalar loads: the address is made uniform and read through the
+// constant address space, so the value lands in SGPRs through the scalar
+// cache. Only for data written before the kernel started (the scalar cache is
+// not coherent with stores of the same launch).
+template <typename T>
+__device__ __forceinline__ T sload(const T *a) {
+  const uint64_t b = (uint64_t)(uintptr_t)a;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  typedef const T __attribute__((address_space(4))) *cptr;
+  return *(cptr)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
-__device__ __forceinline__ float uload_f32(const float *a) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, *a)));
-}
+__device__ __forceinline__ int uload_i32(const int32_t *a) { return sload(a); }
+__device__ __forceinline__ float uload_f32(const float *a) { return sload(a); }
 __device__ __forceinline__ const uint32_t *uload_ptr(const int64_t *a) {
-  const int64_t v = *a;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-  return (const uint32_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return (const uint32_t *)(uintptr_t)sload(a);
 }
 
 // -------------------------------------------------------------------- MFMA

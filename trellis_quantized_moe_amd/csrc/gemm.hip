@@ -53,6 +53,9 @@ namespace exl3 {
 // the shared epilogue on the whole block.
 constexpr int kNRing = 4;
 constexpr int kNSlot = 2048;  // bytes: one block at K <= 8
+// LDS offset of the staged epilogue vectors (after the 2 x 16 x 132 fp32
+// accumulator tile of the epilogue; the ring is free by then)
+constexpr int kEpiVecOff = 2 * 16 * 132 * 4;
 
 template <int K>
 struct StreamGeom {
@@ -89,21 +92,38 @@ __device__ __forceinline__ void swait_vmcnt() {
 // The 4 A fragments of one block (16 bytes each, 64 bytes apart) into
 // registers, on the lanes in `lanes` only (rows past the tile's end are never
 // loaded: their MFMA output rows are discarded). Invisible to the compiler's
-// wait counting: the chain's own vmcnt waits cover it (see a_wait).
+// wait counting: the chain's own vmcnt waits cover it (see a_wait). COH:
+// device-coherent loads (sc1), for rows another workgroup of the same launch
+// wrote.
+template <bool COH>
 __device__ __forceinline__ void aload_block(u32x4 &a0, u32x4 &a1, u32x4 &a2, u32x4 &a3,
                                             uint32_t voff, const char *sbase, uint64_t lanes) {
   uint64_t saved;
-  asm volatile(
-      "s_mov_b64 %4, exec\n\t"
-      "s_and_b64 exec, exec, %7\n\t"
-      "global_load_dwordx4 %0, %5, %6 offset:0\n\t"
-      "global_load_dwordx4 %1, %5, %6 offset:64\n\t"
-      "global_load_dwordx4 %2, %5, %6 offset:128\n\t"
-      "global_load_dwordx4 %3, %5, %6 offset:192\n\t"
-      "s_mov_b64 exec, %4"
-      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lanes)
-      : "memory", "scc");
+  if constexpr (COH) {
+    asm volatile(
+        "s_mov_b64 %4, exec\n\t"
+        "s_and_b64 exec, exec, %7\n\t"
+        "global_load_dwordx4 %0, %5, %6 offset:0 sc1\n\t"
+        "global_load_dwordx4 %1, %5, %6 offset:64 sc1\n\t"
+        "global_load_dwordx4 %2, %5, %6 offset:128 sc1\n\t"
+        "global_load_dwordx4 %3, %5, %6 offset:192 sc1\n\t"
+        "s_mov_b64 exec, %4"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lanes)
+        : "memory", "scc");
+  } else {
+    asm volatile(
+        "s_mov_b64 %4, exec\n\t"
+        "s_and_b64 exec, exec, %7\n\t"
+        "global_load_dwordx4 %0, %5, %6 offset:0\n\t"
+        "global_load_dwordx4 %1, %5, %6 offset:64\n\t"
+        "global_load_dwordx4 %2, %5, %6 offset:128\n\t"
+        "global_load_dwordx4 %3, %5, %6 offset:192\n\t"
+        "s_mov_b64 exec, %4"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lanes)
+        : "memory", "scc");
+  }
 }
 
 // Wait until at most N vector loads are outstanding; the A registers of the
@@ -124,7 +144,7 @@ __device__ __forceinline__ const char *sgpr_ptr(const void *ptr) {
 // P = MFMA chain of one stage over all inputs for this wave's strip.
 constexpr int kNADist = kNRing - 2;  // A blocks in flight ahead of the one in use
 
-template <int K>
+template <int K, bool COH>
 struct StreamChain {
   using G = StreamGeom<K>;
   static constexpr int ND = HalfGeom<K>::kLoadDw, NN = HalfGeom<K>::kNormDw;
@@ -146,7 +166,7 @@ struct StreamChain {
 
   __device__ __forceinline__ void load_a(int ba, int aslot) {
     const char *src = sgpr_ptr(abase + (size_t)ba * 256);
-    aload_block(a[aslot][0], a[aslot][1], a[aslot][2], a[aslot][3], avoff, src, alanes);
+    aload_block<COH>(a[aslot][0], a[aslot][1], a[aslot][2], a[aslot][3], avoff, src, alanes);
   }
   __device__ __forceinline__ void issue(int b, int aslot) {
     const int last = nblk - 1;
@@ -209,11 +229,11 @@ struct StreamChain {
   }
 };
 
-template <int K>
+template <int K, bool COH>
 __device__ __forceinline__ f32x4 stream_chain(const char *strip, int in_f, const char *ring,
                                               const char *abase, uint32_t avoff, uint64_t alanes,
                                               int lane) {
-  StreamChain<K> c;
+  StreamChain<K, COH> c;
   c.alanes = alanes;
   const int g = lane >> 4;
   c.strip = sgpr_ptr(strip);
@@ -226,12 +246,13 @@ __device__ __forceinline__ f32x4 stream_chain(const char *strip, int in_f, const
   const HalfWindow<K> hw(lane);
   c.shift = hw.shift;
 #pragma unroll
-  for (int j = 0; j < StreamChain<K>::ND; ++j) c.traddr[j] = hw.off[j];
+  for (int j = 0; j < StreamChain<K, COH>::ND; ++j) c.traddr[j] = hw.off[j];
   c.mask = codebook_mask();
   return c.run();
 }
 
 // Stage loop of one projection for one wave: acc = sum fmaf(s_t, P_t, acc).
+template <bool COH>
 __device__ __forceinline__ f32x4 stream_strip(const ProjDev &pd, int E, int e, int in_f, int nt,
                                               const char *ring, const char *abase,
                                               uint32_t avoff, uint64_t alanes, int lane,
@@ -249,13 +270,13 @@ __device__ __forceinline__ f32x4 stream_strip(const ProjDev &pd, int E, int e, i
     const char *strip = tens + (size_t)nt * (in_f / 16) * 32 * K;
     f32x4 q;
     switch (K) {
-      case 2: q = stream_chain<2>(strip, in_f, ring, abase, avoff, alanes, lane); break;
-      case 3: q = stream_chain<3>(strip, in_f, ring, abase, avoff, alanes, lane); break;
-      case 4: q = stream_chain<4>(strip, in_f, ring, abase, avoff, alanes, lane); break;
-      case 5: q = stream_chain<5>(strip, in_f, ring, abase, avoff, alanes, lane); break;
-      case 6: q = stream_chain<6>(strip, in_f, ring, abase, avoff, alanes, lane); break;
-      case 7: q = stream_chain<7>(strip, in_f, ring, abase, avoff, alanes, lane); break;
-      default: q = stream_chain<8>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      case 2: q = stream_chain<2, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      case 3: q = stream_chain<3, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      case 4: q = stream_chain<4, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      case 5: q = stream_chain<5, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      case 6: q = stream_chain<6, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      case 7: q = stream_chain<7, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      default: q = stream_chain<8, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] = fmaf(s, q[r], acc[r]);
@@ -263,21 +284,139 @@ __device__ __forceinline__ f32x4 stream_strip(const ProjDev &pd, int E, int e, i
   return acc;
 }
 
-// grid: x = tile, y = NPROJ * (out_f / 64) column groups (projection major).
-template <int EPI>
-__global__ void __launch_bounds__(256, 4) gemm_narrow_kernel(GemmParams p) {
-  constexpr int NPROJ = (EPI == EPI_GATEUP) ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) char smem[4 * kNRing * kNSlot];
-  __shared__ int s_last;
+// DMA every block of this wave's strip, for every live stage, into its ring
+// slots without waiting: the data is not used from LDS (the chain copies
+// each block again) but is then held in the caches, so a work item that must
+// wait for its inputs streams its trellis from HBM while it waits. The caller
+// waits for these copies (vmcnt 0) before the chain reuses the ring.
+__device__ __forceinline__ void prefetch_strip(const ProjDev &pd, int E, int e, int in_f, int nt,
+                                               const char *ring, int lane) {
+  const uint32_t ring_lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)ring);
+  for (int t = 0; t < pd.num_stages; ++t) {
+    const float sc = uload_f32(pd.scale + t * E + e);
+    const char *tens = (const char *)uload_ptr(pd.trellis + t * E + e);
+    const int K = uload_i32(pd.bits + t * E + e);
+    if (sc == 0.0f || tens == nullptr || K < 2 || K > 8) continue;
+    const int blk = 256 * K;  // bytes per 128-input block of the strip
+    const char *strip = tens + (size_t)nt * (in_f / 16) * 32 * K;
+    const int nblk = in_f >> 7;
+    for (int b = 0; b < nblk; ++b) {
+      const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)(ring_lds + (uint32_t)((b % kNRing) * kNSlot)));
+      const char *src = sgpr_ptr(strip + (size_t)b * blk);
+      // lanes past the block's end re-read its last 16 bytes (in bounds)
+      for (int off = 0; off < blk; off += 1024)
+        sdma16((uint32_t)min(16 * lane, blk - off - 16), src + off, dst + off, ~0ull);
+    }
+  }
+}
 
+// Ordered combine at the end of a fused down item (single pass, 16-row
+// tiles). After its d block (128 columns `blk` of every row of the tile) is
+// written and its stores are complete, the item counts that block once for
+// the output row of each of its tile rows; the count that completes a
+// (row, block) (one per kept pair of the row) makes this item sum d over the
+// row's positions in ascending order, from 0 in fp32, and write that output
+// block. The additions are those of the combine kernels, in the same order.
+// s_tmp: 2 * kMaxTopk ints of free LDS; s_rows: kBM ints.
+__device__ __forceinline__ void narrow_combine(const GemmParams &p, const NarrowFusedParams &f,
+                                               int row0, int nrows, int blk, int *s_rows,
+                                               int *s_tmp) {
+  const int nhb = p.out_f >> 7;
+  const int end = min(*f.total_valid, f.pairs);
+  if ((int)threadIdx.x < nrows) {
+    const int q = f.pair_of_pos[p.pass_base + row0 + threadIdx.x];
+    int r = -1;
+    if (q >= 0 && q < f.pairs) {
+      r = q / f.topk;
+      int kept = 0;
+      for (int j = 0; j < f.topk; ++j) {
+        const int pp = f.pos_of_pair[r * f.topk + j];
+        kept += (pp >= 0 && pp < end) ? 1 : 0;
+      }
+      const int c = __hip_atomic_fetch_add(f.row_cnt + (int64_t)r * nhb + blk, 1,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (c != kept - 1) r = -1;
+    }
+    s_rows[threadIdx.x] = r;
+  }
+  __syncthreads();
+  int *s_pp = s_tmp, *s_sorted = s_tmp + kMaxTopk;
+  for (int t = 0; t < nrows; ++t) {
+    const int r = s_rows[t];  // uniform
+    if (r < 0) continue;
+    if ((int)threadIdx.x < f.topk) s_pp[threadIdx.x] = f.pos_of_pair[r * f.topk + threadIdx.x];
+    __syncthreads();
+    // the row's kept positions in ascending order: each pair writes its
+    // position at its rank (ties, possible only in inconsistent caller
+    // metadata, ranked by pair index)
+    int n = 0;
+    for (int j = 0; j < f.topk; ++j) {
+      const int v = s_pp[j];
+      n += (v >= 0 && v < end) ? 1 : 0;
+    }
+    if ((int)threadIdx.x < f.topk) {
+      const int pp = s_pp[threadIdx.x];
+      if (pp >= 0 && pp < end) {
+        int rank = 0;
+        for (int j = 0; j < f.topk; ++j) {
+          const int v = s_pp[j];
+          rank += (v >= 0 && v < end && (v < pp || (v == pp && j < (int)threadIdx.x))) ? 1 : 0;
+        }
+        s_sorted[rank] = pp;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 128) {
+      const int col = blk * 128 + threadIdx.x;
+      float v[kMaxTopk];
+#pragma unroll
+      for (int k = 0; k < kMaxTopk; ++k)
+        if (k < n)  // every load in flight together
+          v[k] = __hip_atomic_load(p.out_f32 + (int64_t)s_sorted[k] * p.ldo + col,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      float y = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kMaxTopk; ++k)
+        if (k < n) y += v[k];
+      const int64_t o = (int64_t)r * p.out_f + col;
+      if (f.out_f32) ((float *)f.out)[o] = y;
+      else ((uint16_t *)f.out)[o] = f32_to_out16(y, f.out_bf16);
+    }
+    __syncthreads();  // s_pp / s_sorted reused for the next row
+  }
+}
+
+// One work item of the 16-row kernels: rows of plan tile `bx` times the
+// 64-column group `by` (for gate/up, by < out_f / 64 is gate, the rest up).
+// FUSED (every kernel of a single pass in one launch, experts_narrow_kernel):
+//  - gate/up: the last item of a 128-column block writes its a~ block with
+//    device-coherent stores, waits for them, then counts the block in
+//    f.tile_ready[bx];
+//  - down: the item first prefetches its trellis (prefetch_strip), then waits
+//    until every a~ block of its tile is counted and reads a~ with
+//    device-coherent loads; the last item of a 128-column block writes d
+//    with device-coherent stores and counts the block for each row of the
+//    tile in f.row_cnt; the count that completes a row's block (one per kept
+//    pair of the row) makes this item sum the row's d in ascending position
+//    for that block and write the output (the ordered combine).
+// Every wait is on items of lower id (gate/up before down), which were
+// dispatched earlier on their XCD and never wait themselves, so it ends; it
+// is also bounded, a give-up counted in ctrl[2].
+template <int EPI, bool FUSED>
+__device__ __forceinline__ void narrow_item(const GemmParams &p, char *smem, int *s_flag, int bx,
+                                            int by, const NarrowFusedParams *f) {
+  constexpr int NPROJ = (EPI == EPI_GATEUP) ? 2 : 1;
+  constexpr bool kCohA = FUSED && EPI == EPI_DOWN;
   int e, row0, nrows;
-  if (!tile_of_block(p, kBM, blockIdx.x, e, row0, nrows)) return;
+  if (!tile_of_block(p, kBM, bx, e, row0, nrows)) return;
   const int ncg = p.out_f >> 6;
-  const int pj = (EPI == EPI_GATEUP) ? (int)(blockIdx.y / ncg) : 0;
-  const int cg = blockIdx.y - pj * ncg;
+  const int pj = (EPI == EPI_GATEUP) ? by / ncg : 0;
+  const int cg = by - pj * ncg;
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
   const int nt = cg * 4 + w;
+  char *ring = smem + w * kNRing * kNSlot;
 
   // Lanes of rows past the tile's end read the last valid row (same cache
   // lines, no extra traffic); their results are never stored.
@@ -289,9 +428,47 @@ __global__ void __launch_bounds__(256, 4) gemm_narrow_kernel(GemmParams p) {
   const uint64_t rows16 = (nrows >= 16) ? 0xFFFFull : ((1ull << nrows) - 1);
   const uint64_t alanes = rows16 | (rows16 << 16) | (rows16 << 32) | (rows16 << 48);
   const ProjDev pd = (pj == 0) ? p.proj[0] : p.proj[1];
-  const f32x4 acc = stream_strip(pd, p.E, e, p.in_f, nt, smem + w * kNRing * kNSlot,
-                                 (const char *)a_tile, avoff, alanes, lane, p.ctrl,
-                                 cg == 0 && w == 0);
+
+  // The epilogue's per-column vectors of this item's 128-column block (and
+  // the route weights of the tile's rows), loaded now so their latency hides
+  // under the chain; staged in LDS if this item runs the epilogue.
+  const int blk = cg >> 1;
+  const int tc = threadIdx.x & 127;
+  const size_t vb = (size_t)e * p.out_f + blk * 128 + tc;
+  uint16_t v_svh0 = 0, v_cs0 = 0, v_svh1 = 0, v_cs1 = 0, v_suh = 0;
+  float v_wt = 0.0f;
+  if (threadIdx.x < 128) {
+    v_svh0 = p.proj[0].svh[vb];
+    v_cs0 = p.proj[0].cs[vb];
+    if constexpr (EPI == EPI_GATEUP) {
+      v_svh1 = p.proj[1].svh[vb];
+      v_cs1 = p.proj[1].cs[vb];
+      v_suh = p.suh_down[vb];
+    }
+  } else if constexpr (EPI == EPI_DOWN) {
+    if ((int)threadIdx.x - 128 < nrows) v_wt = p.weight_of_pos[p.pass_base + row0 + threadIdx.x - 128];
+  }
+
+  if constexpr (FUSED && EPI == EPI_DOWN) {
+    prefetch_strip(pd, p.E, e, p.in_f, nt, ring, lane);
+    if (threadIdx.x == 0) {
+      const int need = f->gu.out_f >> 7;  // a~ blocks of the tile
+      int spins = 0;
+      while (__hip_atomic_load(f->tile_ready + bx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+             need) {
+        if (++spins > (1 << 22)) {
+          atomicAdd(p.ctrl + 2, 1);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+    }
+    __syncthreads();
+    swait_vmcnt<0>();  // the prefetch copies have landed before the ring is reused
+  }
+
+  const f32x4 acc = stream_strip<kCohA>(pd, p.E, e, p.in_f, nt, ring, (const char *)a_tile, avoff,
+                                        alanes, lane, p.ctrl, cg == 0 && w == 0);
 
   // Pre-rotation sums of this work item -> scratch [row][NPROJ][out_f].
   // Hand-off to the last work item of the 128-column block without cache
@@ -310,29 +487,100 @@ __global__ void __launch_bounds__(256, 4) gemm_narrow_kernel(GemmParams p) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  const int blk = cg >> 1;
-  int32_t *cnt = p.ncnt + (int64_t)blockIdx.x * (p.out_f >> 7) + blk;
+  int32_t *cnt = p.ncnt + (int64_t)bx * (p.out_f >> 7) + blk;
   if (threadIdx.x == 0)
-    s_last = (__hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              2 * NPROJ - 1)
-                 ? 1
-                 : 0;
+    *s_flag = (__hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               2 * NPROJ - 1)
+                  ? 1
+                  : 0;
   __syncthreads();
-  if (!s_last) return;
+  if (!*s_flag) return;
   if (threadIdx.x == 0)  // ready for the next launch
     __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   float *T = (float *)smem;  // [NPROJ][16][kLdsStride]
-  for (int i = threadIdx.x; i < NPROJ * kBM * 128; i += blockDim.x) {
+  // every item's sums of the block, all loads in flight together
+  constexpr int kPer = NPROJ * kBM * 128 / 256;
+  float sums[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = threadIdx.x + 256 * k;
     const int q = i / (kBM * 128), rem = i - q * (kBM * 128);
     const int row = rem >> 7, c = rem & 127;
-    T[(q * kBM + row) * kLdsStride + c] =
-        row < nrows ? __hip_atomic_load(p.nacc + (int64_t)(row0 + row) * ldn + q * p.out_f +
-                                            blk * 128 + c,
-                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                    : 0.0f;
+    sums[k] = row < nrows ? __hip_atomic_load(p.nacc + (int64_t)(row0 + row) * ldn +
+                                                  q * p.out_f + blk * 128 + c,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    const int q = i / (kBM * 128), rem = i - q * (kBM * 128);
+    T[(q * kBM + (rem >> 7)) * kLdsStride + (rem & 127)] = sums[k];
+  }
+  // staged vectors, past the accumulator tile
+  uint16_t *lv = (uint16_t *)(smem + kEpiVecOff);
+  float *lwt = (float *)(smem + kEpiVecOff + 5 * 128 * 2);
+  if (threadIdx.x < 128) {
+    lv[tc] = v_svh0;
+    lv[128 + tc] = v_cs0;
+    lv[256 + tc] = v_svh1;
+    lv[384 + tc] = v_cs1;
+    lv[512 + tc] = v_suh;
+  } else if ((int)threadIdx.x - 128 < kBM) {
+    lwt[threadIdx.x - 128] = v_wt;
   }
   __syncthreads();
-  epilogue<EPI>(p, T, kLdsStride, kBM * kLdsStride, e, row0, nrows, blk * 128, 1);
+  EpiVec ev;
+  ev.v = lv;
+  ev.wt = lwt;
+  epilogue<EPI, FUSED, true>(p, T, kLdsStride, kBM * kLdsStride, e, row0, nrows, blk * 128, 1,
+                             ev);
+  if constexpr (FUSED) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's a~ / d stores
+    __syncthreads();                                     // ... and every wave's
+    if constexpr (EPI == EPI_GATEUP) {
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(f->tile_ready + bx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      narrow_combine(p, *f, row0, nrows, blk, s_flag + 1, (int *)smem);
+    }
+  }
+}
+
+// grid: x = tile, y = NPROJ * (out_f / 64) column groups (projection major).
+template <int EPI>
+__global__ void __launch_bounds__(256, 4) gemm_narrow_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[4 * kNRing * kNSlot];
+  __shared__ int s_flag[1];
+  narrow_item<EPI, false>(p, smem, s_flag, blockIdx.x, blockIdx.y, nullptr);
+}
+
+// A single pass of the routed experts on 16-row tiles in one launch: gate/up
+// work items (tile-major: tile x (2 x I/64) column groups), then down items
+// (tile x H/64 groups), each waiting only on gate/up items of its own tile;
+// the combine runs at the end of the down items (see narrow_item). The pack,
+// plan, rotation and the zeroing of every count come before, in stream order.
+__global__ void __launch_bounds__(256, 4) experts_narrow_kernel(NarrowFusedParams f) {
+  __shared__ __attribute__((aligned(16))) char smem[4 * kNRing * kNSlot];
+  __shared__ int s_flag[1 + kBM];
+  int id = blockIdx.x;
+  if (id < f.g1) {
+    const int per = 2 * (f.gu.out_f >> 6);
+    narrow_item<EPI_GATEUP, true>(f.gu, smem, s_flag, id / per, id % per, &f);
+    return;
+  }
+  id -= f.g1;
+  const int per = f.dn.out_f >> 6;
+  narrow_item<EPI_DOWN, true>(f.dn, smem, s_flag, id / per, id % per, &f);
+}
+
+hipError_t launch_experts_narrow(const NarrowFusedParams &f, hipStream_t s) {
+  if (f.tiles <= 0) return hipSuccess;
+  const int64_t g1 = (int64_t)f.tiles * 2 * (f.gu.out_f >> 6);
+  const int64_t g2 = (int64_t)f.tiles * (f.dn.out_f >> 6);
+  if (g1 != f.g1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(experts_narrow_kernel, dim3((unsigned)(g1 + g2)), dim3(256), 0, s, f);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks, hipStream_t s,

@@ -32,14 +32,35 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // was computed in. T is an LDS tile of fp32 pre-rotation accumulators:
 // T[pj * proj_stride + row * ld + c], c = 0 .. 128*nblk-1 (columns relative
 // to colbase). One 16-lane group handles one (row, 128-block) at a time.
-// COH: a~ (gate/up) is written with device-coherent stores, for a reader in
-// the same launch.
-template <int EPI, bool COH = false>
+// COH: a~ (gate/up) and d (down) are written with device-coherent stores, for
+// a reader in the same launch.
+// The per-column vectors of one 128-column block, staged in LDS by a caller
+// that loaded them ahead of time (16-row kernels): svh and chscale of gate
+// and up (or of the one projection), the down input signs (gate/up), and the
+// route weights of the tile's rows (down). Columns relative to colbase.
+// Layout at v (fp16): svh of projection q at v[256 q + c], its chscale at
+// v[256 q + 128 + c], the down input signs at v[512 + c].
+struct EpiVec {
+  const uint16_t *v;
+  const float *wt;
+};
+
+template <int EPI, bool COH = false, bool LDSV = false>
 __device__ __forceinline__ void epilogue(const GemmParams &p, float *T, int ld, int proj_stride,
-                                         int e, int row0, int nrows, int colbase, int nblk) {
+                                         int e, int row0, int nrows, int colbase, int nblk,
+                                         const EpiVec &ev = EpiVec{}) {
   const int ngroups = blockDim.x >> 4;
   const int grp = threadIdx.x >> 4;
   const int i = threadIdx.x & 15;
+  // svh / chscale of projection q at column c (relative to colbase)
+  auto svh_at = [&](int q, int c) -> float {
+    if constexpr (LDSV) return f16_bits_to_f32(ev.v[256 * q + c]);
+    else return f16_bits_to_f32(p.proj[q].svh[(size_t)e * p.out_f + colbase + c]);
+  };
+  auto cs_at = [&](int q, int c) -> float {
+    if constexpr (LDSV) return f16_bits_to_f32(ev.v[256 * q + 128 + c]);
+    else return f16_bits_to_f32(p.proj[q].cs[(size_t)e * p.out_f + colbase + c]);
+  };
   if constexpr (EPI == EPI_GATEUP) {
     // y = H(acc)/sqrt(128) * svh * cs for gate (pj 0) and up (pj 1)
     for (int it = grp; it < 2 * nrows; it += ngroups) {
@@ -49,13 +70,10 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, float *T, int ld, 
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = t[i + 16 * j];
       fwht128_group16(v);
-      const ProjDev &pd = p.proj[q];
-      const size_t ob = (size_t)e * p.out_f + colbase;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int c = i + 16 * j;
-        t[c] = ((v[j] * kRsqrt128) * f16_bits_to_f32(pd.svh[ob + c])) *
-               f16_bits_to_f32(pd.cs[ob + c]);
+        t[c] = ((v[j] * kRsqrt128) * svh_at(q, c)) * cs_at(q, c);
       }
     }
     __syncthreads();
@@ -67,7 +85,8 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, float *T, int ld, 
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int c = i + 16 * j;
-        v[j] = (silu(tg[c]) * tu[c]) * f16_bits_to_f32(p.suh_down[sb + c]);
+        const float sd = LDSV ? f16_bits_to_f32(ev.v[512 + c]) : f16_bits_to_f32(p.suh_down[sb + c]);
+        v[j] = (silu(tg[c]) * tu[c]) * sd;
       }
       fwht128_group16(v);
       uint16_t *o = p.out_h + (int64_t)(row0 + row) * p.ldo + colbase;
@@ -81,7 +100,6 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, float *T, int ld, 
       }
     }
   } else {
-    const ProjDev &pd = p.proj[0];
     for (int it = grp; it < nrows * nblk; it += ngroups) {
       const int row = it / nblk, blk = it - row * nblk;
       const float *t = T + row * ld + blk * 128;
@@ -90,17 +108,19 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, float *T, int ld, 
       for (int j = 0; j < 8; ++j) v[j] = t[i + 16 * j];
       fwht128_group16(v);
       const int cb = colbase + blk * 128;
-      const size_t ob = (size_t)e * p.out_f + cb;
       float wt = 1.0f;
-      if constexpr (EPI == EPI_DOWN) wt = p.weight_of_pos[p.pass_base + row0 + row];
+      if constexpr (EPI == EPI_DOWN)
+        wt = LDSV ? ev.wt[row] : p.weight_of_pos[p.pass_base + row0 + row];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int c = i + 16 * j;
-        const float y = ((v[j] * kRsqrt128) * f16_bits_to_f32(pd.svh[ob + c])) *
-                        f16_bits_to_f32(pd.cs[ob + c]);
+        const float y = ((v[j] * kRsqrt128) * svh_at(0, blk * 128 + c)) * cs_at(0, blk * 128 + c);
         const int64_t o = (int64_t)(row0 + row) * p.ldo + cb + c;
         if constexpr (EPI == EPI_DOWN) {
-          p.out_f32[o] = y * wt;
+          if constexpr (COH)
+            __hip_atomic_store(p.out_f32 + o, y * wt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            p.out_f32[o] = y * wt;
         } else {
           if (p.out_f32) p.out_f32[o] = y;
           else p.out_h[o] = f32_to_out16(y, p.out_bf16);

@@ -126,7 +126,10 @@ struct MoeLayout {
   // with 8+ passes, 2 with 4-7, else 1): one plan, one buffer set of
   // gcap = group * cap rows. Spans are still cut every `cap` pairs.
   int group, units, gcap;
-  bool wide, pipe;
+  // fused: a single pass on 16-row tiles runs its GEMMs and combine in one
+  // launch (experts_narrow_kernel), with separate sums and counts for the
+  // concurrent gate/up and down items
+  bool wide, pipe, fused;
   size_t xt_bytes, at_bytes, d_bytes;  // one buffer each (pipe: two of each)
 };
 
@@ -175,9 +178,18 @@ MoeLayout moe_layout(int32_t rows, int32_t topk, int32_t E, int32_t H, int32_t I
   L.d = take(nbuf * L.d_bytes);
   L.yacc = take(4 * (size_t)rows * H);
   // 16-row tiles: per (tile, 128-column block) completion counts; 128-row
-  // tiles in one pass: per tile, the finished gate/up items
-  L.ncnt_ints = L.pipe ? 0 : L.wide ? L.slots : L.slots * (std::max(I, H) / 128);
-  L.nacc = take(L.wide ? 0 : 4 * (size_t)C * std::max(2 * I, H));
+  // tiles in one pass: per tile, the finished gate/up items. Fused: gate/up
+  // counts [slots][I/128], down counts [slots][H/128], a~ blocks per tile
+  // [slots], d blocks per output row [rows][H/128], and the pre-rotation sums
+  // of gate/up [C][2I] and of down [C][H] side by side.
+  L.fused = P > 0 && !L.wide && L.passes == 1;
+  L.ncnt_ints = L.fused  ? L.slots * (I / 128 + H / 128 + 1) + rows * (H / 128)
+                : L.pipe ? 0
+                : L.wide ? L.slots
+                         : L.slots * (std::max(I, H) / 128);
+  L.nacc = take(L.wide     ? 0
+                : L.fused ? 4 * (size_t)C * (2 * I + H)
+                          : 4 * (size_t)C * std::max(2 * I, H));
   L.ncnt = take(4 * (size_t)L.ncnt_ints);
   L.total = o;
   return L;
@@ -360,6 +372,45 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
         return EXL3_E_LAUNCH;
     }
     return EXL3_OK;
+  }
+
+  if (L.fused) {
+    // launch 1: pack, plan and rotation in one launch (few pairs) or the
+    // rotation after the pack already enqueued; it also zeroes the counts.
+    // launch 2: gate/up, down and combine.
+    if (fused_pack) {
+      ProfScope ps(st, EXL3_K_PACK);
+      if (launch_pack_rotate(*fused_pack, rot_params(0, 0), st) != hipSuccess)
+        return EXL3_E_LAUNCH;
+    } else {
+      ProfScope ps(st, EXL3_K_ROTATE);
+      if (launch_rotate(rot_params(0, 0), st) != hipSuccess) return EXL3_E_LAUNCH;
+    }
+    NarrowFusedParams f{};
+    f.gu = gu_params(0, 0);
+    f.dn = dn_params(0, 0);
+    const int slots = L.slots;
+    int32_t *cnt = at<int32_t>(ws, L.ncnt);
+    float *nacc = at<float>(ws, L.nacc);
+    f.gu.nacc = nacc;
+    f.dn.nacc = nacc + (size_t)L.cap * 2 * I;
+    f.gu.ncnt = cnt;
+    f.dn.ncnt = cnt + (size_t)slots * (I / 128);
+    f.tile_ready = f.dn.ncnt + (size_t)slots * (H / 128);
+    f.row_cnt = f.tile_ready + slots;
+    f.pair_of_pos = pair_of_pos;
+    f.pos_of_pair = pos_of_pair;
+    f.total_valid = total_valid;
+    f.rows = rows;
+    f.topk = topk;
+    f.pairs = (int)P;
+    f.out = out;
+    f.out_f32 = out_dtype == EXL3_F32;
+    f.out_bf16 = out_dtype == EXL3_BF16;
+    f.tiles = tiles_of(0);
+    f.g1 = f.tiles * 2 * (I / 64);
+    ProfScope ps(st, EXL3_K_EXPERTS);
+    return launch_experts_narrow(f, st) == hipSuccess ? EXL3_OK : EXL3_E_LAUNCH;
   }
 
   // otherwise: pass by pass, one pass per unit (128-row tiles: a single pass)

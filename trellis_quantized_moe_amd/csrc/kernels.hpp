@@ -44,6 +44,21 @@ struct GemmParams {
   int32_t *ncnt;
 };
 
+// One launch for a single pass on 16-row tiles (experts_narrow_kernel):
+// gate/up and down work items plus the ordered combine. gu and dn each have
+// their own pre-rotation sums (nacc) and completion counts (ncnt).
+struct NarrowFusedParams {
+  GemmParams gu, dn;
+  int32_t *tile_ready;  // [tiles]: a~ blocks finished per tile (zero at launch)
+  int32_t *row_cnt;     // [rows][H / 128]: d blocks finished per output row (zero)
+  const int32_t *pair_of_pos, *pos_of_pair, *total_valid;
+  int rows, topk, pairs;
+  void *out;            // [rows][H]
+  int out_f32, out_bf16;
+  int tiles;            // plan tile bound (surplus items exit)
+  int g1;               // gate/up work items: tiles * 2 * (I / 64)
+};
+
 struct RotParams {
   const uint16_t *x;  // [rows][H] fp16, or bf16 if x_bf16
   int x_bf16;
@@ -104,6 +119,7 @@ hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks,
 // 128-row tiles (gemm_wide.hip); called by launch_gemm.
 hipError_t launch_gemm_wide(int epi, const GemmParams &p, int tiles, int nblocks,
                             hipStream_t s);
+hipError_t launch_experts_narrow(const NarrowFusedParams &f, hipStream_t s);
 // One pass of 128-row routed experts: gate/up and down in one launch, a
 // tile's down work starting once its own gate/up items are done. `q` holds
 // `slots` ints, zero at launch (slots >= plan tiles of the pass).
@@ -129,6 +145,7 @@ hipError_t launch_decode_tiles(const uint16_t *words, int ntiles, int K,
                                uint16_t *out, hipStream_t s);
 
 constexpr int kBM = 16;       // rows per narrow GEMM work tile
+constexpr int kMaxTopk = 32;  // EXL3_MAX_TOPK
 constexpr int kBMWide = 128;  // rows per wide GEMM work tile
 
 }  // namespace exl3

@@ -405,34 +405,45 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
 
 // The same pack and one-pass plan for at most kSmallPairs pairs, by a single
 // wave and without barriers (decode-size calls, where the big kernel's
-// barriers and phases are most of its time; with more pairs the wave's
-// serial work costs more than the barriers save). Lane l holds pair l; the
-// pairs are counted per expert with LDS atomics, the counts scanned over the
-// experts by the wave, and each pair's rank among the earlier pairs of its
-// expert found with ballots: the same positions as the big kernel.
-constexpr int kSmallPairs = 64;
+// barriers and phases are most of its time). Lane l holds pairs l, l + 64,
+// l + 128 and l + 192 (rounds 0..3); the pairs are counted per expert with
+// LDS atomics, the counts scanned over the experts by the wave, and the
+// rounds walked in pair order, each pair's rank among the earlier pairs of
+// its expert in its round found with ballots: the same positions as the big
+// kernel.
+constexpr int kSmallRounds = 4;
+constexpr int kSmallPairs = 64 * kSmallRounds;
 
 struct SmallPairs {
-  int e;      // expert of the lane's pair; -1 dropped, -2 no pair
-  float w;    // its route weight (when loaded)
-  int pos;    // its position, -1 if none
+  int e[kSmallRounds];      // expert of the lane's pair; -1 dropped, -2 no pair
+  float w[kSmallRounds];    // its route weight (when loaded)
+  int pos[kSmallRounds];    // its position, -1 if none
   int kept, dropped, nact;
 };
 
-// Positions of the (at most 64) pairs by one wave. s_cur and s_off hold E
-// and E + 1 ints of LDS; s_off ends as the expert offsets. With `meta` the
-// weights are loaded and the counts and offsets written.
+// Positions of the (at most kSmallPairs) pairs by one wave. s_cur and s_off
+// hold E and E + 1 ints of LDS; s_off ends as the expert offsets. With
+// `meta` the weights are loaded and the counts and offsets written.
 __device__ SmallPairs small_positions(const PackParams &p, int *s_cur, int *s_off, bool meta) {
   const int lane = threadIdx.x & 63;
   const int E = p.E;
   const int pairs = p.rows * p.topk;
   SmallPairs r;
-  const bool in = lane < pairs;
-  r.e = in ? load_expert(p.ids, p.ids_i64, lane, E) : -2;
-  r.w = (in && meta) ? load_weight(p.w, p.w_dtype, lane) : 0.0f;
   for (int e = lane; e < E; e += 64) s_cur[e] = 0;
-  if (r.e >= 0) atomicAdd(&s_cur[r.e], 1);  // counts are order-free
-  r.dropped = __popcll(__ballot(r.e == -1));
+  int dropped = 0;
+#pragma unroll
+  for (int i = 0; i < kSmallRounds; ++i) {
+    const int q = 64 * i + lane;
+    const bool in = q < pairs;
+    r.e[i] = in ? load_expert(p.ids, p.ids_i64, q, E) : -2;
+    r.w[i] = (in && meta) ? load_weight(p.w, p.w_dtype, q) : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < kSmallRounds; ++i) {
+    if (r.e[i] >= 0) atomicAdd(&s_cur[r.e[i]], 1);  // counts are order-free
+    dropped += __popcll(__ballot(r.e[i] == -1));
+  }
+  r.dropped = dropped;
   int run = 0, nact = 0;
   for (int eb = 0; eb < E; eb += 64) {  // exclusive scan over the experts
     const int e = eb + lane;
@@ -458,16 +469,31 @@ __device__ SmallPairs small_positions(const PackParams &p, int *s_cur, int *s_of
   r.kept = run;
   r.nact = nact;
   if (lane == 0) s_off[E] = run;
-  const bool valid = r.e >= 0;
-  const uint64_t m = match_key(valid ? r.e : E, __ballot(valid), 32 - __clz(E));
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  r.pos = valid ? s_cur[r.e] + __popcll(m & lt_mask) : -1;
+  const int nb = 32 - __clz(E);
+#pragma unroll
+  for (int i = 0; i < kSmallRounds; ++i) {  // rounds in pair order
+    if (64 * i >= pairs) {
+      r.pos[i] = -1;
+      continue;
+    }
+    const bool valid = r.e[i] >= 0;
+    const uint64_t m = match_key(valid ? r.e[i] : E, __ballot(valid), nb);
+    const int rank = __popcll(m & lt_mask);
+    int base = 0;
+    if (valid) base = s_cur[r.e[i]];
+    r.pos[i] = valid ? base + rank : -1;
+    // the round's lowest lane of each expert moves that expert's cursor on;
+    // every lane read the cursor first (LDS ops of one wave complete in order)
+    if (valid && rank == 0) s_cur[r.e[i]] = base + __popcll(m);
+  }
   return r;
 }
 
 // Pack (and with do_plan the one-pass plan) of at most kSmallPairs pairs by
-// the first wave of the block; the other waves return.
-__device__ void pack_small(const PackParams &p) {
+// the first wave of the block; the other waves return. With `zero` the wave
+// also clears the counts p.zero (else the caller's other waves do).
+__device__ void pack_small(const PackParams &p, bool zero) {
   __shared__ int s_cur[kMaxE];
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_rowhit[kSmallPairs];
@@ -483,16 +509,20 @@ __device__ void pack_small(const PackParams &p) {
   }
   if (p.do_plan)
     for (int row = lane; row < p.rows; row += 64) s_rowhit[row] = 0;
-  if (r.e >= 0) {
-    p.pair_of_pos[r.pos] = lane;
-    p.weight_of_pos[r.pos] = r.w;
-    p.pos_of_pair[lane] = r.pos;
-    if (p.do_plan) {
-      p.expert_of_pos[r.pos] = r.e;
-      s_rowhit[lane / p.topk] = 1;
+#pragma unroll
+  for (int i = 0; i < kSmallRounds; ++i) {
+    const int q = 64 * i + lane;
+    if (r.e[i] >= 0) {
+      p.pair_of_pos[r.pos[i]] = q;
+      p.weight_of_pos[r.pos[i]] = r.w[i];
+      p.pos_of_pair[q] = r.pos[i];
+      if (p.do_plan) {
+        p.expert_of_pos[r.pos[i]] = r.e[i];
+        s_rowhit[q / p.topk] = 1;
+      }
+    } else if (r.e[i] == -1) {
+      p.pos_of_pair[q] = -1;
     }
-  } else if (r.e == -1) {
-    p.pos_of_pair[lane] = -1;
   }
   for (int pos = r.kept + lane; pos < pairs; pos += 64) {
     p.pair_of_pos[pos] = -1;
@@ -503,7 +533,8 @@ __device__ void pack_small(const PackParams &p) {
     p.ctrl[1] = 0;  // bad stage entries
     p.ctrl[2] = 0;  // waits that gave up
   }
-  for (int i = lane; i < p.nzero; i += 64) p.zero[i] = 0;
+  if (zero)
+    for (int i = lane; i < p.nzero; i += 64) p.zero[i] = 0;
   plan_units(p, s_off, p.E, r.kept, 0, 1, lane);  // one pass: capacity >= pairs
   // rows whose pairs were all dropped produce zeros
   if (p.out && r.dropped > 0) {
@@ -517,34 +548,44 @@ __device__ void pack_small(const PackParams &p) {
   }
 }
 
-__global__ void __launch_bounds__(64) pack_small_kernel(PackParams p) { pack_small(p); }
+__global__ void __launch_bounds__(64) pack_small_kernel(PackParams p) { pack_small(p, true); }
 
 // Pack, plan and the rotation of the one pass in a single launch (at most
-// kSmallPairs pairs): block 0 packs; every other block recomputes the same
-// positions with one wave (no block waits for another) and rotates its 16
-// (position, 128-block) units.
+// kSmallPairs pairs): block 0 packs, plans and clears the counts; every other
+// block rotates 16 (pair, 128-block) units, one per 16-lane group, finding
+// each pair's position itself: pos(q) = #{kept pairs of a lower expert} +
+// #{earlier pairs of the same expert}, counted over the route IDs (loaded
+// into LDS once per block). That is the stable pack's position by
+// definition, so no block waits for another.
 __global__ void __launch_bounds__(256) pack_rotate_small_kernel(PackParams p, RotParams rp) {
   if (blockIdx.x == 0) {
-    pack_small(p);
+    // waves 1-3 clear the counts of the launches that follow while wave 0
+    // packs and plans
+    if (threadIdx.x >= 64)
+      for (int i = threadIdx.x - 64; i < p.nzero; i += blockDim.x - 64) p.zero[i] = 0;
+    pack_small(p, false);
     return;
   }
-  __shared__ int s_cur[kMaxE];
-  __shared__ int s_off[kMaxE + 1];
-  __shared__ int s_q[kSmallPairs], s_e[kSmallPairs];
-  __shared__ int s_kept;
-  if (threadIdx.x < 64) {
-    const SmallPairs r = small_positions(p, s_cur, s_off, false);
-    if (r.e >= 0) {
-      s_q[r.pos] = threadIdx.x;
-      s_e[r.pos] = r.e;
-    }
-    if (threadIdx.x == 0) s_kept = r.kept;
-  }
+  __shared__ int s_ids[kSmallPairs];
+  const int pairs = p.rows * p.topk;
+  for (int q = threadIdx.x; q < pairs; q += blockDim.x)
+    s_ids[q] = load_expert(p.ids, p.ids_i64, q, p.E);
   __syncthreads();
   const int nblk = rp.H >> 7;
   const int gid = (blockIdx.x - 1) * 16 + (threadIdx.x >> 4);
-  const int item = gid / nblk, blk = gid - item * nblk;
-  if (item < s_kept) rotate_block(rp, item, blk, s_q[item] / p.topk, s_e[item], threadIdx.x & 15);
+  const int q = gid / nblk, blk = gid - q * nblk;
+  if (q >= pairs) return;  // uniform per group
+  const int e = s_ids[q];
+  if (e < 0) return;  // dropped pair
+  const int i = threadIdx.x & 15;
+  int before = 0;
+  for (int q2 = i; q2 < pairs; q2 += 16) {
+    const int e2 = s_ids[q2];
+    before += (e2 >= 0 && (e2 < e || (e2 == e && q2 < q))) ? 1 : 0;
+  }
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) before += __shfl_xor(before, d, 64);
+  rotate_block(rp, before, blk, q / p.topk, e, i);
 }
 
 hipError_t launch_pack_rotate(const PackParams &p, const RotParams &rp, hipStream_t s) {
@@ -560,9 +601,13 @@ hipError_t launch_pack_rotate(const PackParams &p, const RotParams &rp, hipStrea
 
 bool pack_rotate_fits(int64_t pairs, int passes) { return pairs <= kSmallPairs && passes == 1; }
 
+// A pack launched alone takes the single wave up to 64 pairs (one round);
+// with more pairs the 16-wave kernel measured faster there.
+constexpr int kSmallPackAlone = 64;
+
 hipError_t launch_pack(const PackParams &p, hipStream_t s) {
   const int64_t pairs = (int64_t)p.rows * p.topk;
-  if (p.do_pack && pairs <= kSmallPairs && (!p.do_plan || p.passes == 1))
+  if (p.do_pack && pairs <= kSmallPackAlone && (!p.do_plan || p.passes == 1))
     hipLaunchKernelGGL(pack_small_kernel, dim3(1), dim3(64), 0, s, p);
   else
     hipLaunchKernelGGL(pack_plan_kernel, dim3(1), dim3(kPackThreads), 0, s, p);
