@@ -48,7 +48,7 @@ extern "C" {
 /* Exact-match compatibility contract [p1 API contract]: bumped on any
  * incompatible signature, pointer-layout, workspace, residual-encoding or
  * overflow-semantics change. Consumers must require an exact value. */
-#define EXL3_ABI_VERSION 3
+#define EXL3_ABI_VERSION 4
 
 enum exl3_dtype {
   EXL3_F16 = 1, EXL3_BF16 = 2, EXL3_F32 = 3, EXL3_I32 = 4, EXL3_I64 = 5
@@ -144,6 +144,33 @@ typedef struct exl3_route_meta {
 } exl3_route_meta;
 
 /*
+ * Optional per-launch timing, owned by the caller (a diagnostic, not part of
+ * the layer). The caller creates 2 * cap events with exl3_events_create
+ * (which allocates them: call it outside timed or captured regions), fills
+ * the record and passes it to any call through that call's last argument
+ * `prof` (NULL: no timing). While n < cap, each kernel the call launches is
+ * bracketed by events[2 n] and events[2 n + 1], recorded on the call's
+ * stream; kernel_ids[n] (if kernel_ids is not NULL) is set to its
+ * exl3_kernel_id and n is incremented. The library keeps no state of its own
+ * between calls and allocates nothing for it. exl3_profile_read waits for the
+ * first n event pairs and writes each launch's milliseconds to ms[0 .. n-1].
+ * Event recording is not allowed during graph capture: pass NULL there.
+ * A record is not thread-safe; calls on different threads use different
+ * records.
+ */
+enum exl3_kernel_id {
+  EXL3_K_PACK = 1, EXL3_K_ROTATE = 2, EXL3_K_GATEUP = 3, EXL3_K_DOWN = 4,
+  EXL3_K_COMBINE = 5, EXL3_K_LINEAR = 6, EXL3_K_DECODE = 7,
+  EXL3_K_EXPERTS = 8 /* 128-row tiles: gate/up and down of a single pass in one launch, or one
+                        launch of the passes pipelined across launches */
+};
+typedef struct exl3_profile {
+  void **events;        /* host: 2 * cap event handles (hipEvent_t) */
+  int32_t *kernel_ids;  /* host: cap entries, or NULL */
+  int32_t cap;
+  int32_t n;            /* launches recorded so far; the library appends */
+} exl3_profile;
+/*
  * Route histogram -> exclusive scan -> stable pack of (row, expert) pairs.
  * ids: [rows][topk] int32 or int64 (EXL3_I32 / EXL3_I64); w: [rows][topk]
  * fp16, bf16 or fp32 [p1 Validation]. Bit-exact and deterministic.
@@ -151,7 +178,7 @@ typedef struct exl3_route_meta {
 int32_t exl3_route_pack(const void *ids, int32_t ids_dtype, const void *w,
                         int32_t w_dtype, int32_t rows, int32_t topk,
                         int32_t num_experts, const exl3_route_meta *meta,
-                        void *stream);
+                        void *stream, exl3_profile *prof);
 
 /*
  * Plain EXL3 linear [p2 What this changes: row-invariant linear; prompt rows
@@ -168,7 +195,7 @@ size_t exl3_linear_workspace_size(int32_t rows, int32_t in_features,
                                   int32_t out_features);
 int32_t exl3_linear(const uint16_t *x, int32_t x_dtype, int32_t rows,
                     const exl3_proj *proj, void *out, int32_t out_dtype, void *ws,
-                    size_t ws_bytes, void *stream);
+                    size_t ws_bytes, void *stream, exl3_profile *prof);
 
 /*
  * Routed-experts layer. Per kept pair (r, j), e = ids[r][j], w = weight:
@@ -200,7 +227,7 @@ int32_t exl3_moe_forward(const uint16_t *x, int32_t x_dtype, int32_t rows,
                          const exl3_proj *up, const exl3_proj *down, void *out,
                          int32_t out_dtype, int32_t capacity,
                          int32_t num_active_hint, void *ws, size_t ws_bytes,
-                         void *stream);
+                         void *stream, exl3_profile *prof);
 
 /*
  * exl3_moe_forward for callers that cannot allocate device memory (code under
@@ -223,7 +250,8 @@ int32_t exl3_moe_forward_static(const uint16_t *x, int32_t x_dtype, int32_t rows
                                 int32_t w_dtype, int32_t topk, const exl3_proj *gate,
                                 const exl3_proj *up, const exl3_proj *down, void *out,
                                 int32_t out_dtype, int32_t capacity,
-                                int32_t num_active_hint, void *stream);
+                                int32_t num_active_hint, void *stream,
+                                exl3_profile *prof);
 
 /* Experts only, for callers that already hold route metadata (from
  * exl3_route_pack or equivalent) [p1 Summary: exl3_moe_additive]. */
@@ -232,7 +260,7 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t x_dtype, int32_t rows, int3
                           const exl3_proj *up, const exl3_proj *down,
                           void *out, int32_t out_dtype, int32_t capacity,
                           int32_t num_active_hint, void *ws, size_t ws_bytes,
-                          void *stream);
+                          void *stream, exl3_profile *prof);
 
 /*
  * Workspace layout of exl3_moe_forward / exl3_moe_additive (byte offsets
@@ -291,27 +319,13 @@ int32_t exl3_moe_layout(int32_t rows, int32_t topk, int32_t num_experts,
  * out: [ntiles][16 (k)][16 (n)] fp16. For bit-exact decode tests.
  */
 int32_t exl3_decode_tiles(const uint16_t *words, int32_t ntiles, int32_t K,
-                          uint16_t *out, void *stream);
+                          uint16_t *out, void *stream, exl3_profile *prof);
 
-/*
- * Diagnostic per-launch timing (host). exl3_profile_begin() creates
- * 2 * max_launches hipEvents (so it allocates: call it outside timed or
- * captured regions); while active, every kernel the library launches is
- * bracketed by an event pair on its stream (the first max_launches
- * launches). exl3_profile_end() waits for those events, writes up to `cap`
- * (kernel id, milliseconds) pairs to the host arrays, frees the events and
- * returns the number of recorded launches (or a negative status). Not for
- * use during graph capture; not thread-safe.
- */
-enum exl3_kernel_id {
-  EXL3_K_PACK = 1, EXL3_K_ROTATE = 2, EXL3_K_GATEUP = 3, EXL3_K_DOWN = 4,
-  EXL3_K_COMBINE = 5, EXL3_K_LINEAR = 6, EXL3_K_DECODE = 7,
-  EXL3_K_EXPERTS = 8 /* 128-row tiles: gate/up and down of a single pass in one launch, or one
-                        launch of the passes pipelined across launches */
-};
-int32_t exl3_profile_begin(int32_t max_launches);
-int32_t exl3_profile_end(int32_t *kernel_ids /* host */, float *ms /* host */,
-                         int32_t cap);
+/* Create / destroy `count` events into / from the host array `events`
+ * (destroy sets each entry to NULL). */
+int32_t exl3_events_create(int32_t count, void **events /* host */);
+int32_t exl3_events_destroy(int32_t count, void **events /* host */);
+int32_t exl3_profile_read(const exl3_profile *prof /* host */, float *ms /* host */);
 
 #ifdef __cplusplus
 }

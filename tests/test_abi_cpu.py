@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert exl3.abi_version() == 3
+    assert exl3.abi_version() == 4
     L = exl3.lib()
     for s in range(0, -10, -1):
         msg = L.exl3_status_string(s).decode()
@@ -79,7 +79,8 @@ def _fwd(gate=None, up=None, down=None, rows=4, topk=2, capacity=8, out_dtype=ex
     return exl3.lib().exl3_moe_forward(
         ctypes.c_void_p(x), x_dtype, rows, ctypes.c_void_p(ids), ids_dtype, ctypes.c_void_p(w),
         w_dtype, topk, ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down),
-        ctypes.c_void_p(out), out_dtype, capacity, -1, ctypes.c_void_p(ws), ws_bytes, None)
+        ctypes.c_void_p(out), out_dtype, capacity, -1, ctypes.c_void_p(ws), ws_bytes, None,
+        None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -120,7 +121,7 @@ def _lin(x_dtype=exl3.F16, out_dtype=exl3.F32, proj=None, rows=3, x=16384, out=3
     proj = proj or _proj(num_experts=1)
     return exl3.lib().exl3_linear(ctypes.c_void_p(x), x_dtype, rows, ctypes.byref(proj),
                                   ctypes.c_void_p(out), out_dtype, ctypes.c_void_p(ws),
-                                  ws_bytes, None)
+                                  ws_bytes, None, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -140,7 +141,7 @@ def _add(x_dtype=exl3.F16, out_dtype=exl3.F32, meta_ptr=8192):
     return exl3.lib().exl3_moe_additive(
         ctypes.c_void_p(16384), x_dtype, 4, 2, ctypes.byref(mc), ctypes.byref(g),
         ctypes.byref(u), ctypes.byref(d), ctypes.c_void_p(32768), out_dtype, 8, -1,
-        ctypes.c_void_p(65536), 1 << 40, None)
+        ctypes.c_void_p(65536), 1 << 40, None, None)
 
 
 @pytest.mark.parametrize("xdt,odt,code", [
@@ -165,3 +166,22 @@ def test_pipelined_passes_are_grouped_per_launch_unit(rows, cap, passes, group):
 def test_small_tiles_never_group_passes():
     lay = exl3.moe_layout(64, 8, 128, 4096, 1536, 16)  # 16-row tiles, 32 passes
     assert lay.passes == 32 and lay.plan_group == 1
+
+
+def test_profile_record_checks_on_the_host():
+    # the timing record is the caller's: the library validates it and, with
+    # nothing recorded, touches no device
+    L = exl3.lib()
+    ms = (ctypes.c_float * 4)()
+    ev = (ctypes.c_void_p * 8)()
+    ids = (ctypes.c_int32 * 4)()
+    assert L.exl3_profile_read(None, ms) == -1
+    assert L.exl3_profile_read(ctypes.byref(exl3.ProfileC(ev, ids, 4, 5)), ms) == -7
+    assert L.exl3_profile_read(ctypes.byref(exl3.ProfileC(ev, ids, 4, -1)), ms) == -7
+    assert L.exl3_profile_read(ctypes.byref(exl3.ProfileC(ev, ids, 4, 0)), ms) == 0
+    assert L.exl3_profile_read(ctypes.byref(exl3.ProfileC(None, ids, 4, 2)), ms) == -1
+    assert L.exl3_events_create(-1, ev) == -7
+    assert L.exl3_events_create(2, None) == -1
+    assert L.exl3_events_create(0, None) == 0
+    assert L.exl3_events_destroy(-1, ev) == -7
+    assert L.exl3_events_destroy(0, None) == 0

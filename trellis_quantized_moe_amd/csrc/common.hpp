@@ -323,7 +323,7 @@ __device__ __forceinline__ void fwht128_lane8(double (&v)[8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if ((j & d) == 0) {
-        const float lo = v[j], hi = v[j + d];
+        const double lo = v[j], hi = v[j + d];
         v[j] = lo + hi;
         v[j + d] = lo - hi;
       }

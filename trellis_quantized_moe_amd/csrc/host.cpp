@@ -19,29 +19,22 @@ using namespace exl3;
 namespace {
 
 // ------------------------------------------------------------- profiling
-// Optional per-launch timing: when active, every kernel launch is bracketed
-// by two hipEvents on its stream. Off by default; begin/end allocate and free
-// the events (never inside a product call).
-struct Profiler {
-  bool on = false;
-  int cap = 0, n = 0;
-  hipEvent_t *ev = nullptr;
-  int32_t *kid = nullptr;
-} g_prof;
-
+// Optional per-launch timing into the caller's exl3_profile record (null: no
+// timing): the kernel launch in the scope is bracketed by the record's next
+// event pair on its stream. The library keeps no state of its own for it.
 struct ProfScope {
+  exl3_profile *p;
   hipStream_t s;
   int slot = -1;
-  int32_t id;
-  ProfScope(hipStream_t st, int32_t kernel_id) : s(st), id(kernel_id) {
-    if (g_prof.on && g_prof.n < g_prof.cap) {
-      slot = g_prof.n++;
-      g_prof.kid[slot] = id;
-      (void)hipEventRecord(g_prof.ev[2 * slot], s);
+  ProfScope(exl3_profile *prof, hipStream_t st, int32_t kernel_id) : p(prof), s(st) {
+    if (p && p->events && p->n >= 0 && p->n < p->cap) {
+      slot = p->n++;
+      if (p->kernel_ids) p->kernel_ids[slot] = kernel_id;
+      (void)hipEventRecord((hipEvent_t)p->events[2 * slot], s);
     }
   }
   ~ProfScope() {
-    if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
+    if (slot >= 0) (void)hipEventRecord((hipEvent_t)p->events[2 * slot + 1], s);
   }
 };
 
@@ -238,7 +231,8 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
                     const exl3_proj *down, void *out, int32_t out_dtype,
                     const MoeLayout &L, void *ws, const int32_t *pair_of_pos,
                     const int32_t *pos_of_pair, const float *weight_of_pos,
-                    const int32_t *offset, hipStream_t st, const PackParams *fused_pack = nullptr) {
+                    const int32_t *offset, hipStream_t st, exl3_profile *prof,
+                    const PackParams *fused_pack = nullptr) {
   const int H = gate->in_features, I = gate->out_features, E = gate->num_experts;
   const int64_t P = (int64_t)rows * topk;
   const int32_t *total_valid = offset + E;
@@ -355,7 +349,7 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
     // launch k: gate/up of unit k, down of k - 1, rotation of k + 1, combine
     // of k - 2; unit q uses the buffers of parity q & 1
     {
-      ProfScope ps(st, EXL3_K_ROTATE);
+      ProfScope ps(prof, st, EXL3_K_ROTATE);
       if (launch_rotate(rot_params(0, 0), st) != hipSuccess) return EXL3_E_LAUNCH;
     }
     for (int k = 0; k <= L.units + 1; ++k) {
@@ -365,7 +359,7 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
       const GemmParams dn = has_dn ? dn_params(k - 1, (k - 1) & 1) : GemmParams{};
       const RotParams rn = has_rn ? rot_params(k + 1, (k + 1) & 1) : RotParams{};
       const CombineParams cp = has_cb ? cb_params(k - 2, k & 1) : CombineParams{};
-      ProfScope ps(st, EXL3_K_EXPERTS);
+      ProfScope ps(prof, st, EXL3_K_EXPERTS);
       if (launch_gemm_wide_pipe(g, has_gu ? tiles_of(k) : 0, dn, has_dn ? tiles_of(k - 1) : 0, rn,
                                 cp, has_cb ? npos_of(k - 2) : 0, I / 128, (H + 255) / 256,
                                 st) != hipSuccess)
@@ -379,11 +373,11 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
     // rotation after the pack already enqueued; it also zeroes the counts.
     // launch 2: gate/up, down and combine.
     if (fused_pack) {
-      ProfScope ps(st, EXL3_K_PACK);
+      ProfScope ps(prof, st, EXL3_K_PACK);
       if (launch_pack_rotate(*fused_pack, rot_params(0, 0), st) != hipSuccess)
         return EXL3_E_LAUNCH;
     } else {
-      ProfScope ps(st, EXL3_K_ROTATE);
+      ProfScope ps(prof, st, EXL3_K_ROTATE);
       if (launch_rotate(rot_params(0, 0), st) != hipSuccess) return EXL3_E_LAUNCH;
     }
     NarrowFusedParams f{};
@@ -409,7 +403,7 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
     f.out_bf16 = out_dtype == EXL3_BF16;
     f.tiles = tiles_of(0);
     f.g1 = f.tiles * 2 * (I / 64);
-    ProfScope ps(st, EXL3_K_EXPERTS);
+    ProfScope ps(prof, st, EXL3_K_EXPERTS);
     return launch_experts_narrow(f, st) == hipSuccess ? EXL3_OK : EXL3_E_LAUNCH;
   }
 
@@ -418,7 +412,7 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
     const int npos = npos_of(pass);
     const int tiles = tiles_of(pass);
     if (fused_pack && pass == 0) {  // pack, plan and this rotation in one launch
-      ProfScope ps(st, EXL3_K_PACK);
+      ProfScope ps(prof, st, EXL3_K_PACK);
       if (launch_pack_rotate(*fused_pack, rot_params(0, 0), st) != hipSuccess)
         return EXL3_E_LAUNCH;
     } else {
@@ -427,27 +421,27 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
         rp.zero = at<int32_t>(ws, L.ncnt);
         rp.nzero = L.ncnt_ints;
       }
-      ProfScope ps(st, EXL3_K_ROTATE);
+      ProfScope ps(prof, st, EXL3_K_ROTATE);
       if (launch_rotate(rp, st) != hipSuccess) return EXL3_E_LAUNCH;
     }
     const GemmParams g = gu_params(pass, 0);
     if (!wide) {
-      ProfScope ps(st, EXL3_K_GATEUP);
+      ProfScope ps(prof, st, EXL3_K_GATEUP);
       if (launch_gemm(EPI_GATEUP, g, tiles, I / 128, st, wide) != hipSuccess) return EXL3_E_LAUNCH;
     }
     const GemmParams dn = dn_params(pass, 0);
     if (wide) {
-      ProfScope ps(st, EXL3_K_EXPERTS);
+      ProfScope ps(prof, st, EXL3_K_EXPERTS);
       if (launch_gemm_wide_pass(g, dn, tiles, L.slots, I / 128, (H + 255) / 256,
                                 at<int32_t>(ws, L.ncnt), st) != hipSuccess)
         return EXL3_E_LAUNCH;
     } else {
-      ProfScope ps(st, EXL3_K_DOWN);
+      ProfScope ps(prof, st, EXL3_K_DOWN);
       if (launch_gemm(EPI_DOWN, dn, tiles, H / 128, st, wide) != hipSuccess) return EXL3_E_LAUNCH;
     }
     const CombineParams cp = cb_params(pass, 0);
     {
-      ProfScope ps(st, EXL3_K_COMBINE);
+      ProfScope ps(prof, st, EXL3_K_COMBINE);
       const hipError_t err =
           (L.passes == 1) ? launch_combine_rows(cp, st) : launch_combine(cp, npos, st);
       if (err != hipSuccess) return EXL3_E_LAUNCH;
@@ -505,7 +499,8 @@ size_t exl3_linear_workspace_size(int32_t rows, int32_t in_features, int32_t out
 }
 
 int32_t exl3_linear(const uint16_t *x, int32_t x_dtype, int32_t rows, const exl3_proj *proj,
-                    void *out, int32_t out_dtype, void *ws, size_t ws_bytes, void *stream) {
+                    void *out, int32_t out_dtype, void *ws, size_t ws_bytes, void *stream,
+                    exl3_profile *prof) {
   if (rows < 0) return EXL3_E_ARG;
   if (rows == 0) return EXL3_OK;
   if (!x || !out || !ws) return EXL3_E_NULL;
@@ -535,7 +530,7 @@ int32_t exl3_linear(const uint16_t *x, int32_t x_dtype, int32_t rows, const exl3
   rp.zero = LL.ncnt_ints ? at<int32_t>(ws, LL.ncnt) : nullptr;
   rp.nzero = LL.ncnt_ints;
   {
-    ProfScope ps(st, EXL3_K_ROTATE);
+    ProfScope ps(prof, st, EXL3_K_ROTATE);
     if (launch_rotate(rp, st) != hipSuccess) return EXL3_E_LAUNCH;
   }
 
@@ -554,7 +549,7 @@ int32_t exl3_linear(const uint16_t *x, int32_t x_dtype, int32_t rows, const exl3
   g.ctrl = ctrl;
   g.nacc = at<float>(ws, LL.nacc);
   g.ncnt = at<int32_t>(ws, LL.ncnt);
-  ProfScope ps(st, EXL3_K_LINEAR);
+  ProfScope ps(prof, st, EXL3_K_LINEAR);
   const int fo = proj->out_features;
   const bool wide = LL.wide;
   const hipError_t le =
@@ -597,7 +592,7 @@ size_t exl3_moe_workspace_size(int32_t rows, int32_t topk, int32_t num_experts, 
 
 int32_t exl3_route_pack(const void *ids, int32_t ids_dtype, const void *w, int32_t w_dtype,
                         int32_t rows, int32_t topk, int32_t num_experts,
-                        const exl3_route_meta *meta, void *stream) {
+                        const exl3_route_meta *meta, void *stream, exl3_profile *prof) {
   if (rows < 0) return EXL3_E_ARG;
   if (!meta) return EXL3_E_NULL;
   if (topk < 1 || topk > EXL3_MAX_TOPK || num_experts < 1 || num_experts > EXL3_MAX_EXPERTS)
@@ -637,7 +632,7 @@ int32_t exl3_route_pack(const void *ids, int32_t ids_dtype, const void *w, int32
   p.status = meta->status;
   p.do_pack = 1;
   p.do_plan = 0;
-  ProfScope ps((hipStream_t)stream, EXL3_K_PACK);
+  ProfScope ps(prof, (hipStream_t)stream, EXL3_K_PACK);
   return launch_pack(p, (hipStream_t)stream) == hipSuccess ? EXL3_OK : EXL3_E_LAUNCH;
 }
 
@@ -654,7 +649,8 @@ int32_t moe_forward_impl(const uint16_t *x, int32_t x_dtype, int32_t rows, const
                          int32_t ids_dtype, const void *w, int32_t w_dtype, int32_t topk,
                          const exl3_proj *gate, const exl3_proj *up, const exl3_proj *down,
                          void *out, int32_t out_dtype, int32_t capacity, void *ws,
-                         size_t ws_bytes, void *stream, bool ws_is_scratch) {
+                         size_t ws_bytes, void *stream, bool ws_is_scratch,
+                         exl3_profile *prof) {
   if (rows < 0) return EXL3_E_ARG;
   if (rows == 0) return EXL3_OK;
   if (int32_t s = validate_moe_common(x, x_dtype, rows, topk, gate, up, down, out, out_dtype,
@@ -707,11 +703,11 @@ int32_t moe_forward_impl(const uint16_t *x, int32_t x_dtype, int32_t rows, const
   // few pairs in one pass: the pack runs inside the first rotation's launch
   const bool fuse = !L.pipe && pack_rotate_fits((int64_t)rows * topk, L.passes);
   if (!fuse) {
-    ProfScope ps(st, EXL3_K_PACK);
+    ProfScope ps(prof, st, EXL3_K_PACK);
     if (launch_pack(p, st) != hipSuccess) return EXL3_E_LAUNCH;
   }
   return run_experts(x, x_dtype, rows, topk, gate, up, down, out, out_dtype, L, ws, p.pair_of_pos,
-                     p.pos_of_pair, p.weight_of_pos, p.offset, st, fuse ? &p : nullptr);
+                     p.pos_of_pair, p.weight_of_pos, p.offset, st, prof, fuse ? &p : nullptr);
 }
 
 // ------------------------------------------------ static scratch workspace
@@ -750,10 +746,10 @@ int32_t exl3_moe_forward(const uint16_t *x, int32_t x_dtype, int32_t rows, const
                          const void *w, int32_t w_dtype, int32_t topk, const exl3_proj *gate,
                          const exl3_proj *up, const exl3_proj *down, void *out,
                          int32_t out_dtype, int32_t capacity, int32_t num_active_hint,
-                         void *ws, size_t ws_bytes, void *stream) {
+                         void *ws, size_t ws_bytes, void *stream, exl3_profile *prof) {
   (void)num_active_hint;
   return moe_forward_impl(x, x_dtype, rows, ids, ids_dtype, w, w_dtype, topk, gate, up, down,
-                          out, out_dtype, capacity, ws, ws_bytes, stream, false);
+                          out, out_dtype, capacity, ws, ws_bytes, stream, false, prof);
 }
 
 int32_t exl3_moe_forward_static(const uint16_t *x, int32_t x_dtype, int32_t rows,
@@ -761,7 +757,7 @@ int32_t exl3_moe_forward_static(const uint16_t *x, int32_t x_dtype, int32_t rows
                                 int32_t w_dtype, int32_t topk, const exl3_proj *gate,
                                 const exl3_proj *up, const exl3_proj *down, void *out,
                                 int32_t out_dtype, int32_t capacity, int32_t num_active_hint,
-                                void *stream) {
+                                void *stream, exl3_profile *prof) {
   (void)num_active_hint;
   if (rows < 0) return EXL3_E_ARG;
   if (rows == 0) return EXL3_OK;
@@ -771,14 +767,14 @@ int32_t exl3_moe_forward_static(const uint16_t *x, int32_t x_dtype, int32_t rows
   if (!ws) return EXL3_E_DEVICE;
   return moe_forward_impl(x, x_dtype, rows, ids, ids_dtype, w, w_dtype, topk, gate, up, down,
                           out, out_dtype, capacity, ws, EXL3_STATIC_SCRATCH_BYTES, stream,
-                          true);
+                          true, prof);
 }
 
 int32_t exl3_moe_additive(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t topk,
                           const exl3_route_meta *meta, const exl3_proj *gate,
                           const exl3_proj *up, const exl3_proj *down, void *out,
                           int32_t out_dtype, int32_t capacity, int32_t num_active_hint,
-                          void *ws, size_t ws_bytes, void *stream) {
+                          void *ws, size_t ws_bytes, void *stream, exl3_profile *prof) {
   (void)num_active_hint;
   if (rows < 0) return EXL3_E_ARG;
   if (rows == 0) return EXL3_OK;
@@ -821,65 +817,67 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t x_dtype, int32_t rows, int3
   p.zero = L.ncnt_ints ? at<int32_t>(ws, L.ncnt) : nullptr;
   p.nzero = L.ncnt_ints;
   {
-    ProfScope ps(st, EXL3_K_PACK);
+    ProfScope ps(prof, st, EXL3_K_PACK);
     if (launch_pack(p, st) != hipSuccess) return EXL3_E_LAUNCH;
   }
   return run_experts(x, x_dtype, rows, topk, gate, up, down, out, out_dtype, L, ws,
                      meta->pair_of_pos,
-                     meta->pos_of_pair, meta->weight_of_pos, meta->expert_offset, st);
+                     meta->pos_of_pair, meta->weight_of_pos, meta->expert_offset, st, prof);
 }
 
 int32_t exl3_decode_tiles(const uint16_t *words, int32_t ntiles, int32_t K, uint16_t *out,
-                          void *stream) {
+                          void *stream, exl3_profile *prof) {
   if (ntiles < 0 || K < 2 || K > 8) return EXL3_E_ARG;
   if (ntiles == 0) return EXL3_OK;
   if (!words || !out) return EXL3_E_NULL;
   if (!aligned16(words) || !aligned16(out)) return EXL3_E_ALIGN;
   for (const void *q : {(const void *)words, (const void *)out})
     if (int32_t s = check_device(q)) return s;
-  ProfScope ps((hipStream_t)stream, EXL3_K_DECODE);
+  ProfScope ps(prof, (hipStream_t)stream, EXL3_K_DECODE);
   return launch_decode_tiles(words, ntiles, K, out, (hipStream_t)stream) == hipSuccess
              ? EXL3_OK
              : EXL3_E_LAUNCH;
 }
 
-int32_t exl3_profile_begin(int32_t max_launches) {
-  if (g_prof.on || max_launches < 1 || max_launches > (1 << 20)) return EXL3_E_ARG;
-  g_prof.ev = new hipEvent_t[2 * (size_t)max_launches];
-  g_prof.kid = new int32_t[max_launches];
-  for (int i = 0; i < 2 * max_launches; ++i) {
-    if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) {
-      for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_prof.ev[j]);
-      delete[] g_prof.ev;
-      delete[] g_prof.kid;
-      g_prof = Profiler{};
+int32_t exl3_events_create(int32_t count, void **events) {
+  if (count < 0) return EXL3_E_ARG;
+  if (count > 0 && !events) return EXL3_E_NULL;
+  for (int i = 0; i < count; ++i) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy((hipEvent_t)events[j]);
+      for (int j = 0; j < i; ++j) events[j] = nullptr;
       return EXL3_E_DEVICE;
     }
+    events[i] = (void *)e;
   }
-  g_prof.cap = max_launches;
-  g_prof.n = 0;
-  g_prof.on = true;
   return EXL3_OK;
 }
 
-int32_t exl3_profile_end(int32_t *kernel_ids, float *ms, int32_t cap) {
-  if (!g_prof.on) return EXL3_E_ARG;
-  const int n = g_prof.n;
-  int32_t status = n;
-  for (int i = 0; i < n; ++i) {
-    float t = -1.0f;
-    if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess ||
-        hipEventElapsedTime(&t, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess)
-      status = EXL3_E_DEVICE;
-    if (i < cap) {
-      if (kernel_ids) kernel_ids[i] = g_prof.kid[i];
-      if (ms) ms[i] = t;
-    }
+int32_t exl3_events_destroy(int32_t count, void **events) {
+  if (count < 0) return EXL3_E_ARG;
+  if (count > 0 && !events) return EXL3_E_NULL;
+  int32_t status = EXL3_OK;
+  for (int i = 0; i < count; ++i) {
+    if (events[i] && hipEventDestroy((hipEvent_t)events[i]) != hipSuccess) status = EXL3_E_DEVICE;
+    events[i] = nullptr;
   }
-  for (int i = 0; i < 2 * g_prof.cap; ++i) (void)hipEventDestroy(g_prof.ev[i]);
-  delete[] g_prof.ev;
-  delete[] g_prof.kid;
-  g_prof = Profiler{};
+  return status;
+}
+
+int32_t exl3_profile_read(const exl3_profile *prof, float *ms) {
+  if (!prof) return EXL3_E_NULL;
+  if (prof->n < 0 || prof->n > prof->cap) return EXL3_E_ARG;
+  if (prof->n > 0 && (!prof->events || !ms)) return EXL3_E_NULL;
+  int32_t status = EXL3_OK;
+  for (int i = 0; i < prof->n; ++i) {
+    float t = -1.0f;
+    if (hipEventSynchronize((hipEvent_t)prof->events[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&t, (hipEvent_t)prof->events[2 * i],
+                            (hipEvent_t)prof->events[2 * i + 1]) != hipSuccess)
+      status = EXL3_E_DEVICE;
+    ms[i] = t;
+  }
   return status;
 }
 

@@ -43,6 +43,12 @@ class MetaC(ctypes.Structure):
                  "pos_of_pair", "num_active", "status")]
 
 
+class ProfileC(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)),
+                ("kernel_ids", ctypes.POINTER(ctypes.c_int32)),
+                ("cap", ctypes.c_int32), ("n", ctypes.c_int32)]
+
+
 class LayoutC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("ctrl", "meta", "expert_of_pos", "plan", "xt", "at", "d", "yacc",
@@ -52,31 +58,33 @@ class LayoutC(ctypes.Structure):
 
 _lib = None
 _i32, _sz, _vp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+_PP = ctypes.POINTER(ProfileC)
 _SIGS = {
     "exl3_abi_version": (_i32, []),
     "exl3_status_string": (ctypes.c_char_p, [_i32]),
     "exl3_route_pack": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32,
-                               ctypes.POINTER(MetaC), _vp]),
+                               ctypes.POINTER(MetaC), _vp, _PP]),
     "exl3_linear_workspace_size": (_sz, [_i32, _i32, _i32]),
     "exl3_linear": (_i32, [_vp, _i32, _i32, ctypes.POINTER(ProjC), _vp, _i32, _vp, _sz,
-                           _vp]),
+                           _vp, _PP]),
     "exl3_moe_workspace_size": (_sz, [_i32] * 6),
     "exl3_moe_forward": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32,
                                 ctypes.POINTER(ProjC), ctypes.POINTER(ProjC),
                                 ctypes.POINTER(ProjC), _vp, _i32, _i32, _i32, _vp, _sz,
-                                _vp]),
+                                _vp, _PP]),
     "exl3_moe_forward_static": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32,
                                        ctypes.POINTER(ProjC), ctypes.POINTER(ProjC),
-                                       ctypes.POINTER(ProjC), _vp, _i32, _i32, _i32, _vp]),
+                                       ctypes.POINTER(ProjC), _vp, _i32, _i32, _i32, _vp,
+                                       _PP]),
     "exl3_moe_additive": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(MetaC),
                                  ctypes.POINTER(ProjC), ctypes.POINTER(ProjC),
                                  ctypes.POINTER(ProjC), _vp, _i32, _i32, _i32, _vp, _sz,
-                                 _vp]),
+                                 _vp, _PP]),
     "exl3_moe_layout": (_i32, [_i32] * 6 + [ctypes.POINTER(LayoutC)]),
-    "exl3_decode_tiles": (_i32, [_vp, _i32, _i32, _vp, _vp]),
-    "exl3_profile_begin": (_i32, [_i32]),
-    "exl3_profile_end": (_i32, [ctypes.POINTER(ctypes.c_int32),
-                                ctypes.POINTER(ctypes.c_float), _i32]),
+    "exl3_decode_tiles": (_i32, [_vp, _i32, _i32, _vp, _vp, _PP]),
+    "exl3_events_create": (_i32, [_i32, ctypes.POINTER(ctypes.c_void_p)]),
+    "exl3_events_destroy": (_i32, [_i32, ctypes.POINTER(ctypes.c_void_p)]),
+    "exl3_profile_read": (_i32, [_PP, ctypes.POINTER(ctypes.c_float)]),
 }
 KERNEL_NAMES = {1: "route_pack", 2: "rotate", 3: "gemm_gateup", 4: "gemm_down",
                 5: "combine", 6: "gemm_linear", 7: "decode_tiles", 8: "gemm_experts"}
@@ -198,7 +206,7 @@ def exl3_route_pack(ids, w, num_experts, meta=None):
     meta = meta or alloc_meta(rows, topk, num_experts, ids.device)
     mc = _meta_c(meta)
     _check(lib().exl3_route_pack(_p(ids), _DT[ids.dtype], _p(w), _DT[w.dtype], rows, topk,
-                                 num_experts, ctypes.byref(mc), _stream()))
+                                 num_experts, ctypes.byref(mc), _stream(), _prof()))
     return meta
 
 
@@ -215,7 +223,7 @@ def exl3_linear(x, proj, out_dtype=torch.float32, out=None, ws=None):
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     pc = proj.cstruct()
     _check(lib().exl3_linear(_p(x), _dt(x), rows, ctypes.byref(pc), _p(out), _DT[out.dtype],
-                             _p(ws), ws.numel(), _stream()))
+                             _p(ws), ws.numel(), _stream(), _prof()))
     return out
 
 
@@ -245,7 +253,7 @@ def exl3_moe_forward(x, ids, w, gate, up, down, capacity, out_dtype=torch.float3
                                   _DT[w.dtype], topk, ctypes.byref(g), ctypes.byref(u),
                                   ctypes.byref(d), _p(out), _DT[out.dtype], capacity,
                                   num_active_hint,
-                                  _p(ws), ws.numel(), _stream()))
+                                  _p(ws), ws.numel(), _stream(), _prof()))
     return out
 
 
@@ -259,7 +267,7 @@ def exl3_moe_forward_static(x, ids, w, gate, up, down, capacity, out_dtype=torch
     _check(lib().exl3_moe_forward_static(_p(x), _dt(x), rows, _p(ids), _DT[ids.dtype], _p(w),
                                          _DT[w.dtype], topk, ctypes.byref(g), ctypes.byref(u),
                                          ctypes.byref(d), _p(out), _DT[out.dtype], capacity,
-                                         num_active_hint, _stream()))
+                                         num_active_hint, _stream(), _prof()))
     return out
 
 
@@ -279,7 +287,8 @@ def exl3_moe_additive(x, topk, meta, gate, up, down, capacity, out_dtype=torch.f
     mc = _meta_c(meta)
     _check(lib().exl3_moe_additive(_p(x), _dt(x), rows, topk, ctypes.byref(mc),
                                    ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), _p(out),
-                                   _DT[out.dtype], capacity, num_active_hint, _p(ws), ws.numel(), _stream()))
+                                   _DT[out.dtype], capacity, num_active_hint, _p(ws), ws.numel(), _stream(),
+                                   _prof()))
     return out
 
 
@@ -287,7 +296,7 @@ def exl3_decode_tiles(words, K):
     """words: uint16-bit tensor (int16 view) [ntiles * 16K] -> fp16 [ntiles][16][16]."""
     ntiles = words.numel() // (16 * K)
     out = torch.empty(ntiles, 16, 16, dtype=torch.float16, device=words.device)
-    _check(lib().exl3_decode_tiles(_p(words), ntiles, K, _p(out), _stream()))
+    _check(lib().exl3_decode_tiles(_p(words), ntiles, K, _p(out), _stream(), _prof()))
     return out
 
 
@@ -303,26 +312,46 @@ def unpermute_rotated(t):
     return out.reshape(shape)
 
 
+_active_profile = None
+
+
+def _prof():
+    """The caller-owned timing record of the enclosing ``Profile`` block, or None."""
+    return ctypes.byref(_active_profile.c) if _active_profile is not None else None
+
+
 class Profile:
-    """Per-launch kernel timing through the library's event hooks:
-    ``with Profile(n) as p: ...`` then ``p.records`` = [(name, ms), ...]."""
+    """Per-launch kernel timing: ``with Profile(n) as p: ...`` then
+    ``p.records`` = [(name, ms), ...]. The events are created on entry and
+    destroyed on exit (outside the calls being timed); inside the block every
+    call of this module passes the record to the library, which brackets each
+    of its launches with the next event pair."""
 
     def __init__(self, max_launches=4096):
         self.max = max_launches
         self.records = []
 
     def __enter__(self):
-        _check(lib().exl3_profile_begin(self.max))
+        global _active_profile
+        if _active_profile is not None:
+            raise Exl3Error("Profile blocks do not nest")
+        self._events = (ctypes.c_void_p * (2 * self.max))()
+        self._ids = (ctypes.c_int32 * self.max)()
+        _check(lib().exl3_events_create(2 * self.max, self._events))
+        self.c = ProfileC(self._events, self._ids, self.max, 0)
+        _active_profile = self
         return self
 
     def __exit__(self, *exc):
-        ids = (ctypes.c_int32 * self.max)()
+        global _active_profile
+        _active_profile = None
         ms = (ctypes.c_float * self.max)()
-        n = lib().exl3_profile_end(ids, ms, self.max)
-        if n < 0:
-            _check(n)
-        self.records = [(KERNEL_NAMES.get(ids[i], str(ids[i])), float(ms[i]))
-                        for i in range(min(n, self.max))]
+        try:
+            _check(lib().exl3_profile_read(ctypes.byref(self.c), ms))
+            self.records = [(KERNEL_NAMES.get(self._ids[i], str(self._ids[i])), float(ms[i]))
+                            for i in range(self.c.n)]
+        finally:
+            lib().exl3_events_destroy(2 * self.max, self._events)
         return False
 
 
