@@ -311,35 +311,6 @@ __device__ __forceinline__ void fwht128_group16(float (&v)[8]) {
   }
 }
 
-// Unnormalised 128-point FWHT with 8 consecutive entries per lane: lane i of
-// the 16-lane group holds entries 8i..8i+7. Distances 1, 2, 4 in registers,
-// then 8..64 across lanes (xor 1..8). Used for the input rotation only, in
-// fp64: there every butterfly is exact (the inputs are fp16 values, so any
-// sum of 128 of them spans at most 40 significant bits).
-__device__ __forceinline__ void fwht128_lane8(double (&v)[8]) {
-  const int i = threadIdx.x & 15;
-#pragma unroll
-  for (int d = 1; d < 8; d <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if ((j & d) == 0) {
-        const double lo = v[j], hi = v[j + d];
-        v[j] = lo + hi;
-        v[j + d] = lo - hi;
-      }
-    }
-  }
-#pragma unroll
-  for (int d = 1; d < 16; d <<= 1) {
-    const bool upper = (i & d) != 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const double o = __shfl_xor(v[j], d, 64);
-      v[j] = upper ? (o - v[j]) : (v[j] + o);
-    }
-  }
-}
-
 constexpr double kRsqrt128d = 0.088388347648318440550;  // 1/sqrt(128), fp64
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
@@ -349,27 +320,21 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
 }
 
-// fp64 -> fp16, round to nearest even, in one rounding. The value is first
-// rounded to fp32 (RNE). That second rounding can only go wrong where the
-// fp32 result lands exactly on the midpoint between two fp16 values while the
-// fp64 value does not: then the fp32 value is moved one fp32 ulp towards the
-// fp64 value before the fp16 rounding, so the midpoint is resolved the way
-// the fp64 value lies. (Midpoint test: the fp32 significand bits below the
-// fp16 lsb are exactly one half of it; below 2^-14 the fp16 lsb is 2^-24.)
+// fp64 -> fp16, rounded to nearest even, without branches: round to odd
+// into fp32 first (truncate towards zero, then set the last bit if anything
+// was dropped), then round that to fp16. Rounding to odd at 24 bits and then
+// to nearest at 11 gives the correctly rounded result (Boldo and Melquiond,
+// "Emulation of FMA and correctly rounded sums: proved algorithms using
+// rounding to odd", 2008: the intermediate precision exceeds the final one by
+// at least two bits). A NaN stays a NaN.
 __device__ __forceinline__ uint16_t f64_to_f16_bits(double d) {
-  float f = (float)d;
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  const int E = (int)((u >> 23) & 0xFFu) - 127;
-  const int drop = (E >= -14) ? 13 : 13 + (-14 - E);  // fp32 bits below the fp16 lsb
-  const uint32_t mant = (u & 0x7FFFFFu) | ((E > -127) ? 0x800000u : 0u);
-  const bool tie = drop <= 24 && (mant & ((1u << drop) - 1u)) == (1u << (drop - 1));
+  const float f = (float)d;  // nearest even
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
   const double back = (double)f;
-  if (tie && d != back) {
-    // away from zero if |d| > |f|, else towards zero
-    u = ((d > back) == (f > 0.0f)) ? u + 1u : u - 1u;
-    f = __builtin_bit_cast(float, u);
-  }
-  return __builtin_bit_cast(uint16_t, (_Float16)f);
+  const bool inexact = back != d && d == d;
+  const uint32_t t = u - ((fabs(back) > fabs(d)) ? 1u : 0u);  // towards zero
+  const uint32_t r = inexact ? (t | 1u) : u;
+  return __builtin_bit_cast(uint16_t, (_Float16)__builtin_bit_cast(float, r));
 }
 // bfloat16 = the upper 16 bits of an fp32, rounded to nearest even (add
 // 0x7FFF plus the lowest kept bit, then truncate); a NaN stays a (quiet) NaN.

@@ -593,8 +593,9 @@ hipError_t launch_gemm_wide_pass(const GemmParams &gu, const GemmParams &dn, int
 // left of four passes, instead of idling through one pass's stragglers.
 // Items, in dispatch order (longest first): gate/up (tile x 128-column
 // block, heavy tiles first), down (tile x 256-column block), rotation
-// (kRotPerItem x 16 (position, 128-block) units), combine (one position).
-constexpr int kRotPerItem = 4;
+// (64 (position, 128-block) units, one per lane quad), combine (one
+// position).
+constexpr int kRotUnitsPerItem = 64;
 
 template <bool MULTI>
 __global__ void __launch_bounds__(256, MULTI ? 1 : 2)
@@ -618,9 +619,7 @@ __global__ void __launch_bounds__(256, MULTI ? 1 : 2)
   }
   id -= g2;
   if (id < g3) {
-#pragma unroll 1
-    for (int u = 0; u < kRotPerItem; ++u)
-      rotate_unit(rn, ((int64_t)id * kRotPerItem + u) * 16 + (threadIdx.x >> 4), threadIdx.x & 15);
+    rotate_unit(rn, (int64_t)id * kRotUnitsPerItem + (threadIdx.x >> 2), threadIdx.x & 3);
     return;
   }
   combine_position(cb, id - g3);
@@ -635,7 +634,7 @@ hipError_t launch_gemm_wide_pipe(const GemmParams &gu, int tiles_gu, const GemmP
   const int g1 = tiles_gu > 0 ? (tiles_gu + 7) / 8 * 8 * nb_gu : 0;
   const int g2 = tiles_dn > 0 ? (tiles_dn + 7) / 8 * 8 * nb_dn : 0;
   const int64_t units = rn.nitems > 0 ? (int64_t)rn.nitems * (rn.H >> 7) : 0;
-  const int g3 = (int)((units + 16 * kRotPerItem - 1) / (16 * kRotPerItem));
+  const int g3 = (int)((units + kRotUnitsPerItem - 1) / kRotUnitsPerItem);
   const int g4 = npos_cb > 0 ? npos_cb : 0;
   const int64_t total = (int64_t)g1 + g2 + g3 + g4;
   if (total <= 0) return hipSuccess;

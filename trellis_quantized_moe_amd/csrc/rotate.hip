@@ -3,7 +3,7 @@
 
 namespace exl3 {
 
-// One 16-lane group per (item, 128-block), 16 groups per block.
+// One lane quad per (item, 128-block), 64 quads per block.
 __global__ void __launch_bounds__(256) rotate_kernel(RotParams p) {
   if (p.ctrl_clear && blockIdx.x == 0 && threadIdx.x == 0) {
     p.ctrl_clear[0] = 0;  // dropped pairs (none in a linear call)
@@ -15,14 +15,14 @@ __global__ void __launch_bounds__(256) rotate_kernel(RotParams p) {
          i += (int64_t)gridDim.x * blockDim.x)
       p.zero[i] = 0;
   }
-  rotate_unit(p, (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4), threadIdx.x & 15);
+  rotate_unit(p, (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2), threadIdx.x & 3);
 }
 
 hipError_t launch_rotate(const RotParams &p, hipStream_t s) {
   const int64_t groups = (int64_t)p.nitems * (p.H >> 7);
   if (groups <= 0) return hipSuccess;
   if (p.nproj < 1 || p.nproj > 2) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rotate_kernel, dim3((unsigned)((groups + 15) / 16)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(rotate_kernel, dim3((unsigned)((groups + 63) / 64)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

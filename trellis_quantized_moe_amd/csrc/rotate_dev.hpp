@@ -15,46 +15,90 @@
 
 namespace exl3 {
 
-// One (item, 128-block) unit whose source row and expert are known. Lane i
-// (0..15 of the group) loads entries 8i..8i+7 (16 bytes) of the x block
-// once, transforms it for every projection, and stores each result as one
-// 16-byte run in the kSigma order: slots 0..7 of its half-group hold entries
-// {0,4,1,5,2,6,3,7} of the lane's 8. Every lane of the group must call this
+// A 64-bit value from lane (l ^ D) of the same group of four lanes (D = 1
+// or 2), by two DPP quad permutes: no LDS traffic, unlike a bpermute.
+template <int D>
+__device__ __forceinline__ double quad_xor(double v) {
+  static_assert(D == 1 || D == 2, "quad lanes");
+  constexpr int ctrl = (D == 1) ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, ctrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), ctrl, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// One (item, 128-block) unit whose source row and expert are known, done by
+// the 4 lanes of a lane quad. Lane i (0..3 of the quad) loads entries
+// 32i .. 32i + 31 (64 bytes) of the x block once and, for every projection,
+// multiplies by suh (exact: the signs are +-1), runs the five butterfly
+// levels of distances 1..16 in its registers and the two of distances 32
+// and 64 across the quad (DPP), all in fp64 (exact for fp16 inputs: any sum
+// of 128 of them spans at most 47 significant bits), scales by 1/sqrt(128)
+// and rounds once to fp16. Each 16-entry group is stored in the kSigma
+// order (slot p holds entry kSigma[p]). Every lane of the quad must call this
 // with the same unit.
-__device__ __forceinline__ void rotate_block(const RotParams &p, int item, int blk, int row, int e,
-                                             int i) {
-  const int64_t col = blk * 128 + 8 * i;
-  const u32x4 xv = *(const u32x4 *)(p.x + (int64_t)row * p.H + col);
-  u32x4 sv[2];
+template <bool BF16>
+__device__ __forceinline__ void rotate_block_t(const RotParams &p, int item, int blk, int row,
+                                               int e, int i) {
+  const int64_t col = blk * 128 + 32 * i;
+  const u32x4 *xp = (const u32x4 *)(p.x + (int64_t)row * p.H + col);
+  u32x4 xv[4];
 #pragma unroll
-  for (int pj = 0; pj < 2; ++pj)
-    if (pj < p.nproj) sv[pj] = *(const u32x4 *)(p.suh[pj] + (int64_t)e * p.H + col);
+  for (int c = 0; c < 4; ++c) xv[c] = xp[c];
+  const bool upper1 = (i & 1) != 0, upper2 = (i & 2) != 0;
+#pragma unroll 1
+  for (int pj = 0; pj < p.nproj; ++pj) {
+    const u32x4 *sp = (const u32x4 *)(p.suh[pj] + (int64_t)e * p.H + col);
+    u32x4 sv[4];
 #pragma unroll
-  for (int pj = 0; pj < 2; ++pj) {
-    if (pj >= p.nproj) break;
+    for (int c = 0; c < 4; ++c) sv[c] = sp[c];
     // halves are unpacked with shifts: this compiler mis-compiles a bit_cast
     // of a vector element taken inside an unrolled loop (it reuses element 0)
-    double v[8];
+    double v[32];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t xw = xv[j], sw = sv[pj][j];
-      const float x0 = p.x_bf16 ? bf16_bits_to_f32((uint16_t)(xw & 0xFFFFu))
-                                : f16_bits_to_f32((uint16_t)(xw & 0xFFFFu));
-      const float x1 = p.x_bf16 ? bf16_bits_to_f32((uint16_t)(xw >> 16))
-                                : f16_bits_to_f32((uint16_t)(xw >> 16));
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t xw = xv[j >> 2][j & 3], sw = sv[j >> 2][j & 3];
+      const float x0 = BF16 ? bf16_bits_to_f32((uint16_t)(xw & 0xFFFFu))
+                            : f16_bits_to_f32((uint16_t)(xw & 0xFFFFu));
+      const float x1 = BF16 ? bf16_bits_to_f32((uint16_t)(xw >> 16))
+                            : f16_bits_to_f32((uint16_t)(xw >> 16));
       v[2 * j] = (double)(x0 * f16_bits_to_f32((uint16_t)(sw & 0xFFFFu)));
       v[2 * j + 1] = (double)(x1 * f16_bits_to_f32((uint16_t)(sw >> 16)));
     }
-    // exact butterflies and one rounding: x~ is the fp16 value nearest to
-    // Hhat(x * suh) itself
-    fwht128_lane8(v);
-    uint16_t h[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) h[j] = f64_to_f16_bits(v[j] * kRsqrt128d);
-    const u32x4 o = {(uint32_t)h[0] | ((uint32_t)h[4] << 16), (uint32_t)h[1] | ((uint32_t)h[5] << 16),
-                     (uint32_t)h[2] | ((uint32_t)h[6] << 16), (uint32_t)h[3] | ((uint32_t)h[7] << 16)};
-    *(u32x4 *)(p.xt + ((int64_t)item * p.nproj + pj) * p.H + col) = o;
+    for (int d = 1; d < 32; d <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if ((j & d) == 0) {
+          const double lo = v[j], hi = v[j + d];
+          v[j] = lo + hi;
+          v[j + d] = lo - hi;
+        }
+      }
+    }
+    // across the quad: the lower lane of a pair keeps v + o, the upper o - v
+    const double s1 = upper1 ? -1.0 : 1.0, s2 = upper2 ? -1.0 : 1.0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] = fma(v[j], s1, quad_xor<1>(v[j]));
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] = fma(v[j], s2, quad_xor<2>(v[j]));
+    uint16_t h[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) h[j] = f64_to_f16_bits(v[j] * kRsqrt128d);
+    u32x4 *op = (u32x4 *)(p.xt + ((int64_t)item * p.nproj + pj) * p.H + col);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {  // 8 entries: slots {0,4,1,5,2,6,3,7}
+      const uint16_t *q = h + 8 * g;
+      op[g] = (u32x4){(uint32_t)q[0] | ((uint32_t)q[4] << 16), (uint32_t)q[1] | ((uint32_t)q[5] << 16),
+                      (uint32_t)q[2] | ((uint32_t)q[6] << 16), (uint32_t)q[3] | ((uint32_t)q[7] << 16)};
+    }
   }
+}
+
+__device__ __forceinline__ void rotate_block(const RotParams &p, int item, int blk, int row, int e,
+                                             int i) {
+  if (p.x_bf16) rotate_block_t<true>(p, item, blk, row, e, i);
+  else rotate_block_t<false>(p, item, blk, row, e, i);
 }
 
 // Unit gid = item * (H / 128) + block: the row and expert of the item come
@@ -67,7 +111,7 @@ __device__ __forceinline__ void rotate_unit(const RotParams &p, int64_t gid, int
   int row, e;
   if (p.pair_of_pos != nullptr) {
     const int pos = p.pass_base + item;
-    if (pos >= min(*p.total_valid, p.pairs)) return;  // uniform per group
+    if (pos >= min(*p.total_valid, p.pairs)) return;  // uniform per quad
     const int q = p.pair_of_pos[pos];
     if (q < 0 || q >= p.pairs) return;  // inconsistent metadata: drop
     row = q / p.topk;
