@@ -291,30 +291,123 @@ def run_additive(args, torch, exl3, synth, reps=20):
             "layer_hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
-def cpu_baseline(wl, synth, rows=(0, 1)):
-    """The float64 oracle on a bounded sample of the prefill workload: whole
-    tokens (rows 0 and 1, all 8 routed pairs each) through the layer, expert
-    dequantisation included, on one thread (BLAS limited to 1)."""
+# ------------------------------------------------------------- CPU baseline
+# The float64 oracle, as it stands, timed on the host's cores: a process pool
+# (spawned workers, BLAS limited to one thread each) over a bounded sample of
+# each workload. The unit of work is one routed pair (MoE layers: gate and up,
+# SwiGLU, down; expert dequantisation included) or one row (linear); a
+# worker's pairs are grouped by expert so each dequantises an expert once.
+
+_CPU_WL = {}
+
+
+def _cpu_workload(key):
+    from trellis_quantized_moe_amd import synth
+    if key not in _CPU_WL:
+        if key[0] == "moe":
+            _CPU_WL[key] = synth.moe_workload(key[1], rows=key[2], materialize=False)
+        else:
+            _CPU_WL[key] = synth.linear_workload(key[1], key[2])
+    return _CPU_WL[key]
+
+
+def _cpu_warm(keys):
+    """Worker start-up, outside the timed region: imports, the workloads'
+    inputs and the BLAS description."""
+    import numpy  # noqa: F401
+    from threadpoolctl import threadpool_info
+
+    import oracle.moe  # noqa: F401
+    for k in keys:
+        _cpu_workload(k)
+    return [(i.get("internal_api"), i.get("version")) for i in threadpool_info()]
+
+
+def _cpu_task(task):
+    """One worker's share of a sample; returns its busy seconds."""
     from threadpoolctl import threadpool_limits
 
+    from oracle import linear as olin
     from oracle import moe as omoe
     from oracle.linear import WeightCache
-
-    pairs = [(r, j, int(wl.ids[r, j])) for r in rows for j in range(wl.topk)
-             if 0 <= int(wl.ids[r, j]) < wl.num_experts]
-    experts = {e for _, _, e in pairs}
-    views = [synth.materialized_view(p, experts) for p in (wl.gate, wl.up, wl.down)]
+    from trellis_quantized_moe_amd import synth
+    key, items = task
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        cache = WeightCache()
-        for r, j, e in pairs:
-            at = omoe.stage1(wl.x[r:r + 1].astype(np.float64), e, *views, "R", cache)
-            omoe.down_output(at, e, views[2], cache)
-        dt = time.perf_counter() - t0
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "prefill workload, rows %s with all their routed pairs (%d pairs, %d experts) "
-                      "through the float64 oracle, dequantisation included: %.1f s"
-                      % (list(rows), len(pairs), len(experts), dt)}
+        if key[0] == "moe":
+            wl = _cpu_workload(key)
+            experts = {e for _, _, e in items}
+            views = [synth.materialized_view(p, experts) for p in (wl.gate, wl.up, wl.down)]
+            t0 = time.perf_counter()
+            cache = WeightCache()
+            for r, j, e in items:
+                at = omoe.stage1(wl.x[r:r + 1].astype(np.float64), e, *views, "R", cache)
+                omoe.down_output(at, e, views[2], cache)
+        else:
+            proj, x = _cpu_workload(key)
+            t0 = time.perf_counter()
+            olin.linear(x[list(items)].astype(np.float64), proj, "R", WeightCache())
+        return time.perf_counter() - t0
+
+
+def _cpu_samples(synth):
+    """(name, key, tokens, work items) of each sampled workload."""
+    out = []
+    # (workload, its rows, the sampled rows); decode: the 32-row layer
+    for name, nrows, rows in (("prefill", 3072, range(8)), ("decode", 32, range(2)),
+                              ("additive", 128, range(2))):
+        wl = synth.moe_workload(name, rows=nrows, materialize=False)
+        pairs = [(r, j, int(wl.ids[r, j])) for r in rows for j in range(wl.topk)
+                 if 0 <= int(wl.ids[r, j]) < wl.num_experts]
+        out.append((name, ("moe", name, nrows), len(rows), pairs))
+    out.append(("linear_K4", ("linear", 4, 64), 64, list(range(64))))
+    return out
+
+
+def cpu_baseline(synth):
+    """The oracle over the host's cores (see above, at most 16 workers) on
+    bounded samples: 8 prefill rows (64 pairs), 2 rows of the 32-row decode
+    layer, 2 additive rows, 64 rows of the 4096 -> 4096 K = 4 linear. Returns
+    the prefill figure (the headline workload) with the others under
+    'per_workload'."""
+    import multiprocessing
+    import platform
+    from concurrent.futures import ProcessPoolExecutor
+
+    samples = _cpu_samples(synth)
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    res = {}
+    ctx = multiprocessing.get_context("spawn")
+    with ProcessPoolExecutor(workers, mp_context=ctx) as ex:
+        blas = list(ex.map(_cpu_warm, [[k for _, k, _, _ in samples]] * workers))[0]
+        for name, key, tokens, items in samples:
+            if key[0] == "moe":
+                items = sorted(items, key=lambda t: (t[2], t[0], t[1]))
+            n = min(workers, len(items))
+            tasks = [(key, items[len(items) * i // n:len(items) * (i + 1) // n]) for i in range(n)]
+            t0 = time.perf_counter()
+            busy = list(ex.map(_cpu_task, tasks))
+            wall = time.perf_counter() - t0
+            res[name] = {"value": tokens / wall, "unit": "tokens/s", "cores": n,
+                         "wall_s": wall, "busy_s": sum(busy),
+                         "sample": "%d tokens, %d %s over %d worker processes" % (
+                             tokens, len(items), "pairs" if key[0] == "moe" else "rows", n)}
+    head = res["prefill"]
+    return {"value": head["value"], "unit": "tokens/s", "cores": head["cores"], "kind": "oracle",
+            "sample": "prefill workload, rows 0-7 with all their routed pairs (%s) through the "
+                      "float64 oracle, expert dequantisation included; %.1f s wall"
+                      % (head["sample"], head["wall_s"]),
+            "host": {"cpu": model, "threads_available": len(os.sched_getaffinity(0)),
+                     "numpy": np.__version__, "blas": blas},
+            "per_workload": res}
 
 
 KERNEL_SOURCES = ("gemm_wide.hip", "gemm_shared.hpp", "common.hpp", "kernels.hpp",
@@ -431,7 +524,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         _log("cpu baseline (oracle)")
-        cpu = cpu_baseline(wl, synth)
+        cpu = cpu_baseline(synth)
 
     line = {
         "metric": METRIC, "value": pre["tokens_per_s"], "unit": "tokens/s",
