@@ -288,6 +288,68 @@ def test_dropped_ids_and_unrouted_rows():
             assert _rel_err(y.cpu().double().numpy(), ref) <= (TOL if dt == torch.float32 else 5e-3)
 
 
+def _ws_meta(ws, rows, topk, E, H, I, cap):
+    """The pack metadata a forward call left in its workspace (the layout of
+    exl3moe.h: count, offset, pair_of_pos, weight_of_pos, pos_of_pair, each
+    256-byte aligned, then expert_of_pos)."""
+    lay = exl3.moe_layout(rows, topk, E, H, I, cap)
+    P = rows * topk
+    b = ws.cpu().numpy()
+    al = lambda v: (v + 255) // 256 * 256
+    o = lay.meta
+    out = {}
+    for name, n, dt in (("count", E, np.int32), ("offset", E + 1, np.int32),
+                        ("pair_of_pos", P, np.int32), ("weight_of_pos", P, np.float32),
+                        ("pos_of_pair", P, np.int32)):
+        out[name] = b[o:o + 4 * n].view(dt)
+        o = al(o + 4 * n)
+    out["expert_of_pos"] = b[lay.expert_of_pos:lay.expert_of_pos + 4 * P].view(np.int32)
+    return out
+
+
+@pytest.mark.parametrize("rows,topk,E,idt,seed", [(1200, 8, 64, "i32", 11),
+                                                   (3072, 8, 192, "i64", 12)])
+def test_forward_pack_many_pairs_bit_exact(rows, topk, E, idt, seed):
+    """Calls with 8192 pairs or more pack over several workgroups (three
+    launches): the metadata they leave in the workspace must be the oracle's
+    stable pack bit for bit (dropped IDs, fully dropped rows, skewed counts),
+    expert_of_pos must label every kept position with its expert, and rows
+    with no kept pair must come out as zeros."""
+    _say("forward pack", rows, topk, E, idt)
+    wl = synth.moe_workload("tiny", rows=rows, topk=topk, E=E)
+    rng = np.random.default_rng(seed)
+    pop = rng.zipf(1.3, size=(rows, topk)) % E  # skewed expert popularity
+    ids_np = np.where(rng.random((rows, topk)) < 0.03, rng.integers(-3, 0, (rows, topk)),
+                      pop).astype(np.int64)
+    ids_np[7, :] = E + 1               # a fully dropped row
+    ids_np[rows - 2, :] = -1           # another, near the end
+    wl.ids = ids_np.astype(np.int64 if idt == "i64" else np.int32)
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    cap = rows * topk
+    need = exl3.moe_workspace_size(rows, topk, E, wl.hidden, wl.intermediate, cap)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    out = torch.full((rows, wl.hidden), 7.0, dtype=torch.float32, device=DEV)
+    y = moe_forward(x, ids, w, gate, up, down, cap, torch.float32, out=out, ws=ws)
+    torch.cuda.synchronize()
+    got = _ws_meta(ws, rows, topk, E, wl.hidden, wl.intermediate, cap)
+    ref = oroute.route_pack(ids_np, wl.weights_f64, E)
+    kept = int(ref["offset"][E])
+    assert np.array_equal(got["count"], ref["count"])
+    assert np.array_equal(got["offset"], ref["offset"])
+    assert np.array_equal(got["pair_of_pos"][:kept], ref["pair_of_pos"][:kept])
+    assert np.all(got["pair_of_pos"][kept:] == -1)
+    assert np.array_equal(got["pos_of_pair"], ref["pos_of_pair"])
+    assert np.array_equal(got["weight_of_pos"][:kept].astype(np.float64),
+                          ref["weight_of_pos"][:kept])
+    lab = np.repeat(np.arange(E), ref["count"])
+    assert np.array_equal(got["expert_of_pos"][:kept], lab)
+    yc = y.cpu().numpy()
+    assert np.all(yc[7] == 0) and np.all(yc[rows - 2] == 0)
+    rs = [0, 1, rows // 2, rows - 1]
+    refy = omoe.moe_forward(wl.x, wl.ids, wl.weights_f64, wl.gate, wl.up, wl.down, "R", rows=rs)
+    assert _rel_err(yc[rs].astype(np.float64), refy) <= TOL
+
+
 # ---------------------------------------------------- full-size workloads
 def _sampled_parity(wl, rows_sample, capacity):
     gate, up, down, x, ids, w = _moe_inputs(wl)

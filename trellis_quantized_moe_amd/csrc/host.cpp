@@ -113,7 +113,7 @@ bool linear_wide(int rows, int out) {
 
 struct MoeLayout {
   size_t ctrl, count, offset, pair_of_pos, weight_of_pos, pos_of_pair, num_active, status;
-  size_t expert_of_pos, plan, xt, at, d, yacc, nacc, ncnt, total;
+  size_t expert_of_pos, plan, xt, at, d, yacc, nacc, ncnt, pack, total;
   int passes, slots, cap, ncnt_ints;
   // A launch unit is `group` consecutive passes (on the pipelined path 4
   // with 8+ passes, 2 with 4-7, else 1): one plan, one buffer set of
@@ -184,6 +184,7 @@ MoeLayout moe_layout(int32_t rows, int32_t topk, int32_t E, int32_t H, int32_t I
                 : L.fused ? 4 * (size_t)C * (2 * I + H)
                           : 4 * (size_t)C * std::max(2 * I, H));
   L.ncnt = take(4 * (size_t)L.ncnt_ints);
+  L.pack = take(4 * pack_scratch_ints(P, E));
   L.total = o;
   return L;
 }
@@ -700,6 +701,8 @@ int32_t moe_forward_impl(const uint16_t *x, int32_t x_dtype, int32_t rows, const
   p.ctrl = at<int32_t>(ws, L.ctrl);
   p.zero = L.ncnt_ints ? at<int32_t>(ws, L.ncnt) : nullptr;
   p.nzero = L.ncnt_ints;
+  p.gwc = at<int32_t>(ws, L.pack);
+  p.nblk = pack_blocks((int64_t)rows * topk);
   // few pairs in one pass: the pack runs inside the first rotation's launch
   const bool fuse = !L.pipe && pack_rotate_fits((int64_t)rows * topk, L.passes);
   if (!fuse) {

@@ -112,6 +112,10 @@ struct PackParams {
                   // [2] waits that gave up (both zeroed)
   int32_t *zero;  // narrow-tile completion counts, zeroed (nzero ints)
   int nzero;
+  // the pack over several workgroups (many pairs): per-wave counts and
+  // positions [nblk][16][E] plus nblk dropped counts (pack_scratch_ints)
+  int32_t *gwc;
+  int nblk;
 };
 
 hipError_t launch_gemm(int epi, const GemmParams &p, int tiles, int nblocks,
@@ -137,6 +141,10 @@ hipError_t launch_rotate(const RotParams &p, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int npos, hipStream_t s);
 hipError_t launch_combine_rows(const CombineParams &p, hipStream_t s);
 hipError_t launch_pack(const PackParams &p, hipStream_t s);
+// Scratch ints launch_pack needs in PackParams::gwc for a pack of `pairs`
+// pairs (0: none), and its workgroup count PackParams::nblk.
+size_t pack_scratch_ints(int64_t pairs, int E);
+int pack_blocks(int64_t pairs);
 // Pack, one-pass plan and the rotation of that pass in one launch, for calls
 // where pack_rotate_fits (few pairs, one pass). rp: the pass's rotation.
 bool pack_rotate_fits(int64_t pairs, int passes);

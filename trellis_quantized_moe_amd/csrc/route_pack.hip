@@ -237,6 +237,127 @@ __device__ void plan_units(const PackParams &p, const int *s_off, int E, int kep
   }
 }
 
+// ---------------------------------------------------- phases of the pack
+// Shared by the one-workgroup kernel and the three-launch form for many
+// pairs. A wave's segment of pairs [q0, q1) is walked in rounds of 64 pairs
+// in pair order.
+
+// a1: the segment's pairs counted per expert into wc (this wave's LDS row);
+// returns the number of pairs with an ID outside [0, E).
+__device__ __forceinline__ int count_segment(const PackParams &p, int q0, int q1, int *wc,
+                                             int lane) {
+  int drop = 0;
+  for (int qb = q0; qb < q1; qb += 64 * kPackBatch) {
+    int eb[kPackBatch];
+#pragma unroll
+    for (int i = 0; i < kPackBatch; ++i) {
+      const int q = qb + 64 * i + lane;
+      eb[i] = (q < q1) ? load_expert(p.ids, p.ids_i64, q, p.E) : -2;
+    }
+#pragma unroll
+    for (int i = 0; i < kPackBatch; ++i) {
+      const int e = eb[i];
+      if (e >= 0) atomicAdd(&wc[e], 1);  // counts are order-free
+      drop += (e == -1) ? 1 : 0;
+    }
+  }
+  return drop;
+}
+
+// a3: stable scatter of the segment; wc[e] holds the next position of expert
+// e for this wave. Inside a round, the lanes holding the same expert find
+// each other with ballots, so positions follow pair order without atomics.
+__device__ __forceinline__ void scatter_segment(const PackParams &p, int q0, int q1, int *wc,
+                                                int lane) {
+  const int E = p.E;
+  const int nb = 32 - __clz(E);  // bits of the keys 0 .. E
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int qb = q0; qb < q1; qb += 64 * kPackBatch) {
+    int eb[kPackBatch];
+    float wb[kPackBatch];
+#pragma unroll
+    for (int i = 0; i < kPackBatch; ++i) {
+      const int q = qb + 64 * i + lane;
+      const bool in = q < q1;
+      eb[i] = in ? load_expert(p.ids, p.ids_i64, q, E) : -2;
+      wb[i] = in ? load_weight(p.w, p.w_dtype, q) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kPackBatch; ++i) {
+      if (qb + 64 * i >= q1) break;  // uniform
+      const int q = qb + 64 * i + lane;
+      const int e = eb[i];
+      const bool valid = e >= 0;
+      const uint64_t m = match_key(valid ? e : E, __ballot(valid), nb);
+      if (valid) {
+        const int rank = __popcll(m & lt_mask);
+        const int base = wc[e];
+        const int pos = base + rank;
+        if (rank == 0) wc[e] = base + __popcll(m);
+        p.pair_of_pos[pos] = q;
+        p.weight_of_pos[pos] = wb[i];
+        p.pos_of_pair[q] = pos;
+      } else if (e == -1) {
+        p.pos_of_pair[q] = -1;
+      }
+    }
+  }
+}
+
+// The positions [a, b) of the metadata after the pack: empty ones past the
+// kept pairs cleared, kept ones given their expert (positions before the
+// first span, possible only with caller-supplied offsets, get expert 0).
+// s_off: the expert offsets (E + 1). Threads t of nt.
+__device__ __forceinline__ void finish_positions(const PackParams &p, const int *s_off, int a,
+                                                 int b, int t, int nt, bool clear_tail) {
+  const int E = p.E, kept = s_off[E];
+  for (int pos = a + t; pos < b; pos += nt) {
+    if (pos >= kept) {
+      if (clear_tail) {
+        p.pair_of_pos[pos] = -1;
+        p.weight_of_pos[pos] = 0.0f;
+      }
+      continue;
+    }
+    if (p.do_plan) p.expert_of_pos[pos] = (pos < s_off[0]) ? 0 : expert_at(s_off, E, pos);
+  }
+}
+
+// Zero output rows r in [r0, r1) none of whose pairs is kept.
+__device__ __forceinline__ void zero_unrouted_rows(const PackParams &p, int r0, int r1, int t,
+                                                   int nt) {
+  for (int r = r0 + t; r < r1; r += nt) {
+    bool any = false;
+    for (int j = 0; j < p.topk; ++j) any |= p.pos_of_pair[r * p.topk + j] >= 0;
+    if (!any) {
+      for (int c = 0; c < p.H; ++c) {
+        if (p.out_f32) ((float *)p.out)[(int64_t)r * p.H + c] = 0.0f;
+        else ((uint16_t *)p.out)[(int64_t)r * p.H + c] = 0;
+      }
+    }
+  }
+}
+
+// a4 and the clears of the call: the plan of every launch unit, ctrl[1..2]
+// and the completion counts. One workgroup of kPackThreads; s_wc is free
+// LDS for the parallel planner.
+__device__ __forceinline__ void plan_and_clear(const PackParams &p, const int *s_off, int *s_wc,
+                                               int tid) {
+  const int E = p.E, w = tid >> 6, lane = tid & 63;
+  if (tid == 0 && p.ctrl) {
+    p.ctrl[1] = 0;  // bad stage entries
+    p.ctrl[2] = 0;  // waits that gave up
+  }
+  for (int i = tid; i < p.nzero; i += kPackThreads) p.zero[i] = 0;
+  const int kept = s_off[E];
+  if (p.group > 1 && p.passes <= kPackWaves * kMaxE) {
+    __syncthreads();  // s_wc is free
+    plan_units_parallel(p, s_off, E, kept, w, kPackWaves, lane, s_wc);
+  } else {
+    plan_units(p, s_off, E, kept, w, kPackWaves, lane);
+  }
+}
+
 __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
   __shared__ int s_wc[kPackWaves][kMaxE];  // per wave: count, then next position
   __shared__ int s_off[kMaxE + 1];
@@ -253,28 +374,12 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
     const int seg = (((pairs + kPackWaves - 1) / kPackWaves) + 63) & ~63;
     const int q0 = w * seg;
     const int q1 = min(q0 + seg, pairs);
-    const int nb = 32 - __clz(E);  // bits of the keys 0 .. E
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int *wc = s_wc[w];
     for (int e = lane; e < E; e += 64) wc[e] = 0;
     __syncthreads();
 
     // a1: this wave's histogram (only this wave touches its row)
-    int drop = 0;
-    for (int qb = q0; qb < q1; qb += 64 * kPackBatch) {
-      int eb[kPackBatch];
-#pragma unroll
-      for (int i = 0; i < kPackBatch; ++i) {
-        const int q = qb + 64 * i + lane;
-        eb[i] = (q < q1) ? load_expert(p.ids, p.ids_i64, q, E) : -2;
-      }
-#pragma unroll
-      for (int i = 0; i < kPackBatch; ++i) {
-        const int e = eb[i];
-        if (e >= 0) atomicAdd(&wc[e], 1);  // counts are order-free
-        drop += (e == -1) ? 1 : 0;
-      }
-    }
+    const int drop = count_segment(p, q0, q1, wc, lane);
     if (drop) atomicAdd(&s_dropped, drop);
     __syncthreads();
 
@@ -310,40 +415,8 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
     }
 
     // a3: stable scatter, the same walk again
-    for (int qb = q0; qb < q1; qb += 64 * kPackBatch) {
-      int eb[kPackBatch];
-      float wb[kPackBatch];
-#pragma unroll
-      for (int i = 0; i < kPackBatch; ++i) {
-        const int q = qb + 64 * i + lane;
-        const bool in = q < q1;
-        eb[i] = in ? load_expert(p.ids, p.ids_i64, q, E) : -2;
-        wb[i] = in ? load_weight(p.w, p.w_dtype, q) : 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < kPackBatch; ++i) {
-        if (qb + 64 * i >= q1) break;  // uniform
-        const int q = qb + 64 * i + lane;
-        const int e = eb[i];
-        const bool valid = e >= 0;
-        const uint64_t m = match_key(valid ? e : E, __ballot(valid), nb);
-        if (valid) {
-          const int rank = __popcll(m & lt_mask);
-          const int base = wc[e];
-          const int pos = base + rank;
-          if (rank == 0) wc[e] = base + __popcll(m);
-          p.pair_of_pos[pos] = q;
-          p.weight_of_pos[pos] = wb[i];
-          p.pos_of_pair[q] = pos;
-        } else if (e == -1) {
-          p.pos_of_pair[q] = -1;
-        }
-      }
-    }
-    for (int pos = s_off[E] + tid; pos < pairs; pos += kPackThreads) {
-      p.pair_of_pos[pos] = -1;
-      p.weight_of_pos[pos] = 0.0f;
-    }
+    scatter_segment(p, q0, q1, wc, lane);
+    finish_positions(p, s_off, 0, pairs, tid, kPackThreads, true);
   } else {
     // caller-supplied offsets, clamped into the pairs and made nondecreasing
     // (a prefix maximum leaves consistent offsets unchanged), so every index
@@ -359,40 +432,130 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
     if (drop) atomicAdd(&s_dropped, drop);
     __syncthreads();
     if (tid == 0 && p.ctrl) p.ctrl[0] = s_dropped;
+    if (p.do_plan) finish_positions(p, s_off, 0, pairs, tid, kPackThreads, false);
   }
 
   if (!p.do_plan) return;
-  if (tid == 0 && p.ctrl) {
-    p.ctrl[1] = 0;  // bad stage entries
-    p.ctrl[2] = 0;  // waits that gave up
-  }
-  for (int i = tid; i < p.nzero; i += kPackThreads) p.zero[i] = 0;
+  plan_and_clear(p, s_off, &s_wc[0][0], tid);
 
-  // expert of every kept position, one expert per wave at a time (positions
-  // before the first span, possible only with caller-supplied offsets, get
-  // expert 0)
-  const int kept = s_off[E];
-  for (int e = w; e < E; e += kPackWaves) {
-    const int a = (e == 0) ? 0 : s_off[e], b = s_off[e + 1];
-    for (int pos = a + lane; pos < b; pos += 64) p.expert_of_pos[pos] = e;
-  }
-
-  // a4: one wave per pass (units of grouped passes: count, then write)
-  if (p.group > 1 && p.passes <= kPackWaves * kMaxE) {
-    __syncthreads();  // the per-wave position counters are free
-    plan_units_parallel(p, s_off, E, kept, w, kPackWaves, lane, &s_wc[0][0]);
-  } else {
-    plan_units(p, s_off, E, kept, w, kPackWaves, lane);
-  }
-
-  // rows whose pairs were all dropped produce zeros: one row per thread to
-  // find them (rare), then the row is cleared by that thread. A pack that
+  // rows whose pairs were all dropped produce zeros (rare). A pack that
   // dropped nothing has no such row.
   __syncthreads();
-  if (p.out && (!p.do_pack || s_dropped > 0)) {
-    for (int r = tid; r < p.rows; r += kPackThreads) {
+  if (p.out && (!p.do_pack || s_dropped > 0)) zero_unrouted_rows(p, 0, p.rows, tid, kPackThreads);
+}
+
+// ------------------------------------------- the pack over many workgroups
+// For many pairs the walk above is split over nblk workgroups of kPackThreads
+// in three launches (stream order carries every dependency): block b owns
+// pairs [b S, (b + 1) S), S = kPairsPerPackBlock, and its wave w the w-th
+// sixteenth of them.
+//   pack_count_kernel: every wave counts its pairs per expert into gwc[b][w][e];
+//   pack_scan_kernel (one workgroup): expert totals, the exclusive scan over
+//     experts and over (b, w) in that order, written back into gwc as each
+//     wave's first position per expert; counts, offsets and status words;
+//   pack_scatter_kernel: every wave scatters its pairs from those positions
+//     (the same positions as one walk over all pairs), then clears and labels
+//     its block's share of the positions; one extra workgroup plans.
+constexpr int kPairsPerPackBlock = 4096;
+
+int pack_blocks(int64_t pairs) { return (int)((pairs + kPairsPerPackBlock - 1) / kPairsPerPackBlock); }
+
+__device__ __forceinline__ void pack_block_segment(const PackParams &p, int b, int w, int &q0,
+                                                   int &q1) {
+  const int pairs = p.rows * p.topk;
+  const int seg = kPairsPerPackBlock / kPackWaves;  // whole rounds of 64
+  q0 = min(b * kPairsPerPackBlock + w * seg, pairs);
+  q1 = min(q0 + seg, pairs);
+}
+
+__global__ void __launch_bounds__(kPackThreads) pack_count_kernel(PackParams p) {
+  __shared__ int s_wc[kPackWaves][kMaxE];
+  __shared__ int s_dropped;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, b = blockIdx.x, E = p.E;
+  if (tid == 0) s_dropped = 0;
+  int *wc = s_wc[w];
+  for (int e = lane; e < E; e += 64) wc[e] = 0;
+  __syncthreads();
+  int q0, q1;
+  pack_block_segment(p, b, w, q0, q1);
+  const int drop = count_segment(p, q0, q1, wc, lane);
+  if (drop) atomicAdd(&s_dropped, drop);
+  int32_t *g = p.gwc + ((int64_t)b * kPackWaves + w) * E;
+  for (int e = lane; e < E; e += 64) g[e] = wc[e];
+  __syncthreads();
+  if (tid == 0) p.gwc[(int64_t)p.nblk * kPackWaves * E + b] = s_dropped;
+}
+
+__global__ void __launch_bounds__(kPackThreads) pack_scan_kernel(PackParams p) {
+  __shared__ int s_tmp[kPackWaves];
+  const int tid = threadIdx.x, E = p.E, nw = p.nblk * kPackWaves;
+  // one block's 16 wave counts per step, loaded together
+  int c = 0;
+  if (tid < E)
+    for (int b = 0; b < p.nblk; ++b) {
+      int v[kPackWaves];
+#pragma unroll
+      for (int w = 0; w < kPackWaves; ++w) v[w] = p.gwc[(int64_t)(b * kPackWaves + w) * E + tid];
+#pragma unroll
+      for (int w = 0; w < kPackWaves; ++w) c += v[w];
+    }
+  int total;
+  const int ex = block_exclusive_scan(c, s_tmp, total);
+  int nact;
+  block_exclusive_scan((tid < E && c > 0) ? 1 : 0, s_tmp, nact);
+  if (tid < E) {
+    int run = ex;
+    for (int b = 0; b < p.nblk; ++b) {
+      int32_t *g = p.gwc + (int64_t)b * kPackWaves * E + tid;
+      int v[kPackWaves];
+#pragma unroll
+      for (int w = 0; w < kPackWaves; ++w) v[w] = g[(int64_t)w * E];
+#pragma unroll
+      for (int w = 0; w < kPackWaves; ++w) {
+        g[(int64_t)w * E] = run;
+        run += v[w];
+      }
+    }
+    p.count[tid] = c;
+    p.offset[tid] = ex;
+  }
+  if (tid == 0) {
+    int dropped = 0;
+    for (int b = 0; b < p.nblk; ++b) dropped += p.gwc[(int64_t)nw * E + b];
+    p.offset[E] = total;
+    *p.num_active = nact;
+    *p.status = dropped;
+    if (p.ctrl) p.ctrl[0] = dropped;
+  }
+}
+
+__global__ void __launch_bounds__(kPackThreads) pack_scatter_kernel(PackParams p) {
+  __shared__ int s_wc[kPackWaves][kMaxE];
+  __shared__ int s_off[kMaxE + 1];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, b = blockIdx.x, E = p.E;
+  for (int e = tid; e <= E; e += kPackThreads) s_off[e] = p.offset[e];
+  if (b == p.nblk) {  // the planner
+    __syncthreads();
+    if (p.do_plan) plan_and_clear(p, s_off, &s_wc[0][0], tid);
+    return;
+  }
+  int *wc = s_wc[w];
+  const int32_t *g = p.gwc + ((int64_t)b * kPackWaves + w) * E;
+  for (int e = lane; e < E; e += 64) wc[e] = g[e];
+  __syncthreads();
+  int q0, q1;
+  pack_block_segment(p, b, w, q0, q1);
+  scatter_segment(p, q0, q1, wc, lane);
+  const int pairs = p.rows * p.topk;
+  const int a = min(b * kPairsPerPackBlock, pairs), z = min(a + kPairsPerPackBlock, pairs);
+  finish_positions(p, s_off, a, z, tid, kPackThreads, true);
+  // rows with no kept pair (IDs all outside [0, E)) produce zeros: the rows
+  // whose first pair is in this block, found from their IDs
+  if (p.out && p.do_plan && *p.status > 0) {
+    const int r0 = (a + p.topk - 1) / p.topk, r1 = (z + p.topk - 1) / p.topk;
+    for (int r = r0 + tid; r < r1; r += kPackThreads) {
       bool any = false;
-      for (int j = 0; j < p.topk; ++j) any |= p.pos_of_pair[r * p.topk + j] >= 0;
+      for (int j = 0; j < p.topk; ++j) any |= load_expert(p.ids, p.ids_i64, r * p.topk + j, E) >= 0;
       if (!any) {
         for (int c = 0; c < p.H; ++c) {
           if (p.out_f32) ((float *)p.out)[(int64_t)r * p.H + c] = 0.0f;
@@ -606,13 +769,31 @@ bool pack_rotate_fits(int64_t pairs, int passes) { return pairs <= kSmallPairs &
 // with more pairs the 16-wave kernel measured faster there.
 constexpr int kSmallPackAlone = 64;
 
+// From this many pairs the pack runs over several workgroups (three
+// launches, pack_count/scan/scatter): on the 24576-pair prefill layer the one
+// workgroup took 80 us, 45 of them in the scatter.
+constexpr int64_t kMultiPackPairs = 2 * kPairsPerPackBlock;
+
 hipError_t launch_pack(const PackParams &p, hipStream_t s) {
   const int64_t pairs = (int64_t)p.rows * p.topk;
-  if (p.do_pack && pairs <= kSmallPackAlone && (!p.do_plan || p.passes == 1))
+  if (p.do_pack && pairs <= kSmallPackAlone && (!p.do_plan || p.passes == 1)) {
     hipLaunchKernelGGL(pack_small_kernel, dim3(1), dim3(64), 0, s, p);
-  else
+  } else if (p.do_pack && pairs >= kMultiPackPairs && p.gwc) {
+    // (exl3_route_pack has no workspace: it keeps the one-workgroup kernel)
+    if (p.nblk != pack_blocks(pairs) || p.E > kMaxE) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_count_kernel, dim3(p.nblk), dim3(kPackThreads), 0, s, p);
+    hipLaunchKernelGGL(pack_scan_kernel, dim3(1), dim3(kPackThreads), 0, s, p);
+    hipLaunchKernelGGL(pack_scatter_kernel, dim3(p.nblk + 1), dim3(kPackThreads), 0, s, p);
+  } else {
     hipLaunchKernelGGL(pack_plan_kernel, dim3(1), dim3(kPackThreads), 0, s, p);
+  }
   return hipGetLastError();
+}
+
+size_t pack_scratch_ints(int64_t pairs, int E) {
+  if (pairs < kMultiPackPairs) return 0;
+  const int64_t nb = pack_blocks(pairs);
+  return (size_t)(nb * kPackWaves * (int64_t)E + nb);
 }
 
 }  // namespace exl3
