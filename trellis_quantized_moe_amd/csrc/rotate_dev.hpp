@@ -101,6 +101,62 @@ __device__ __forceinline__ void rotate_block(const RotParams &p, int item, int b
   else rotate_block_t<false>(p, item, blk, row, e, i);
 }
 
+// The same unit by 16 lanes of 8 entries each (lane i: entries 8i .. 8i+7):
+// three butterfly levels in registers and four across the 16 lanes. Less
+// work per lane than the quad form, for the latency-bound decode-size launch
+// (pack_rotate_small_kernel). Same arithmetic (exact fp64 sums, one
+// rounding), so the same bits.
+template <bool BF16>
+__device__ __forceinline__ void rotate_block16_t(const RotParams &p, int item, int blk, int row,
+                                                 int e, int i) {
+  const int64_t col = blk * 128 + 8 * i;
+  const u32x4 xv = *(const u32x4 *)(p.x + (int64_t)row * p.H + col);
+#pragma unroll 1
+  for (int pj = 0; pj < p.nproj; ++pj) {
+    const u32x4 sv = *(const u32x4 *)(p.suh[pj] + (int64_t)e * p.H + col);
+    double v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t xw = xv[j], sw = sv[j];
+      const float x0 = BF16 ? bf16_bits_to_f32((uint16_t)(xw & 0xFFFFu))
+                            : f16_bits_to_f32((uint16_t)(xw & 0xFFFFu));
+      const float x1 = BF16 ? bf16_bits_to_f32((uint16_t)(xw >> 16))
+                            : f16_bits_to_f32((uint16_t)(xw >> 16));
+      v[2 * j] = (double)(x0 * f16_bits_to_f32((uint16_t)(sw & 0xFFFFu)));
+      v[2 * j + 1] = (double)(x1 * f16_bits_to_f32((uint16_t)(sw >> 16)));
+    }
+#pragma unroll
+    for (int d = 1; d < 8; d <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if ((j & d) == 0) {
+          const double lo = v[j], hi = v[j + d];
+          v[j] = lo + hi;
+          v[j + d] = lo - hi;
+        }
+      }
+    }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const double s = (i & d) ? -1.0 : 1.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = fma(v[j], s, __shfl_xor(v[j], d, 64));
+    }
+    uint16_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = f64_to_f16_bits(v[j] * kRsqrt128d);
+    *(u32x4 *)(p.xt + ((int64_t)item * p.nproj + pj) * p.H + col) =
+        (u32x4){(uint32_t)h[0] | ((uint32_t)h[4] << 16), (uint32_t)h[1] | ((uint32_t)h[5] << 16),
+                (uint32_t)h[2] | ((uint32_t)h[6] << 16), (uint32_t)h[3] | ((uint32_t)h[7] << 16)};
+  }
+}
+
+__device__ __forceinline__ void rotate_block16(const RotParams &p, int item, int blk, int row,
+                                               int e, int i) {
+  if (p.x_bf16) rotate_block16_t<true>(p, item, blk, row, e, i);
+  else rotate_block16_t<false>(p, item, blk, row, e, i);
+}
+
 // Unit gid = item * (H / 128) + block: the row and expert of the item come
 // from the pack (MoE) or are the item itself (linear).
 __device__ __forceinline__ void rotate_unit(const RotParams &p, int64_t gid, int i) {

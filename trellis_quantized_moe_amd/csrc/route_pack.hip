@@ -714,13 +714,12 @@ __device__ void pack_small(const PackParams &p, bool zero) {
 __global__ void __launch_bounds__(64) pack_small_kernel(PackParams p) { pack_small(p, true); }
 
 // Pack, plan and the rotation of the one pass in a single launch (at most
-// kSmallPairs pairs): block 0 packs, plans and clears the counts; in every
-// other block each 16-lane group takes one pair and up to four of its
-// 128-blocks (one per lane quad), finding the pair's position itself:
-// pos(q) = #{kept pairs of a lower expert} + #{earlier pairs of the same
-// expert}, counted over the route IDs (loaded into LDS once per block). That
-// is the stable pack's position by definition, so no block waits for
-// another.
+// kSmallPairs pairs): block 0 packs, plans and clears the counts; every other
+// block rotates 16 (pair, 128-block) units, one per 16-lane group, finding
+// each pair's position itself: pos(q) = #{kept pairs of a lower expert} +
+// #{earlier pairs of the same expert}, counted over the route IDs (loaded
+// into LDS once per block). That is the stable pack's position by
+// definition, so no block waits for another.
 __global__ void __launch_bounds__(256) pack_rotate_small_kernel(PackParams p, RotParams rp) {
   if (blockIdx.x == 0) {
     // waves 1-3 clear the counts of the launches that follow while wave 0
@@ -735,9 +734,9 @@ __global__ void __launch_bounds__(256) pack_rotate_small_kernel(PackParams p, Ro
   for (int q = threadIdx.x; q < pairs; q += blockDim.x)
     s_ids[q] = load_expert(p.ids, p.ids_i64, q, p.E);
   __syncthreads();
-  const int nblk = rp.H >> 7, nb4 = (nblk + 3) >> 2;
+  const int nblk = rp.H >> 7;
   const int gid = (blockIdx.x - 1) * 16 + (threadIdx.x >> 4);
-  const int q = gid / nb4, blk = 4 * (gid - q * nb4) + ((threadIdx.x >> 2) & 3);
+  const int q = gid / nblk, blk = gid - q * nblk;
   if (q >= pairs) return;  // uniform per group
   const int e = s_ids[q];
   if (e < 0) return;  // dropped pair
@@ -749,7 +748,7 @@ __global__ void __launch_bounds__(256) pack_rotate_small_kernel(PackParams p, Ro
   }
 #pragma unroll
   for (int d = 1; d < 16; d <<= 1) before += __shfl_xor(before, d, 64);
-  if (blk < nblk) rotate_block(rp, before, blk, q / p.topk, e, threadIdx.x & 3);
+  rotate_block16(rp, before, blk, q / p.topk, e, i);
 }
 
 hipError_t launch_pack_rotate(const PackParams &p, const RotParams &rp, hipStream_t s) {
@@ -757,9 +756,9 @@ hipError_t launch_pack_rotate(const PackParams &p, const RotParams &rp, hipStrea
   if (!p.do_pack || !p.do_plan || p.passes != 1 || pairs > kSmallPairs || rp.nproj < 1 ||
       rp.nproj > 2 || rp.pass_base != 0 || rp.nitems < pairs)
     return hipErrorInvalidValue;
-  const int64_t groups = pairs * (((rp.H >> 7) + 3) >> 2);  // (pair, 4 blocks)
-  hipLaunchKernelGGL(pack_rotate_small_kernel, dim3((unsigned)(1 + (groups + 15) / 16)),
-                     dim3(256), 0, s, p, rp);
+  const int64_t units = pairs * (rp.H >> 7);
+  hipLaunchKernelGGL(pack_rotate_small_kernel, dim3((unsigned)(1 + (units + 15) / 16)), dim3(256),
+                     0, s, p, rp);
   return hipGetLastError();
 }
 
