@@ -353,8 +353,8 @@ def _cpu_samples(synth):
     """(name, key, tokens, work items) of each sampled workload."""
     out = []
     # (workload, its rows, the sampled rows); decode: the 32-row layer
-    for name, nrows, rows in (("prefill", 3072, range(8)), ("decode", 32, range(2)),
-                              ("additive", 128, range(2))):
+    for name, nrows, rows in (("prefill", 3072, range(16)), ("decode", 32, range(4)),
+                              ("additive", 128, range(4))):
         wl = synth.moe_workload(name, rows=nrows, materialize=False)
         pairs = [(r, j, int(wl.ids[r, j])) for r in rows for j in range(wl.topk)
                  if 0 <= int(wl.ids[r, j]) < wl.num_experts]
@@ -363,18 +363,32 @@ def _cpu_samples(synth):
     return out
 
 
-def cpu_baseline(synth):
-    """The oracle over the host's cores (see above, at most 16 workers) on
-    bounded samples: 8 prefill rows (64 pairs), 2 rows of the 32-row decode
-    layer, 2 additive rows, 64 rows of the 4096 -> 4096 K = 4 linear. Returns
-    the prefill figure (the headline workload) with the others under
-    'per_workload'."""
+def cpu_pool():
+    """The worker pool of the CPU baseline, started (and its workers warmed
+    up) before this process touches the GPU: its workers are new
+    interpreters, and a process that has initialised the GPU starts no new
+    program. Returns (pool, warm-up future list, worker count)."""
     import multiprocessing
-    import platform
     from concurrent.futures import ProcessPoolExecutor
 
-    samples = _cpu_samples(synth)
+    from trellis_quantized_moe_amd import synth
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    keys = [k for _, k, _, _ in _cpu_samples(synth)]
+    ex = ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("spawn"))
+    warm = [ex.submit(_cpu_warm, keys) for _ in range(workers)]
+    return ex, warm, workers
+
+
+def cpu_baseline(synth, pool):
+    """The oracle over the host's cores (see above, at most 16 workers) on
+    bounded samples: 16 prefill rows (128 pairs), 4 rows of the 32-row decode
+    layer, 4 additive rows, 64 rows of the 4096 -> 4096 K = 4 linear. Returns
+    the prefill figure (the headline workload) with the others under
+    'per_workload'. pool: cpu_pool()."""
+    import platform
+
+    ex, warm, workers = pool
+    samples = _cpu_samples(synth)
     model = platform.processor() or "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -385,9 +399,8 @@ def cpu_baseline(synth):
     except OSError:
         pass
     res = {}
-    ctx = multiprocessing.get_context("spawn")
-    with ProcessPoolExecutor(workers, mp_context=ctx) as ex:
-        blas = list(ex.map(_cpu_warm, [[k for _, k, _, _ in samples]] * workers))[0]
+    with ex:
+        blas = [f.result() for f in warm][0]
         for name, key, tokens, items in samples:
             if key[0] == "moe":
                 items = sorted(items, key=lambda t: (t[2], t[0], t[1]))
@@ -402,7 +415,7 @@ def cpu_baseline(synth):
                              tokens, len(items), "pairs" if key[0] == "moe" else "rows", n)}
     head = res["prefill"]
     return {"value": head["value"], "unit": "tokens/s", "cores": head["cores"], "kind": "oracle",
-            "sample": "prefill workload, rows 0-7 with all their routed pairs (%s) through the "
+            "sample": "prefill workload, rows 0-15 with all their routed pairs (%s) through the "
                       "float64 oracle, expert dequantisation included; %.1f s wall"
                       % (head["sample"], head["wall_s"]),
             "host": {"cpu": model, "threads_available": len(os.sched_getaffinity(0)),
@@ -459,6 +472,9 @@ def main():
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus %d refused)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    # the CPU baseline's workers start now, before the GPU is touched
+    pool = cpu_pool() if not (args.no_cpu or args.only or args.copy_probe) else None
 
     import torch
 
@@ -524,7 +540,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         _log("cpu baseline (oracle)")
-        cpu = cpu_baseline(synth)
+        cpu = cpu_baseline(synth, pool)
 
     line = {
         "metric": METRIC, "value": pre["tokens_per_s"], "unit": "tokens/s",
