@@ -373,6 +373,21 @@ def test_decode_workload_sampled(M):
     assert _sampled_parity(wl, sorted(rows), M * 8) <= TOL
 
 
+def test_decode_rows_same_bytes_in_both_wait_modes():
+    """Each decode row alone (every work item of the single-pass launch
+    resident at once: down items wait per a~ block inside their chains) and
+    inside an 8-row batch (the launch runs in waves: down items wait for
+    their whole tile first) gives the same bytes."""
+    _say("decode rows alone vs in an 8-row batch")
+    wl = synth.moe_workload("decode", rows=8)
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    full = moe_forward(x, ids, w, gate, up, down, 8 * 8, torch.float32)
+    for r in range(8):
+        one = moe_forward(x[r:r + 1], ids[r:r + 1], w[r:r + 1], gate, up, down, 8,
+                          torch.float32)
+        assert torch.equal(one.view(torch.int32), full[r:r + 1].view(torch.int32)), r
+
+
 def test_additive_workload_sampled():
     """The additive layer (base K=3 + residual K=2, 30% zero residual
     scales, half of those with a null trellis). Rows by rule: for each of

@@ -18,6 +18,8 @@
 //                 stages with s_t == 0 skipped
 //   epilogue    = fixed-order fp32 FWHT per 128-block, then per-element
 //                 scalings, identical code for every tile shape.
+
+#include <atomic>
 #include <algorithm>
 #include <utility>
 
@@ -66,6 +68,15 @@ struct StreamGeom {
   static constexpr uint64_t kMask1 = (kLanes1 >= 64) ? ~0ull : ((1ull << kLanes1) - 1);
 };
 
+// Every asm block below that reads an SGPR operand (a base address) in a
+// vector memory instruction first spends five wait states (its own SALU
+// instructions plus s_nop): the compiler may write that SGPR with a VALU
+// instruction (v_readfirstlane, or v_readlane reloading a spilled SGPR) just
+// before the block, CDNA requires five wait states between such a write and
+// a vector memory read of the SGPR, and the compiler's hazard check does not
+// look inside inline asm. Without them the load can use the register's
+// previous contents as its address.
+
 // 16-byte-per-lane global->LDS copy (lanes in `lanes`): lane L reads
 // sbase + voff and writes LDS byte m0 + 16 L.
 __device__ __forceinline__ void sdma16(uint32_t voff, const void *sbase, uint32_t lds_base,
@@ -75,7 +86,7 @@ __device__ __forceinline__ void sdma16(uint32_t voff, const void *sbase, uint32_
       "s_mov_b64 %0, exec\n\t"
       "s_and_b64 exec, exec, %4\n\t"
       "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
+      "s_nop 1\n\t"
       "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b64 exec, %0"
       : "=&s"(saved)
@@ -103,6 +114,7 @@ __device__ __forceinline__ void aload_block(u32x4 &a0, u32x4 &a1, u32x4 &a2, u32
     asm volatile(
         "s_mov_b64 %4, exec\n\t"
         "s_and_b64 exec, exec, %7\n\t"
+        "s_nop 2\n\t"
         "global_load_dwordx4 %0, %5, %6 offset:0 sc1\n\t"
         "global_load_dwordx4 %1, %5, %6 offset:64 sc1\n\t"
         "global_load_dwordx4 %2, %5, %6 offset:128 sc1\n\t"
@@ -115,6 +127,7 @@ __device__ __forceinline__ void aload_block(u32x4 &a0, u32x4 &a1, u32x4 &a2, u32
     asm volatile(
         "s_mov_b64 %4, exec\n\t"
         "s_and_b64 exec, exec, %7\n\t"
+        "s_nop 2\n\t"
         "global_load_dwordx4 %0, %5, %6 offset:0\n\t"
         "global_load_dwordx4 %1, %5, %6 offset:64\n\t"
         "global_load_dwordx4 %2, %5, %6 offset:128\n\t"
@@ -134,6 +147,27 @@ __device__ __forceinline__ void a_wait(u32x4 &a0, u32x4 &a1, u32x4 &a2, u32x4 &a
   asm volatile("s_waitcnt vmcnt(%4)" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3) : "n"(N) : "memory");
 }
 
+// One device-coherent dword load (sc1), invisible to the compiler's wait
+// counting like aload_block: a readiness count another workgroup of the same
+// launch writes. Every lane loads the same (uniform) address.
+__device__ __forceinline__ void flag_load(uint32_t &v, const char *sbase) {
+  asm volatile("s_nop 4\n\tglobal_load_dword %0, %1, %2 sc1"
+               : "=&v"(v)
+               : "v"(0u), "s"(sbase)
+               : "memory");
+}
+
+// a_wait that also holds the block's readiness count.
+template <int N>
+__device__ __forceinline__ void a_wait_f(u32x4 &a0, u32x4 &a1, u32x4 &a2, u32x4 &a3,
+                                         uint32_t &f) {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%5)"
+               : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(f)
+               : "n"(N)
+               : "memory");
+}
+
 __device__ __forceinline__ const char *sgpr_ptr(const void *ptr) {
   const uint64_t b = (uint64_t)(uintptr_t)ptr;
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
@@ -141,15 +175,45 @@ __device__ __forceinline__ const char *sgpr_ptr(const void *ptr) {
   return (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Wait until the n counts in `flags` are set: lane j of the wave reads
+// count j (64 at a time, one load for all of them) and the wave votes;
+// bounded, a give-up counted in ctrl[2].
+__device__ __forceinline__ void wait_all_set(const int32_t *flags, int n, int32_t *ctrl) {
+  const int lane = threadIdx.x & 63;
+  int spins = 0;
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    const int j = j0 + lane;
+    for (;;) {
+      const int v =
+          j < n ? __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
+      if (__all(v >= 1)) break;
+      if (++spins > (1 << 22)) {
+        if (lane == 0) atomicAdd(ctrl + 2, 1);
+        return;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+}
+
 // P = MFMA chain of one stage over all inputs for this wave's strip.
 constexpr int kNADist = kNRing - 2;  // A blocks in flight ahead of the one in use
 
-template <int K, bool COH>
+// WA (the single-pass launch's down items): A block b is the a~ block b of
+// the tile, written by a gate/up item of the same launch, and is read only
+// once aflags[b] is set. The count of block b + kNADist is loaded together
+// with A[b] (kNADist blocks before its A is issued) and checked when A[b]
+// has arrived, so the chain starts as soon as its first blocks are ready
+// and meets the later ones as they come.
+template <int K, bool COH, bool WA>
 struct StreamChain {
   using G = StreamGeom<K>;
   static constexpr int ND = HalfGeom<K>::kLoadDw, NN = HalfGeom<K>::kNormDw;
   static constexpr int TD = Geom<K>::kTileDw;
-  static constexpr int kIssue = 4 + G::kDma;  // loads per block: A, then T
+  static constexpr int kF = WA ? 1 : 0;          // readiness loads per block
+  static constexpr int kIssue = kF + 4 + G::kDma;  // loads per block: flag, A, then T
+  // outstanding loads issued after A[b] when A[b] is needed
+  static constexpr int kAWait = G::kDma + (kNADist - 1) * kIssue;
   static_assert(kNADist + 1 == kNRing - 1, "the A lead equals the trellis lead");
 
   const char *strip;  // uniform: the strip's trellis
@@ -163,15 +227,36 @@ struct StreamChain {
   uint32_t shift, mask;
   int nblk;
   u32x4 a[kNADist + 1][4];  // A of blocks b .. b + kNADist (ring by b % (kNADist + 1))
+  const int32_t *aflags;    // WA: readiness counts of the tile's A blocks
+  int32_t *ctrl;            // WA: [2] counts a wait that gave up
+  uint32_t fl[kNADist + 1]; // WA: count of A block b + kNADist, with A[b]
 
   __device__ __forceinline__ void load_a(int ba, int aslot) {
     const char *src = sgpr_ptr(abase + (size_t)ba * 256);
     aload_block<COH>(a[aslot][0], a[aslot][1], a[aslot][2], a[aslot][3], avoff, src, alanes);
   }
+  __device__ __forceinline__ void load_flag(int bf, int fslot) {
+    if constexpr (WA) flag_load(fl[fslot], sgpr_ptr(aflags + bf));
+  }
   __device__ __forceinline__ void issue(int b, int aslot) {
     const int last = nblk - 1;
+    load_flag(min(b + 2 * kNADist, last), aslot);
     load_a(min(b + kNADist, last), aslot);
     issue_t(min(b + kNRing - 1, last));
+  }
+  // WA: spin until A block ba is ready (all loads drained first, so the
+  // exact counts of later waits still hold); bounded, a give-up counted.
+  __device__ __forceinline__ void wait_ready(int ba) {
+    swait_vmcnt<0>();
+    int spins = 0;
+    while (__builtin_amdgcn_readfirstlane(
+               (int)__hip_atomic_load(aflags + ba, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < 1) {
+      if (++spins > (1 << 22)) {
+        if ((threadIdx.x & 63) == 0) atomicAdd(ctrl + 2, 1);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
   }
   __device__ __forceinline__ void issue_t(int bt) {
     const char *src = sgpr_ptr(strip + (size_t)bt * G::kBlk);
@@ -197,11 +282,18 @@ struct StreamChain {
     }
   }
 
-  // Block b: wait for A[b] (issued kNADist blocks earlier, first in its
-  // group; T[b] was issued before it), issue A[b + 4] and T[b + 5], compute.
+  // Block b: wait for A[b] (issued kNADist blocks earlier after its group's
+  // readiness load; T[b] was issued before it), check that the next A block
+  // is ready (WA), issue A[b + kNADist] and T[b + kNRing - 1], compute.
   template <int AS>
   __device__ __forceinline__ void block(int b, f32x4 &acc) {
-    a_wait<kNADist * kIssue - 4>(a[AS][0], a[AS][1], a[AS][2], a[AS][3]);
+    if constexpr (WA) {
+      a_wait_f<kAWait>(a[AS][0], a[AS][1], a[AS][2], a[AS][3], fl[AS]);
+      const int nb = min(b + kNADist, nblk - 1);
+      if (__builtin_amdgcn_readfirstlane((int)fl[AS]) < 1) wait_ready(nb);
+    } else {
+      a_wait<kAWait>(a[AS][0], a[AS][1], a[AS][2], a[AS][3]);
+    }
     issue(b, (AS + kNADist) % (kNADist + 1));
     compute(b, AS, acc);
   }
@@ -214,27 +306,51 @@ struct StreamChain {
 
   __device__ __forceinline__ f32x4 run() {
     const int last = nblk - 1;
-    // prologue in steady-state order: T[0], then A[j] T[j + 1] for j = 0..3
+    if constexpr (WA) {  // the first blocks' A must be ready before it is loaded
+      swait_vmcnt<0>();
+      wait_all_set(aflags, min(kNADist, nblk), ctrl);
+    }
+    // prologue in steady-state order: T[0], then (count of A[j + kNADist])
+    // A[j] T[j + 1] for j = 0 .. kNADist - 1
     issue_t(0);
 #pragma unroll
     for (int j = 0; j < kNADist; ++j) {
+      load_flag(min(j + kNADist, last), j);
       load_a(min(j, last), j);
       issue_t(min(j + 1, last));
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int b = 0; b < nblk; b += kNADist + 1)
       blocks(b, acc, std::make_integer_sequence<int, kNADist + 1>{});
-    swait_vmcnt<0>();  // no DMA may land after the ring is reused
+    // no DMA may land after the ring is reused, and no load after its
+    // register is given to something else
+    static_assert(kNADist == 2, "the drain below names every A and count register");
+    if constexpr (WA)
+      asm volatile("s_waitcnt vmcnt(0)"
+                   : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[0][2]), "+v"(a[0][3]), "+v"(a[1][0]),
+                     "+v"(a[1][1]), "+v"(a[1][2]), "+v"(a[1][3]), "+v"(a[2][0]), "+v"(a[2][1]),
+                     "+v"(a[2][2]), "+v"(a[2][3]), "+v"(fl[0]), "+v"(fl[1]), "+v"(fl[2])
+                   :
+                   : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)"
+                   : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[0][2]), "+v"(a[0][3]), "+v"(a[1][0]),
+                     "+v"(a[1][1]), "+v"(a[1][2]), "+v"(a[1][3]), "+v"(a[2][0]), "+v"(a[2][1]),
+                     "+v"(a[2][2]), "+v"(a[2][3])
+                   :
+                   : "memory");
     return acc;
   }
 };
 
-template <int K, bool COH>
+template <int K, bool COH, bool WA>
 __device__ __forceinline__ f32x4 stream_chain(const char *strip, int in_f, const char *ring,
                                               const char *abase, uint32_t avoff, uint64_t alanes,
-                                              int lane) {
-  StreamChain<K, COH> c;
+                                              int lane, const int32_t *aflags, int32_t *ctrl) {
+  StreamChain<K, COH, WA> c;
   c.alanes = alanes;
+  c.aflags = aflags;
+  c.ctrl = ctrl;
   const int g = lane >> 4;
   c.strip = sgpr_ptr(strip);
   c.ring = ring;
@@ -246,17 +362,19 @@ __device__ __forceinline__ f32x4 stream_chain(const char *strip, int in_f, const
   const HalfWindow<K> hw(lane);
   c.shift = hw.shift;
 #pragma unroll
-  for (int j = 0; j < StreamChain<K, COH>::ND; ++j) c.traddr[j] = hw.off[j];
+  for (int j = 0; j < StreamChain<K, COH, WA>::ND; ++j) c.traddr[j] = hw.off[j];
   c.mask = codebook_mask();
   return c.run();
 }
 
 // Stage loop of one projection for one wave: acc = sum fmaf(s_t, P_t, acc).
-template <bool COH>
+// aflags (WA): readiness counts of the tile's A blocks.
+template <bool COH, bool WA = false>
 __device__ __forceinline__ f32x4 stream_strip(const ProjDev &pd, int E, int e, int in_f, int nt,
                                               const char *ring, const char *abase,
                                               uint32_t avoff, uint64_t alanes, int lane,
-                                              int32_t *ctrl, bool report) {
+                                              int32_t *ctrl, bool report,
+                                              const int32_t *aflags = nullptr) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int t = 0; t < pd.num_stages; ++t) {
     const float s = uload_f32(pd.scale + t * E + e);
@@ -270,13 +388,13 @@ __device__ __forceinline__ f32x4 stream_strip(const ProjDev &pd, int E, int e, i
     const char *strip = tens + (size_t)nt * (in_f / 16) * 32 * K;
     f32x4 q;
     switch (K) {
-      case 2: q = stream_chain<2, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
-      case 3: q = stream_chain<3, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
-      case 4: q = stream_chain<4, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
-      case 5: q = stream_chain<5, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
-      case 6: q = stream_chain<6, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
-      case 7: q = stream_chain<7, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
-      default: q = stream_chain<8, COH>(strip, in_f, ring, abase, avoff, alanes, lane); break;
+      case 2: q = stream_chain<2, COH, WA>(strip, in_f, ring, abase, avoff, alanes, lane, aflags, ctrl); break;
+      case 3: q = stream_chain<3, COH, WA>(strip, in_f, ring, abase, avoff, alanes, lane, aflags, ctrl); break;
+      case 4: q = stream_chain<4, COH, WA>(strip, in_f, ring, abase, avoff, alanes, lane, aflags, ctrl); break;
+      case 5: q = stream_chain<5, COH, WA>(strip, in_f, ring, abase, avoff, alanes, lane, aflags, ctrl); break;
+      case 6: q = stream_chain<6, COH, WA>(strip, in_f, ring, abase, avoff, alanes, lane, aflags, ctrl); break;
+      case 7: q = stream_chain<7, COH, WA>(strip, in_f, ring, abase, avoff, alanes, lane, aflags, ctrl); break;
+      default: q = stream_chain<8, COH, WA>(strip, in_f, ring, abase, avoff, alanes, lane, aflags, ctrl); break;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] = fmaf(s, q[r], acc[r]);
@@ -391,11 +509,13 @@ __device__ __forceinline__ void narrow_combine(const GemmParams &p, const Narrow
 // 64-column group `by` (for gate/up, by < out_f / 64 is gate, the rest up).
 // FUSED (every kernel of a single pass in one launch, experts_narrow_kernel):
 //  - gate/up: the last item of a 128-column block writes its a~ block with
-//    device-coherent stores, waits for them, then counts the block in
-//    f.tile_ready[bx];
-//  - down: the item first prefetches its trellis (prefetch_strip), then waits
-//    until every a~ block of its tile is counted and reads a~ with
-//    device-coherent loads; the last item of a 128-column block writes d
+//    device-coherent stores, waits for them, then sets the block's count in
+//    f.blk_ready[bx][blk];
+//  - down: the item first prefetches its trellis (prefetch_strip), then
+//    reads a~ with device-coherent loads: WA, its chain reads each a~ block
+//    once that block's count is set (the chain starts on the first blocks);
+//    otherwise it first waits until every a~ block of its tile is set. The
+//    last item of a 128-column block writes d
 //    with device-coherent stores and counts the block for each row of the
 //    tile in f.row_cnt; the count that completes a row's block (one per kept
 //    pair of the row) makes this item sum the row's d in ascending position
@@ -403,7 +523,8 @@ __device__ __forceinline__ void narrow_combine(const GemmParams &p, const Narrow
 // Every wait is on items of lower id (gate/up before down), which were
 // dispatched earlier on their XCD and never wait themselves, so it ends; it
 // is also bounded, a give-up counted in ctrl[2].
-template <int EPI, bool FUSED>
+
+template <int EPI, bool FUSED, bool WA = false>
 __device__ __forceinline__ void narrow_item(const GemmParams &p, char *smem, int *s_flag, int bx,
                                             int by, const NarrowFusedParams *f) {
   constexpr int NPROJ = (EPI == EPI_GATEUP) ? 2 : 1;
@@ -449,26 +570,17 @@ __device__ __forceinline__ void narrow_item(const GemmParams &p, char *smem, int
     if ((int)threadIdx.x - 128 < nrows) v_wt = p.weight_of_pos[p.pass_base + row0 + threadIdx.x - 128];
   }
 
+  const int32_t *aflags = nullptr;
   if constexpr (FUSED && EPI == EPI_DOWN) {
     prefetch_strip(pd, p.E, e, p.in_f, nt, ring, lane);
-    if (threadIdx.x == 0) {
-      const int need = f->gu.out_f >> 7;  // a~ blocks of the tile
-      int spins = 0;
-      while (__hip_atomic_load(f->tile_ready + bx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-             need) {
-        if (++spins > (1 << 22)) {
-          atomicAdd(p.ctrl + 2, 1);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(8);
-      }
-    }
-    __syncthreads();
+    aflags = f->blk_ready + (int64_t)bx * (p.in_f >> 7);
+    if constexpr (!WA) wait_all_set(aflags, p.in_f >> 7, p.ctrl);
     swait_vmcnt<0>();  // the prefetch copies have landed before the ring is reused
   }
 
-  const f32x4 acc = stream_strip<kCohA>(pd, p.E, e, p.in_f, nt, ring, (const char *)a_tile, avoff,
-                                        alanes, lane, p.ctrl, cg == 0 && w == 0);
+  const f32x4 acc =
+      stream_strip<kCohA, kCohA && WA>(pd, p.E, e, p.in_f, nt, ring, (const char *)a_tile, avoff,
+                                       alanes, lane, p.ctrl, cg == 0 && w == 0, aflags);
 
   // Pre-rotation sums of this work item -> scratch [row][NPROJ][out_f].
   // Hand-off to the last work item of the 128-column block without cache
@@ -540,7 +652,8 @@ __device__ __forceinline__ void narrow_item(const GemmParams &p, char *smem, int
     __syncthreads();                                     // ... and every wave's
     if constexpr (EPI == EPI_GATEUP) {
       if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(f->tile_ready + bx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(f->blk_ready + (int64_t)bx * (p.out_f >> 7) + blk, 1,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       narrow_combine(p, *f, row0, nrows, blk, s_flag + 1, (int *)smem);
     }
@@ -560,6 +673,8 @@ __global__ void __launch_bounds__(256, 4) gemm_narrow_kernel(GemmParams p) {
 // (tile x H/64 groups), each waiting only on gate/up items of its own tile;
 // the combine runs at the end of the down items (see narrow_item). The pack,
 // plan, rotation and the zeroing of every count come before, in stream order.
+// WA: down items wait per a~ block inside their chain (see StreamChain).
+template <bool WA>
 __global__ void __launch_bounds__(256, 4) experts_narrow_kernel(NarrowFusedParams f) {
   __shared__ __attribute__((aligned(16))) char smem[4 * kNRing * kNSlot];
   __shared__ int s_flag[1 + kBM];
@@ -571,15 +686,41 @@ __global__ void __launch_bounds__(256, 4) experts_narrow_kernel(NarrowFusedParam
   }
   id -= f.g1;
   const int per = f.dn.out_f >> 6;
-  narrow_item<EPI_DOWN, true>(f.dn, smem, s_flag, id / per, id % per, &f);
+  narrow_item<EPI_DOWN, true, WA>(f.dn, smem, s_flag, id / per, id % per, &f);
 }
 
+// Work items of experts_narrow_kernel the current device holds at once
+// (cached per device).
+static int64_t narrow_resident_items() {
+  static std::atomic<int64_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int64_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, experts_narrow_kernel<true>, 256, 0) !=
+          hipSuccess)
+    return 0;
+  v = (int64_t)cus * per_cu;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// Per-block waits pay when every work item is resident at once (the down
+// items then sit on CUs while gate/up finishes: starting on the first a~
+// blocks shortens the critical path); with more items the launch runs in
+// waves, down items of early tiles overlap gate/up of later ones anyway and
+// the per-block readiness loads only cost issue slots.
 hipError_t launch_experts_narrow(const NarrowFusedParams &f, hipStream_t s) {
   if (f.tiles <= 0) return hipSuccess;
   const int64_t g1 = (int64_t)f.tiles * 2 * (f.gu.out_f >> 6);
   const int64_t g2 = (int64_t)f.tiles * (f.dn.out_f >> 6);
   if (g1 != f.g1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(experts_narrow_kernel, dim3((unsigned)(g1 + g2)), dim3(256), 0, s, f);
+  if (g1 + g2 <= narrow_resident_items())
+    hipLaunchKernelGGL(experts_narrow_kernel<true>, dim3((unsigned)(g1 + g2)), dim3(256), 0, s, f);
+  else
+    hipLaunchKernelGGL(experts_narrow_kernel<false>, dim3((unsigned)(g1 + g2)), dim3(256), 0, s, f);
   return hipGetLastError();
 }
 

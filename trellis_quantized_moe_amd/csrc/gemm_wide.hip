@@ -94,11 +94,17 @@ static_assert(WideLds<EPI_LINEAR>::kBytes <= 80 * 1024, "two workgroups per CU")
 __device__ __forceinline__ int a_swizzle(int r) { return (r >> 1) & 3; }
 
 // 16-byte-per-lane global->LDS copy: lane L reads sbase + voff and writes
-// LDS byte m0 + 16 L. The wave's LDS destination goes through m0.
+// LDS byte m0 + 16 L. The wave's LDS destination goes through m0. Each of
+// these asm blocks spends five wait states (SALU instructions plus s_nop)
+// before its vector memory instruction: the compiler may write the SGPR
+// operands with a VALU instruction (v_readfirstlane) just before the block,
+// CDNA requires five wait states between such a write and a vector memory
+// read of the SGPR, and the compiler's hazard check does not look inside
+// inline asm.
 __device__ __forceinline__ void dma16(uint32_t voff, const void *sbase, uint32_t lds_base) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
+      "s_nop 3\n\t"
       "global_load_lds_dwordx4 %0, %1"
       :
       : "v"(voff), "s"(sbase), "s"(lds_base)
@@ -110,7 +116,7 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void *sbase, uint32_t
 __device__ __forceinline__ void dma16_coh(uint32_t voff, const void *sbase, uint32_t lds_base) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
+      "s_nop 3\n\t"
       "global_load_lds_dwordx4 %0, %1 sc1"
       :
       : "v"(voff), "s"(sbase), "s"(lds_base)
@@ -133,7 +139,7 @@ __device__ __forceinline__ void dma16_lanes(uint32_t voff, const void *sbase, ui
       "s_mov_b64 %0, exec\n\t"
       "s_and_b64 exec, exec, %4\n\t"
       "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
+      "s_nop 1\n\t"
       "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b64 exec, %0"
       : "=&s"(saved)

@@ -172,11 +172,11 @@ MoeLayout moe_layout(int32_t rows, int32_t topk, int32_t E, int32_t H, int32_t I
   L.yacc = take(4 * (size_t)rows * H);
   // 16-row tiles: per (tile, 128-column block) completion counts; 128-row
   // tiles in one pass: per tile, the finished gate/up items. Fused: gate/up
-  // counts [slots][I/128], down counts [slots][H/128], a~ blocks per tile
-  // [slots], d blocks per output row [rows][H/128], and the pre-rotation sums
-  // of gate/up [C][2I] and of down [C][H] side by side.
+  // counts [slots][I/128], down counts [slots][H/128], finished a~ blocks
+  // [slots][I/128], d blocks per output row [rows][H/128], and the
+  // pre-rotation sums of gate/up [C][2I] and of down [C][H] side by side.
   L.fused = P > 0 && !L.wide && L.passes == 1;
-  L.ncnt_ints = L.fused  ? L.slots * (I / 128 + H / 128 + 1) + rows * (H / 128)
+  L.ncnt_ints = L.fused  ? L.slots * (2 * (I / 128) + H / 128) + rows * (H / 128)
                 : L.pipe ? 0
                 : L.wide ? L.slots
                          : L.slots * (std::max(I, H) / 128);
@@ -391,8 +391,8 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
     f.dn.nacc = nacc + (size_t)L.cap * 2 * I;
     f.gu.ncnt = cnt;
     f.dn.ncnt = cnt + (size_t)slots * (I / 128);
-    f.tile_ready = f.dn.ncnt + (size_t)slots * (H / 128);
-    f.row_cnt = f.tile_ready + slots;
+    f.blk_ready = f.dn.ncnt + (size_t)slots * (H / 128);
+    f.row_cnt = f.blk_ready + (size_t)slots * (I / 128);
     f.pair_of_pos = pair_of_pos;
     f.pos_of_pair = pos_of_pair;
     f.total_valid = total_valid;

@@ -49,7 +49,7 @@ struct GemmParams {
 // their own pre-rotation sums (nacc) and completion counts (ncnt).
 struct NarrowFusedParams {
   GemmParams gu, dn;
-  int32_t *tile_ready;  // [tiles]: a~ blocks finished per tile (zero at launch)
+  int32_t *blk_ready;   // [tiles][I / 128]: a~ block finished (zero at launch)
   int32_t *row_cnt;     // [rows][H / 128]: d blocks finished per output row (zero)
   const int32_t *pair_of_pos, *pos_of_pair, *total_valid;
   int rows, topk, pairs;
