@@ -47,7 +47,7 @@ def test_workspace_sizes():
     assert c == L.exl3_moe_workspace_size(3072, 8, 192, 6144, 2048, 24576)
     assert L.exl3_moe_workspace_size(4, 2, 8, 200, 512, 8) == 0  # not a multiple of 128
     lay = exl3.moe_layout(3072, 8, 192, 6144, 2048, 2048)
-    assert lay.passes == 12 and lay.plan_group == 4
+    assert lay.passes == 12 and lay.plan_group == 6
     offs = [lay.ctrl, lay.meta, lay.expert_of_pos, lay.plan, lay.xt, lay.at, lay.d, lay.yacc]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.total == a
@@ -152,11 +152,13 @@ def test_additive_validates_dtypes_on_the_host(xdt, odt, code):
 
 
 @pytest.mark.parametrize("rows,cap,passes,group", [
-    (3072, 2048, 12, 4), (3072, 10 ** 6, 1, 1), (3072, 12288, 2, 1), (3072, 8192, 3, 1),
-    (3072, 6144, 4, 2), (3072, 4916, 5, 2), (3072, 3511, 7, 2), (3072, 3072, 8, 4)])
+    (3072, 2048, 12, 6), (3072, 10 ** 6, 1, 1), (3072, 12288, 2, 1), (3072, 8192, 3, 2),
+    (3072, 6144, 4, 2), (3072, 4916, 5, 3), (3072, 3511, 7, 4), (3072, 3072, 8, 4),
+    (3072, 1024, 24, 8)])
 def test_pipelined_passes_are_grouped_per_launch_unit(rows, cap, passes, group):
-    # 128-row tiles (rows * topk >= 64 * experts): 4 passes share a launch
-    # unit from 8 passes on, 2 from 4 (one plan, buffers of group * capacity)
+    # 128-row tiles (rows * topk >= 64 * experts), several passes: a launch
+    # unit holds half the passes, rounded up, at most 8 (one plan, buffers
+    # of group * capacity)
     lay = exl3.moe_layout(rows, 8, 192, 6144, 2048, cap)
     assert (lay.passes, lay.plan_group) == (passes, group)
     one = exl3.moe_layout(rows, 8, 192, 6144, 2048, cap if group == 1 else 10 ** 6)

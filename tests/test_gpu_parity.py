@@ -486,11 +486,12 @@ def test_moe_wide_pipelined_edge_cases():
         assert torch.equal(y2.view(torch.int32), y.view(torch.int32)), null
 
 
-@pytest.mark.parametrize("cap,group", [(100, 2), (50, 4), (7, 4)])
+@pytest.mark.parametrize("cap,group", [(100, 3), (50, 6), (7, 8)])
 def test_moe_wide_grouped_passes_additive_equals_forward(cap, group):
-    """128-row tiles over several passes grouped into launch units (2 or 4
-    passes per plan and buffer set): exl3_moe_additive on the route pack
-    equals exl3_moe_forward, and both equal the one-pass result."""
+    """128-row tiles over several passes grouped into launch units (3, 6 or
+    8 passes per plan and buffer set: 6, 12 and 86 passes):
+    exl3_moe_additive on the route pack equals exl3_moe_forward, and both
+    equal the one-pass result."""
     wl = _wide_wl()
     lay = exl3.moe_layout(wl.rows, wl.topk, wl.num_experts, wl.hidden, wl.intermediate, cap)
     assert lay.plan_group == group, (lay.passes, lay.plan_group)
@@ -538,7 +539,7 @@ def test_moe_wide_active_residual_stage():
         assert np.sum(p.scale[1] != 0) >= 3
     gate, up, down, x, ids, w = _moe_inputs(wl)
     one = moe_forward(x, ids, w, gate, up, down, 10 ** 6, torch.float32)
-    for cap, group in ((100, 2), (7, 4)):
+    for cap, group in ((100, 3), (7, 8)):
         lay = exl3.moe_layout(wl.rows, wl.topk, wl.num_experts, wl.hidden, wl.intermediate, cap)
         assert lay.plan_group == group
         _say("wide residual capacity", cap, lay.passes)

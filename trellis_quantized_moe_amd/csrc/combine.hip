@@ -1,11 +1,13 @@
-// Ordered top-k combine kernels (the per-position work is combine_position).
+// Ordered top-k combine kernels (the per-row work of a pass range is
+// combine_row).
 #include "combine_dev.hpp"
 
 namespace exl3 {
 
-// One workgroup of 256 threads per packed position of the pass.
+// One workgroup of 256 threads per row (rows with no pair in the pass range
+// return at once).
 __global__ void __launch_bounds__(256) combine_kernel(CombineParams p) {
-  combine_position(p, blockIdx.x);
+  combine_row(p, blockIdx.x);
 }
 
 // Single pass (every kept position in it): one workgroup of 512 threads per
@@ -78,9 +80,8 @@ __global__ void __launch_bounds__(kRowThreads) combine_rows_kernel(CombineParams
 }
 
 hipError_t launch_combine(const CombineParams &p, int npos, hipStream_t s) {
-  if (npos <= 0) return hipSuccess;
-  const dim3 grid(npos);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, p);
+  if (npos <= 0 || p.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3(p.rows), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -599,8 +599,8 @@ hipError_t launch_gemm_wide_pass(const GemmParams &gu, const GemmParams &dn, int
 // left of four passes, instead of idling through one pass's stragglers.
 // Items, in dispatch order (longest first): gate/up (tile x 128-column
 // block, heavy tiles first), down (tile x 256-column block), rotation
-// (64 (position, 128-block) units, one per lane quad), combine (one
-// position).
+// (64 (position, 128-block) units, one per lane quad), combine (one row;
+// rows without a pair in the unit return at once).
 constexpr int kRotUnitsPerItem = 64;
 
 template <bool MULTI>
@@ -628,12 +628,12 @@ __global__ void __launch_bounds__(256, MULTI ? 1 : 2)
     rotate_unit(rn, (int64_t)id * kRotUnitsPerItem + (threadIdx.x >> 2), threadIdx.x & 3);
     return;
   }
-  combine_position(cb, id - g3);
+  combine_row(cb, id - g3);
 }
 
 hipError_t launch_gemm_wide_pipe(const GemmParams &gu, int tiles_gu, const GemmParams &dn,
                                  int tiles_dn, const RotParams &rn, const CombineParams &cb,
-                                 int npos_cb, int nb_gu, int nb_dn, hipStream_t s) {
+                                 int rows_cb, int nb_gu, int nb_dn, hipStream_t s) {
   if (rn.nitems > 0 && (rn.nproj < 1 || rn.nproj > 2)) return hipErrorInvalidValue;
   const bool multi = (tiles_gu > 0 && (gu.proj[0].num_stages > 1 || gu.proj[1].num_stages > 1)) ||
                      (tiles_dn > 0 && dn.proj[0].num_stages > 1);
@@ -641,7 +641,7 @@ hipError_t launch_gemm_wide_pipe(const GemmParams &gu, int tiles_gu, const GemmP
   const int g2 = tiles_dn > 0 ? (tiles_dn + 7) / 8 * 8 * nb_dn : 0;
   const int64_t units = rn.nitems > 0 ? (int64_t)rn.nitems * (rn.H >> 7) : 0;
   const int g3 = (int)((units + kRotUnitsPerItem - 1) / kRotUnitsPerItem);
-  const int g4 = npos_cb > 0 ? npos_cb : 0;
+  const int g4 = rows_cb > 0 ? rows_cb : 0;
   const int64_t total = (int64_t)g1 + g2 + g3 + g4;
   if (total <= 0) return hipSuccess;
   const dim3 grid((unsigned)total);

@@ -115,8 +115,8 @@ struct MoeLayout {
   size_t ctrl, count, offset, pair_of_pos, weight_of_pos, pos_of_pair, num_active, status;
   size_t expert_of_pos, plan, xt, at, d, yacc, nacc, ncnt, pack, total;
   int passes, slots, cap, ncnt_ints;
-  // A launch unit is `group` consecutive passes (on the pipelined path 4
-  // with 8+ passes, 2 with 4-7, else 1): one plan, one buffer set of
+  // A launch unit is `group` consecutive passes (on the pipelined path
+  // about half the passes, at most 8; else 1): one plan, one buffer set of
   // gcap = group * cap rows. Spans are still cut every `cap` pairs.
   int group, units, gcap;
   // fused: a single pass on 16-row tiles runs its GEMMs and combine in one
@@ -151,13 +151,14 @@ MoeLayout moe_layout(int32_t rows, int32_t topk, int32_t E, int32_t H, int32_t I
   L.expert_of_pos = take(4 * (size_t)P);
   L.wide = P > 0 && moe_wide(P, E);
   // 128-row tiles over several passes run pipelined across launches, with
-  // two buffers (by unit parity) of x~, a~ and d. A launch unit holds 4
-  // passes from 8 passes on, 2 from 4: more work per launch to spread over
-  // the CUs and fewer launch tails, for buffers of group * capacity rows
-  // (measured on the 3072-row prefill at capacity 2048: 4.37 / 4.20 / 4.05
-  // ms per layer with 1 / 2 / 4 passes per unit)
+  // two buffers (by unit parity) of x~, a~ and d. A launch unit holds about
+  // half the passes (two units), at most 8: more work per launch to spread
+  // over the CUs and fewer launch tails, for buffers of group * capacity
+  // rows (on the 3072-row prefill at capacity 2048, 12 passes: 4.37 / 4.20
+  // / 4.05 ms per layer with 1 / 2 / 4 passes per unit, and 6 passes per
+  // unit faster again; 1.3 GB of buffers at 6)
   L.pipe = L.wide && L.passes >= 2;
-  L.group = !L.pipe ? 1 : L.passes >= 8 ? 4 : L.passes >= 4 ? 2 : 1;
+  L.group = !L.pipe ? 1 : std::min(8, (L.passes + 1) / 2);
   L.units = (L.passes + L.group - 1) / L.group;
   L.gcap = L.group * L.cap;
   L.plan = take(4 * (size_t)L.units * (1 + 3 * (size_t)L.group * L.slots));
@@ -362,7 +363,7 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
       const CombineParams cp = has_cb ? cb_params(k - 2, k & 1) : CombineParams{};
       ProfScope ps(prof, st, EXL3_K_EXPERTS);
       if (launch_gemm_wide_pipe(g, has_gu ? tiles_of(k) : 0, dn, has_dn ? tiles_of(k - 1) : 0, rn,
-                                cp, has_cb ? npos_of(k - 2) : 0, I / 128, (H + 255) / 256,
+                                cp, has_cb ? rows : 0, I / 128, (H + 255) / 256,
                                 st) != hipSuccess)
         return EXL3_E_LAUNCH;
     }

@@ -132,11 +132,12 @@ hipError_t launch_gemm_wide_pass(const GemmParams &gu, const GemmParams &dn, int
 // Several passes of 128-row routed experts, pipelined across launches: one
 // launch runs gate/up of pass k (gu, tiles_gu), down of pass k - 1 (dn,
 // tiles_dn), the rotation of pass k + 1 (rn) and the combine of pass k - 2
-// (cb, npos_cb positions); an absent part has 0 tiles / items. The caller
+// (cb, one item for each of rows_cb rows); an absent part has 0 tiles /
+// items. The caller
 // gives each pass's x~, a~ and d the buffer of its parity.
 hipError_t launch_gemm_wide_pipe(const GemmParams &gu, int tiles_gu, const GemmParams &dn,
                                  int tiles_dn, const RotParams &rn, const CombineParams &cb,
-                                 int npos_cb, int nb_gu, int nb_dn, hipStream_t s);
+                                 int rows_cb, int nb_gu, int nb_dn, hipStream_t s);
 hipError_t launch_rotate(const RotParams &p, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int npos, hipStream_t s);
 hipError_t launch_combine_rows(const CombineParams &p, hipStream_t s);
