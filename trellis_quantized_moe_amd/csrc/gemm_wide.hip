@@ -79,8 +79,6 @@ struct WideLds {
   static constexpr int kRingBytes = kTOff + kTRing * kTstage;
   static constexpr int kBytes = kTileBytes > kRingBytes ? kTileBytes : kRingBytes;
   static constexpr int kAChunks = NPROJ * 8 / 4;  // 1 KB A chunks per wave per stage
-  static constexpr int kTDma = 2;                 // trellis DMAs per wave per stage
-  static constexpr int kDma = kAChunks + kTDma;
 };
 static_assert(WideLds<EPI_GATEUP>::kBytes <= 80 * 1024, "two workgroups per CU");
 static_assert(WideLds<EPI_LINEAR>::kBytes <= 80 * 1024, "two workgroups per CU");
@@ -183,14 +181,25 @@ struct WideIter {
   static constexpr int U = 2 * MS;     // units per stage, two MFMAs each
   static constexpr int PPU = 16 / U;   // decode pairs per unit
   static constexpr int SEG = 64 * K;   // bytes of a strip's stage
-  static constexpr uint64_t kHalfLanes = (SEG >= 512) ? 0xFFFFFFFFull : ((1ull << (SEG / 16)) - 1);
-  static constexpr uint64_t kSegLanes = kHalfLanes | (kHalfLanes << 32);
+  // A 64-lane trellis copy moves 16 bytes a lane: 16 lanes carry a strip's
+  // stage for K <= 4 (4 strips a copy), 32 lanes otherwise (2 strips); a
+  // strip's LDS slot is as wide as its lanes.
+  static constexpr int LPS = (SEG <= 256) ? 16 : 32;  // lanes per strip
+  static constexpr int SPD = 64 / LPS;                // strips per copy
+  static constexpr int TDMA = 4 / SPD;                // trellis copies per wave and stage
+  static constexpr int DMA = L::kAChunks + TDMA;      // copies per wave and stage
+  static constexpr int TSTR = 16 * LPS;               // LDS bytes of a strip's slot
+  static constexpr uint64_t kStripLanes =
+      (SEG == TSTR) ? ((1ull << LPS) - 1) : ((1ull << (SEG / 16)) - 1);
+  static constexpr uint64_t kSegLanes =
+      (LPS == 32) ? (kStripLanes | (kStripLanes << 32))
+                  : (kStripLanes | (kStripLanes << 16) | (kStripLanes << 32) | (kStripLanes << 48));
 
   const WideArgs &c;
   const char *smem;
   const char *tens;
   uint32_t shift, mask;
-  uint32_t tvoff[2];
+  uint32_t tvoff[TDMA];
   uint32_t traddr[ND];
   uint32_t afrag;
   uint32_t tdst;  // LDS address of this wave's T region (uniform)
@@ -205,10 +214,10 @@ struct WideIter {
                                       int nt0, int ktiles)
       : c(c_), smem(smem_), tens(tens_) {
     const int lane = c.lane, g = lane >> 4, n = lane & 15;
-    const int sl = lane & 31;
+    const int sl = lane % LPS;
 #pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      const int ns = 2 * d + (lane >> 5);
+    for (int d = 0; d < TDMA; ++d) {
+      const int ns = SPD * d + lane / LPS;
       tvoff[d] = (uint32_t)((nt0 + ns) * ktiles * 32 * K + 16 * min(sl, SEG / 16 - 1));
     }
     tdst = uniform_u32(c.lds0 + L::kTOff + c.w * kTwave);
@@ -220,8 +229,8 @@ struct WideIter {
     mask = codebook_mask();
   }
 
-  // DMA d (0 .. kDma-1) of stages (ka, kt) into slots (sa, st): A chunks
-  // first, then the trellis (two strips per DMA).
+  // DMA d (0 .. DMA-1) of stages (ka, kt) into slots (sa, st): A chunks
+  // first, then the trellis (SPD strips per DMA).
   __device__ __forceinline__ void dma(int d, int ka, int kt, int sa, int st) const {
     if (d < L::kAChunks) {
       const char *ab = uniform_ptr(c.abase + (size_t)ka * kArow);
@@ -229,8 +238,8 @@ struct WideIter {
     } else {
       const int td = d - L::kAChunks;
       const char *tb = uniform_ptr(tens + (size_t)kt * 2 * 32 * K);
-      const uint32_t dst = uniform_u32(tdst + st * kTstage + td * 2 * kTstrip);
-      if constexpr (SEG >= 512) dma16(tvoff[td], tb, dst);
+      const uint32_t dst = uniform_u32(tdst + st * kTstage + td * SPD * TSTR);
+      if constexpr (SEG == TSTR) dma16(tvoff[td], tb, dst);
       else dma16_lanes(tvoff[td], tb, dst, kSegLanes);
     }
   }
@@ -241,7 +250,7 @@ struct WideIter {
     for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
       for (int j = 0; j < ND; ++j)
-        raw[ns][j] = *(const uint32_t *)(smem + traddr[j] + off + ns * kTstrip);
+        raw[ns][j] = *(const uint32_t *)(smem + traddr[j] + off + ns * TSTR);
   }
 
   template <int Q>
@@ -272,8 +281,8 @@ struct WideIter {
                                        int kt, int sa_w, int st_w) {
     constexpr int ms = u / 2, ns0 = (u & 1) * 2;
 #pragma unroll
-    for (int d = 0; d < L::kDma; ++d)
-      if ((d * U) / L::kDma == u) dma(d, ka, kt, sa_w, st_w);
+    for (int d = 0; d < DMA; ++d)
+      if ((d * U) / DMA == u) dma(d, ka, kt, sa_w, st_w);
     decode_range<u * PPU, PPU>(bn);
     pacc[ms][ns0] = mfma16x16x32(af[ms], __builtin_bit_cast(f16x8, bc[ns0]), pacc[ms][ns0]);
     pacc[ms][ns0 + 1] =
@@ -291,7 +300,7 @@ struct WideIter {
   __device__ __forceinline__ void iteration(int ks, int sa, const BRegs &bc, BRegs &bn,
                                             f32x4 (&pacc)[8][4]) {
     const int last = c.nks - 1;
-    wait_vmcnt<L::kDma + L::kTDma>();
+    wait_vmcnt<DMA + TDMA>();
     __syncthreads();
     ar = afrag + (uint32_t)(sa * L::kAStage);
     // every A fragment of the stage at once: under load an LDS read takes a
@@ -312,18 +321,18 @@ struct WideIter {
     // prologue, in the order of the steady state: T[0], T[1], A[0] T[2],
     // A[1] T[3]
 #pragma unroll
-    for (int d = L::kAChunks; d < L::kDma; ++d) dma(d, 0, 0, 0, 0);
+    for (int d = L::kAChunks; d < DMA; ++d) dma(d, 0, 0, 0, 0);
 #pragma unroll
-    for (int d = L::kAChunks; d < L::kDma; ++d) dma(d, 0, min(1, last), 0, 1);
+    for (int d = L::kAChunks; d < DMA; ++d) dma(d, 0, min(1, last), 0, 1);
 #pragma unroll
     for (int d = 0; d < L::kAChunks; ++d) dma(d, 0, 0, 0, 0);
 #pragma unroll
-    for (int d = L::kAChunks; d < L::kDma; ++d) dma(d, 0, min(2, last), 0, 2);
+    for (int d = L::kAChunks; d < DMA; ++d) dma(d, 0, min(2, last), 0, 2);
 #pragma unroll
     for (int d = 0; d < L::kAChunks; ++d) dma(d, min(1, last), 0, 1, 0);
 #pragma unroll
-    for (int d = L::kAChunks; d < L::kDma; ++d) dma(d, 0, min(3, last), 0, 3);
-    wait_vmcnt<3 * L::kTDma + 2 * L::kAChunks>();  // T[0] (this wave's own copy)
+    for (int d = L::kAChunks; d < DMA; ++d) dma(d, 0, min(3, last), 0, 3);
+    wait_vmcnt<3 * TDMA + 2 * L::kAChunks>();  // T[0] (this wave's own copy)
     read_raw(0);
     decode_seq(b0, std::make_integer_sequence<int, 16>{});
     int sa = 0;
