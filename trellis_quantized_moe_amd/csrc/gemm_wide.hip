@@ -33,8 +33,9 @@
 //
 // Pipeline over 32-input stages (one MFMA k-step; 2 trellis tiles along k):
 //  - A (rotated activations) is copied global->LDS by DMA into a ring of 3
-//    slots. Each wave copies a quarter and all waves read all of it, so one
-//    barrier per stage publishes it.
+//    slots. Each wave copies its share of the rows the tile's MFMAs read
+//    (AMap) and all waves read all of it, so one barrier per stage
+//    publishes it.
 //  - Trellis words are copied global->LDS by DMA into a ring of 4 slots per
 //    wave. A wave copies and reads only its own strips, so its own vmcnt
 //    wait is enough (no barrier).
@@ -78,7 +79,6 @@ struct WideLds {
   static constexpr int kTOff = kARing * kAStage;
   static constexpr int kRingBytes = kTOff + kTRing * kTstage;
   static constexpr int kBytes = kTileBytes > kRingBytes ? kTileBytes : kRingBytes;
-  static constexpr int kAChunks = NPROJ * 8 / 4;  // 1 KB A chunks per wave per stage
 };
 static_assert(WideLds<EPI_GATEUP>::kBytes <= 80 * 1024, "two workgroups per CU");
 static_assert(WideLds<EPI_LINEAR>::kBytes <= 80 * 1024, "two workgroups per CU");
@@ -145,6 +145,22 @@ __device__ __forceinline__ void dma16_lanes(uint32_t voff, const void *sbase, ui
       : "memory", "scc");
 }
 
+// dma16_lanes with device-coherent loads (sc1).
+__device__ __forceinline__ void dma16_lanes_coh(uint32_t voff, const void *sbase,
+                                                uint32_t lds_base, uint64_t lanes) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_and_b64 exec, exec, %4\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 1\n\t"
+      "global_load_lds_dwordx4 %1, %2 sc1\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_base), "s"(lanes)
+      : "memory", "scc");
+}
+
 __device__ __forceinline__ const char *uniform_ptr(const char *ptr) {
   const uint64_t b = (uint64_t)(uintptr_t)ptr;
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
@@ -165,9 +181,54 @@ __device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
 struct WideArgs {
   int e, row0, nrows, nb, w, pj, lane, nks, colbase;
   const char *abase;     // A rows of the tile (uniform)
-  uint32_t avoff[4];     // per A chunk: lane's byte offset from abase
-  uint32_t adst[4];      // per A chunk: LDS byte offset inside an A slot (uniform)
+  int64_t lda, aps;      // A row stride and projection stride (elements)
   uint32_t lds0;         // LDS address of smem
+};
+
+// The A copies of one wave for a tile of MS row blocks: a stage needs the
+// NPROJ x MS 16-row chunks (1 KB each: 16 rows x 64 B) its MFMAs read, and
+// the 4 waves share them evenly, so every wave issues AD copies a stage (a
+// constant per MS, which keeps each vmcnt wait exact); one projection at
+// MS = 2 is copied as 8-row halves, one per wave. Chunk f covers rows
+// 16 (f % MS) .. +15 of projection f / MS; lane L copies row 16 rg + L / 4
+// (+ 8 for the second half), LDS slot L % 4 holding the global 16-byte
+// chunk (L % 4) ^ a_swizzle(row & 15). Rows past the tile's end re-read its
+// last row (never stored).
+template <int EPI, int MS, bool COH>
+struct AMap {
+  using L = WideLds<EPI>;
+  static constexpr int TC = L::NPROJ * MS;       // 16-row chunks a stage needs
+  static constexpr bool kHalf = TC < 4;          // 8-row halves
+  static constexpr int AD = kHalf ? 1 : TC / 4;  // copies per wave and stage
+  static_assert(kHalf ? TC * 2 == 4 : TC % 4 == 0, "the waves share the chunks evenly");
+  uint32_t voff[AD];  // lane's byte offset from the stage's A rows
+  uint32_t dst[AD];   // LDS byte offset inside an A slot (uniform)
+
+  __device__ __forceinline__ explicit AMap(const WideArgs &c) {
+    const int lane = c.lane;
+#pragma unroll
+    for (int d = 0; d < AD; ++d) {
+      const int f = kHalf ? (c.w >> 1) : c.w * AD + d;
+      const int half = kHalf ? (c.w & 1) : 0;
+      const int q = f / MS, rg = f % MS;
+      const int r = 16 * rg + 8 * half + ((kHalf ? (lane & 31) : lane) >> 2);
+      const int rs = min(r, c.nrows - 1);
+      const int gc = (lane & 3) ^ a_swizzle(r & 15);
+      voff[d] = (uint32_t)(2 * ((int64_t)rs * c.lda + q * c.aps + gc * 8));
+      dst[d] = uniform_u32((uint32_t)(L::kAOff + q * kAbuf + rg * 1024 + half * 512));
+    }
+  }
+  // copy d of stage ka into A slot sa
+  __device__ __forceinline__ void copy(const WideArgs &c, int d, int ka, int sa) const {
+    const char *ab = uniform_ptr(c.abase + (size_t)ka * kArow);
+    const uint32_t to = uniform_u32(c.lds0 + dst[d] + sa * L::kAStage);
+    if constexpr (kHalf) {
+      if constexpr (COH) dma16_lanes_coh(voff[d], ab, to, 0xFFFFFFFFull);
+      else dma16_lanes(voff[d], ab, to, 0xFFFFFFFFull);
+    } else {
+      dma16_a<COH>(voff[d], ab, to);
+    }
+  }
 };
 
 // Decoded B registers of one stage: one MFMA B operand per strip.
@@ -187,7 +248,9 @@ struct WideIter {
   static constexpr int LPS = (SEG <= 256) ? 16 : 32;  // lanes per strip
   static constexpr int SPD = 64 / LPS;                // strips per copy
   static constexpr int TDMA = 4 / SPD;                // trellis copies per wave and stage
-  static constexpr int DMA = L::kAChunks + TDMA;      // copies per wave and stage
+  using AM = AMap<EPI, MS, COH>;
+  static constexpr int AD = AM::AD;                   // A copies per wave and stage
+  static constexpr int DMA = AD + TDMA;               // copies per wave and stage
   static constexpr int TSTR = 16 * LPS;               // LDS bytes of a strip's slot
   static constexpr uint64_t kStripLanes =
       (SEG == TSTR) ? ((1ull << LPS) - 1) : ((1ull << (SEG / 16)) - 1);
@@ -196,6 +259,7 @@ struct WideIter {
                   : (kStripLanes | (kStripLanes << 16) | (kStripLanes << 32) | (kStripLanes << 48));
 
   const WideArgs &c;
+  const AM am;
   const char *smem;
   const char *tens;
   uint32_t shift, mask;
@@ -212,7 +276,7 @@ struct WideIter {
 
   __device__ __forceinline__ WideIter(const WideArgs &c_, const char *smem_, const char *tens_,
                                       int nt0, int ktiles)
-      : c(c_), smem(smem_), tens(tens_) {
+      : c(c_), am(c_), smem(smem_), tens(tens_) {
     const int lane = c.lane, g = lane >> 4, n = lane & 15;
     const int sl = lane % LPS;
 #pragma unroll
@@ -232,11 +296,10 @@ struct WideIter {
   // DMA d (0 .. DMA-1) of stages (ka, kt) into slots (sa, st): A chunks
   // first, then the trellis (SPD strips per DMA).
   __device__ __forceinline__ void dma(int d, int ka, int kt, int sa, int st) const {
-    if (d < L::kAChunks) {
-      const char *ab = uniform_ptr(c.abase + (size_t)ka * kArow);
-      dma16_a<COH>(c.avoff[d], ab, uniform_u32(c.lds0 + c.adst[d] + sa * L::kAStage));
+    if (d < AD) {
+      am.copy(c, d, ka, sa);
     } else {
-      const int td = d - L::kAChunks;
+      const int td = d - AD;
       const char *tb = uniform_ptr(tens + (size_t)kt * 2 * 32 * K);
       const uint32_t dst = uniform_u32(tdst + st * kTstage + td * SPD * TSTR);
       if constexpr (SEG == TSTR) dma16(tvoff[td], tb, dst);
@@ -321,18 +384,18 @@ struct WideIter {
     // prologue, in the order of the steady state: T[0], T[1], A[0] T[2],
     // A[1] T[3]
 #pragma unroll
-    for (int d = L::kAChunks; d < DMA; ++d) dma(d, 0, 0, 0, 0);
+    for (int d = AD; d < DMA; ++d) dma(d, 0, 0, 0, 0);
 #pragma unroll
-    for (int d = L::kAChunks; d < DMA; ++d) dma(d, 0, min(1, last), 0, 1);
+    for (int d = AD; d < DMA; ++d) dma(d, 0, min(1, last), 0, 1);
 #pragma unroll
-    for (int d = 0; d < L::kAChunks; ++d) dma(d, 0, 0, 0, 0);
+    for (int d = 0; d < AD; ++d) dma(d, 0, 0, 0, 0);
 #pragma unroll
-    for (int d = L::kAChunks; d < DMA; ++d) dma(d, 0, min(2, last), 0, 2);
+    for (int d = AD; d < DMA; ++d) dma(d, 0, min(2, last), 0, 2);
 #pragma unroll
-    for (int d = 0; d < L::kAChunks; ++d) dma(d, min(1, last), 0, 1, 0);
+    for (int d = 0; d < AD; ++d) dma(d, min(1, last), 0, 1, 0);
 #pragma unroll
-    for (int d = L::kAChunks; d < DMA; ++d) dma(d, 0, min(3, last), 0, 3);
-    wait_vmcnt<3 * TDMA + 2 * L::kAChunks>();  // T[0] (this wave's own copy)
+    for (int d = AD; d < DMA; ++d) dma(d, 0, min(3, last), 0, 3);
+    wait_vmcnt<3 * TDMA + 2 * AD>();  // T[0] (this wave's own copy)
     read_raw(0);
     decode_seq(b0, std::make_integer_sequence<int, 16>{});
     int sa = 0;
@@ -348,27 +411,33 @@ struct WideIter {
 
 // A wave with no work for this stage still copies its share of A and takes
 // part in the barrier cadence of its workgroup (1 + nks barriers).
-template <int EPI, bool COH>
+template <int EPI, bool COH, int MS>
 __device__ __forceinline__ void wide_idle_stage(const WideArgs &c) {
-  using L = WideLds<EPI>;
+  using AM = AMap<EPI, MS, COH>;
+  const AM am(c);
   const int nks = c.nks, last = nks - 1;
   auto issue = [&](int ka, int sa) {
-    const char *ab = uniform_ptr(c.abase + (size_t)ka * kArow);
 #pragma unroll
-    for (int ch = 0; ch < L::kAChunks; ++ch)
-      dma16_a<COH>(c.avoff[ch], ab, uniform_u32(c.lds0 + c.adst[ch] + sa * L::kAStage));
+    for (int d = 0; d < AM::AD; ++d) am.copy(c, d, ka, sa);
   };
   __syncthreads();
   issue(0, 0);
   issue(min(1, last), 1);
   int sa = 0;
   for (int ks = 0; ks < nks; ++ks) {
-    wait_vmcnt<L::kAChunks>();
+    wait_vmcnt<AM::AD>();
     __syncthreads();
     issue(min(ks + 2, last), (sa == 0) ? 2 : sa - 1);
     sa = (sa == 2) ? 0 : sa + 1;
   }
   wait_vmcnt<0>();
+}
+
+template <int EPI, bool COH>
+__device__ __forceinline__ void wide_idle_rows(const WideArgs &c, int msub) {
+  if (msub <= 2) wide_idle_stage<EPI, COH, 2>(c);
+  else if (msub <= 4) wide_idle_stage<EPI, COH, 4>(c);
+  else wide_idle_stage<EPI, COH, 8>(c);
 }
 
 template <int EPI, int K, bool COH>
@@ -414,21 +483,10 @@ __device__ __forceinline__ bool wide_item(const GemmParams &p, char *smem, int b
   const int ktiles = p.in_f >> 4;
   const int msub = (c.nrows + 15) >> 4;
 
-  // A chunk ch of this wave: 16 rows x 64 B of one stage; lane L -> row
-  // 16 rg + L/4, LDS slot L%4 holding the global 16-byte chunk
-  // (L%4) ^ a_swizzle(row & 15). Rows past the tile's end re-read its last
-  // row (never stored).
+  // the A rows of the tile (the copies per stage: AMap)
   c.abase = (const char *)(p.A + (int64_t)c.row0 * p.lda);
-#pragma unroll
-  for (int ch = 0; ch < L::kAChunks; ++ch) {
-    const int f = w * L::kAChunks + ch;
-    const int q = f >> 3, rg = f & 7;
-    const int r = 16 * rg + (lane >> 2);
-    const int rs = min(r, c.nrows - 1);
-    const int gc = (lane & 3) ^ a_swizzle(r & 15);
-    c.avoff[ch] = (uint32_t)(2 * ((int64_t)rs * p.lda + q * p.a_proj_stride + gc * 8));
-    c.adst[ch] = uniform_u32((uint32_t)(L::kAOff + q * kAbuf + rg * 1024));
-  }
+  c.lda = p.lda;
+  c.aps = p.a_proj_stride;
 
   f32x4 acc[MULTI ? 8 : 1][4];
   f32x4 pacc[8][4];
@@ -458,7 +516,7 @@ __device__ __forceinline__ bool wide_item(const GemmParams &p, char *smem, int b
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns) pacc[ms][ns] = (f32x4){0.f, 0.f, 0.f, 0.f};
     if (!active) {
-      wide_idle_stage<EPI, kCohLoad>(c);
+      wide_idle_rows<EPI, kCohLoad>(c, msub);
     } else {
       switch (K) {
         case 2: wide_stage_rows<EPI, 2, kCohLoad>(c, smem, tens, nt0, ktiles, msub, pacc); break;
