@@ -3,10 +3,9 @@
 // pass while later passes compute).
 // y_r = sum of the row's weighted per-pair outputs d, added in fp32 in
 // ascending packed position (expert, then pair index), pass after pass.
-// TensorFold PR #837 (What this changes: the weighted combine; an expert's
-// how many rows an expert serves must not alter any row's result) — the
-// fixed order makes the row's
-// bytes independent of other rows, capacity and chunking.
+// TensorFold PR #837 (What this changes: the weighted combine; how many rows
+// an expert serves must not alter any row's result) — the fixed order makes
+// the row's bytes independent of other rows, capacity and chunking.
 #pragma once
 
 #include "common.hpp"
