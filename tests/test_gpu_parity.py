@@ -635,6 +635,27 @@ def test_linear_bf16_out_of_fp16_range():
     _check_range_rows(got, ref, [1])
 
 
+def test_linear_fp16_subnormal_inputs():
+    """fp16 x holding subnormal values is read exactly: the rotation widens
+    each fp16 input inside its product with the sign, and a flushed
+    subnormal would zero rows 0 and 2 here. Rows: 0 only subnormals; 1
+    normal values with every 5th input subnormal; 2 zeros and a few
+    subnormals; 3 normal."""
+    p, x = _linear_case(256, 384, ((4, 1.0),), 4, seed=21)
+    rng = np.random.default_rng(22)
+    sub = (rng.integers(-1023, 1024, size=(4, 256)) * 2.0 ** -24).astype(np.float16)
+    x[0] = sub[0]
+    x[1, ::5] = sub[1, ::5]
+    x[2] = 0
+    x[2, ::17] = sub[2, ::17]
+    assert np.all(np.abs(x[0][x[0] != 0]) < 2.0 ** -14)
+    dp = exl3.DeviceProj(p, DEV)
+    ref = olinear.linear(x, p, "R")
+    got = linear(torch.from_numpy(x).to(DEV), dp, torch.float32).cpu().double().numpy()
+    _check_range_rows(got, ref, [])
+    assert np.any(got[0]) and np.any(got[2])
+
+
 def test_moe_bf16_out_of_fp16_range():
     """The same rows through the routed-experts layer (16-row tiles). Row 1
     overflows at R2; rows 3 and 4 overflow at R3 instead: SwiGLU multiplies

@@ -312,6 +312,7 @@ __device__ __forceinline__ void fwht128_group16(float (&v)[8]) {
 }
 
 constexpr double kRsqrt128d = 0.088388347648318440550;  // 1/sqrt(128), fp64
+constexpr uint32_t kNegZeroBits = 0x80000000u;          // fp32 -0
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);  // RNE
@@ -320,22 +321,64 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
 }
 
-// fp64 -> fp16, rounded to nearest even, without branches: round to odd
-// into fp32 first (truncate towards zero, then set the last bit if anything
-// was dropped), then round that to fp16. Rounding to odd at 24 bits and then
-// to nearest at 11 gives the correctly rounded result (Boldo and Melquiond,
-// "Emulation of FMA and correctly rounded sums: proved algorithms using
-// rounding to odd", 2008: the intermediate precision exceeds the final one by
-// at least two bits). A NaN stays a NaN.
-__device__ __forceinline__ uint16_t f64_to_f16_bits(double d) {
-  const float f = (float)d;  // nearest even
-  const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  const double back = (double)f;
-  const bool inexact = back != d && d == d;
-  const uint32_t t = u - ((fabs(back) > fabs(d)) ? 1u : 0u);  // towards zero
-  const uint32_t r = inexact ? (t | 1u) : u;
-  return __builtin_bit_cast(uint16_t, (_Float16)__builtin_bit_cast(float, r));
+// fp64 -> fp32 rounded to odd: the 29 low mantissa bits an fp32 drops are
+// cleared, and the lowest kept bit is set when any of them was set (their
+// sum with 0x1FFFFFFF carries into bit 29 exactly then). The fp32 conversion
+// of the result is exact, so it is the truncated value with its last bit
+// forced to 1 when anything was dropped. This holds for |d| in the fp32
+// normal range; below it the result is a subnormal fp32 or zero, which fp16
+// rounds to a signed zero either way, and above it both give an infinity.
+// Inf and NaN pass through (a NaN keeps a nonzero mantissa).
+__device__ __forceinline__ float f64_to_f32_odd(double d) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, d);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  const uint32_t sticky = ((lo & 0x1FFFFFFFu) + 0x1FFFFFFFu) & 0x20000000u;
+  const uint32_t lo2 = (lo & 0xE0000000u) | sticky;
+  return (float)__builtin_bit_cast(double, ((uint64_t)hi << 32) | lo2);
 }
+
+// Two fp64 values -> two fp16 (a in the low half), each rounded to nearest
+// even: round to odd into fp32 first, then to nearest at 11 bits. Rounding
+// to odd at 24 bits and then to nearest at 11 gives the correctly rounded
+// result (Boldo and Melquiond, "Emulation of FMA and correctly rounded sums:
+// proved algorithms using rounding to odd", 2008: the intermediate precision
+// exceeds the final one by at least two bits). The last step is one packed
+// conversion.
+__device__ __forceinline__ uint32_t f64x2_to_f16x2_bits(double a, double b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 f = {f64_to_f32_odd(a), f64_to_f32_odd(b)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+
+// x * s exactly (x an fp32, s the low or, with HI, the high fp16 half of a
+// dword) as one mixed-precision FMA: the fp16 operand is widened exactly,
+// the product of an fp16 and an fp16- or bf16-valued fp32 fits in 24 bits,
+// and the addend -0 (negz holds its bits) leaves every product, a zero's
+// sign included, unchanged.
+// x * s exactly for two fp16 operands taken from the same half (HI) of the
+// dwords x2 and s2: the same FMA with both operands widened in the unit.
+template <bool HI>
+__device__ __forceinline__ float mul_f16_by_f16(uint32_t x2, uint32_t s2, uint32_t negz) {
+  float r;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,1,0] op_sel_hi:[1,1,0]"
+        : "=v"(r) : "v"(x2), "v"(s2), "s"(negz));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,1,0]" : "=v"(r) : "v"(x2), "v"(s2), "s"(negz));
+  return r;
+}
+
+template <bool HI>
+__device__ __forceinline__ float mul_f32_by_f16(float x, uint32_t s2, uint32_t negz) {
+  float r;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+        : "=v"(r) : "v"(x), "v"(s2), "s"(negz));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(s2), "s"(negz));
+  return r;
+}
+
 // bfloat16 = the upper 16 bits of an fp32, rounded to nearest even (add
 // 0x7FFF plus the lowest kept bit, then truncate); a NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {

@@ -52,18 +52,21 @@ __device__ __forceinline__ void rotate_block_t(const RotParams &p, int item, int
     u32x4 sv[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) sv[c] = sp[c];
-    // halves are unpacked with shifts: this compiler mis-compiles a bit_cast
-    // of a vector element taken inside an unrolled loop (it reuses element 0)
+    // x stays packed: each product widens its two fp16 (or bf16) operands
+    // itself, which keeps 32 widened copies of x out of the registers
     double v[32];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const uint32_t xw = xv[j >> 2][j & 3], sw = sv[j >> 2][j & 3];
-      const float x0 = BF16 ? bf16_bits_to_f32((uint16_t)(xw & 0xFFFFu))
-                            : f16_bits_to_f32((uint16_t)(xw & 0xFFFFu));
-      const float x1 = BF16 ? bf16_bits_to_f32((uint16_t)(xw >> 16))
-                            : f16_bits_to_f32((uint16_t)(xw >> 16));
-      v[2 * j] = (double)(x0 * f16_bits_to_f32((uint16_t)(sw & 0xFFFFu)));
-      v[2 * j + 1] = (double)(x1 * f16_bits_to_f32((uint16_t)(sw >> 16)));
+      if constexpr (BF16) {
+        v[2 * j] = (double)mul_f32_by_f16<false>(__builtin_bit_cast(float, xw << 16), sw,
+                                                  kNegZeroBits);
+        v[2 * j + 1] = (double)mul_f32_by_f16<true>(
+            __builtin_bit_cast(float, xw & 0xFFFF0000u), sw, kNegZeroBits);
+      } else {
+        v[2 * j] = (double)mul_f16_by_f16<false>(xw, sw, kNegZeroBits);
+        v[2 * j + 1] = (double)mul_f16_by_f16<true>(xw, sw, kNegZeroBits);
+      }
     }
 #pragma unroll
     for (int d = 1; d < 32; d <<= 1) {
@@ -82,15 +85,14 @@ __device__ __forceinline__ void rotate_block_t(const RotParams &p, int item, int
     for (int j = 0; j < 32; ++j) v[j] = fma(v[j], s1, quad_xor<1>(v[j]));
 #pragma unroll
     for (int j = 0; j < 32; ++j) v[j] = fma(v[j], s2, quad_xor<2>(v[j]));
-    uint16_t h[32];
-#pragma unroll
-    for (int j = 0; j < 32; ++j) h[j] = f64_to_f16_bits(v[j] * kRsqrt128d);
     u32x4 *op = (u32x4 *)(p.xt + ((int64_t)item * p.nproj + pj) * p.H + col);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {  // 8 entries: slots {0,4,1,5,2,6,3,7}
-      const uint16_t *q = h + 8 * g;
-      op[g] = (u32x4){(uint32_t)q[0] | ((uint32_t)q[4] << 16), (uint32_t)q[1] | ((uint32_t)q[5] << 16),
-                      (uint32_t)q[2] | ((uint32_t)q[6] << 16), (uint32_t)q[3] | ((uint32_t)q[7] << 16)};
+      const double *q = v + 8 * g;
+      op[g] = (u32x4){f64x2_to_f16x2_bits(q[0] * kRsqrt128d, q[4] * kRsqrt128d),
+                      f64x2_to_f16x2_bits(q[1] * kRsqrt128d, q[5] * kRsqrt128d),
+                      f64x2_to_f16x2_bits(q[2] * kRsqrt128d, q[6] * kRsqrt128d),
+                      f64x2_to_f16x2_bits(q[3] * kRsqrt128d, q[7] * kRsqrt128d)};
     }
   }
 }
@@ -122,8 +124,8 @@ __device__ __forceinline__ void rotate_block16_t(const RotParams &p, int item, i
                             : f16_bits_to_f32((uint16_t)(xw & 0xFFFFu));
       const float x1 = BF16 ? bf16_bits_to_f32((uint16_t)(xw >> 16))
                             : f16_bits_to_f32((uint16_t)(xw >> 16));
-      v[2 * j] = (double)(x0 * f16_bits_to_f32((uint16_t)(sw & 0xFFFFu)));
-      v[2 * j + 1] = (double)(x1 * f16_bits_to_f32((uint16_t)(sw >> 16)));
+      v[2 * j] = (double)mul_f32_by_f16<false>(x0, sw, kNegZeroBits);
+      v[2 * j + 1] = (double)mul_f32_by_f16<true>(x1, sw, kNegZeroBits);
     }
 #pragma unroll
     for (int d = 1; d < 8; d <<= 1) {
@@ -142,12 +144,11 @@ __device__ __forceinline__ void rotate_block16_t(const RotParams &p, int item, i
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = fma(v[j], s, __shfl_xor(v[j], d, 64));
     }
-    uint16_t h[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) h[j] = f64_to_f16_bits(v[j] * kRsqrt128d);
     *(u32x4 *)(p.xt + ((int64_t)item * p.nproj + pj) * p.H + col) =
-        (u32x4){(uint32_t)h[0] | ((uint32_t)h[4] << 16), (uint32_t)h[1] | ((uint32_t)h[5] << 16),
-                (uint32_t)h[2] | ((uint32_t)h[6] << 16), (uint32_t)h[3] | ((uint32_t)h[7] << 16)};
+        (u32x4){f64x2_to_f16x2_bits(v[0] * kRsqrt128d, v[4] * kRsqrt128d),
+                f64x2_to_f16x2_bits(v[1] * kRsqrt128d, v[5] * kRsqrt128d),
+                f64x2_to_f16x2_bits(v[2] * kRsqrt128d, v[6] * kRsqrt128d),
+                f64x2_to_f16x2_bits(v[3] * kRsqrt128d, v[7] * kRsqrt128d)};
   }
 }
 
