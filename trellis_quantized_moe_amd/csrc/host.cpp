@@ -242,19 +242,16 @@ int32_t run_experts(const uint16_t *x, int32_t x_dtype, int32_t rows, int32_t to
   const bool wide = L.wide;
   const int bm = wide ? kBMWide : kBM;
   // Launch units of L.group passes (see MoeLayout): u covers packed
-  // positions [u * gcap, (u + 1) * gcap), with spans still cut every cap.
+  // positions [u * gcap, (u + 1) * gcap), planned as one range.
   auto npos_of = [&](int u) {
     return (int)std::min<int64_t>(L.gcap, P - (int64_t)u * L.gcap);
   };
   auto tiles_of = [&](int u) {  // bound on the unit's plan tiles
-    int t = 0;
-    for (int j = 0; j < L.group; ++j) {
-      const int64_t pass = (int64_t)u * L.group + j;
-      if (pass >= L.passes) break;
-      const int np = (int)std::min<int64_t>(L.cap, P - pass * L.cap);
-      t += std::min(E, np) + (np + bm - 1) / bm;
-    }
-    return t;
+    // the unit's positions are planned as one range: full tiles, plus at
+    // most one partial tile per expert present
+    const int64_t first = (int64_t)u * L.group * L.cap;
+    const int np = (int)std::min<int64_t>((int64_t)L.group * L.cap, P - first);
+    return std::min(E, np) + (np + bm - 1) / bm;
   };
   auto plan_of = [&](int u) {
     return at<int32_t>(ws, L.plan) + (size_t)u * (1 + 3 * (size_t)L.group * L.slots);

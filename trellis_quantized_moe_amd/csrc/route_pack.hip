@@ -108,24 +108,20 @@ __device__ __forceinline__ uint64_t match_key(int key, uint64_t live, int nb) {
 
 constexpr int kPackBatch = 8;  // rounds whose loads are issued together
 
-// a4 for one pass, by one wave: the row tiles of every expert's sub-span
-// inside the pass; only the experts overlapping the pass are visited.
+// a4 for one position range [pb, pe) (a pass, or a launch unit of several
+// passes), by one wave: the row tiles of every expert's sub-span inside the
+// range; only the experts overlapping the range are visited.
 // Order: full tiles (bm rows) first, in expert order, then the partial
 // tiles (at most one per expert: the end of its span); for 128-row tiles
-// and at most 128 experts in the pass those go by rows descending, ties in
+// and at most 128 experts in the range those go by rows descending, ties in
 // expert order, otherwise in expert order. Heavy tiles so come first in
 // dispatch order, where each gets a CU of its own before the light ones
 // fill the second slots; the order never changes a result. s_off: the
 // expert offsets (E + 1, nondecreasing), kept = s_off[E].
-// Tiles of one pass, appended to `plan` at tile index `base`, their first
-// rows offset by `roff` (the pass's place in its launch unit). Returns the
-// pass's tile count; the caller writes the unit's count.
-// With WRITE false only the count is computed (no stores, no sort).
-template <bool WRITE = true>
-__device__ int plan_one_pass(const PackParams &p, const int *s_off, int E, int kept, int pass,
-                             int lane, int32_t *plan, int base, int roff) {
-  const int pb = pass * p.capacity;
-  const int pe = (int)min((int64_t)pb + p.capacity, (int64_t)kept);
+// Tiles of the range go to `plan` (after its count word), their first rows
+// relative to pb. Returns the range's tile count; the caller writes it.
+__device__ int plan_range(const PackParams &p, const int *s_off, int E, int pb, int pe, int lane,
+                          int32_t *plan) {
   int total = 0;
   if (pb < pe) {
     const int e_lo = expert_at(s_off, E, pb), e_hi = expert_at(s_off, E, pe - 1);
@@ -147,11 +143,11 @@ __device__ int plan_one_pass(const PackParams &p, const int *s_off, int E, int k
         const int y = __shfl_up(x, d, 64);
         if (lane >= d) x += y;
       }
-      const int slot0 = base + total + x - nf;
-      for (int t = 0; WRITE && t < nf; ++t) {
+      const int slot0 = total + x - nf;
+      for (int t = 0; t < nf; ++t) {
         int32_t *d = plan + 1 + 3 * (slot0 + t);
         d[0] = e;
-        d[1] = roff + lo - pb + t * bm;
+        d[1] = lo - pb + t * bm;
         d[2] = bm;
       }
       total += __shfl(x, 63, 64);
@@ -175,7 +171,7 @@ __device__ int plan_one_pass(const PackParams &p, const int *s_off, int E, int k
       const int rows = (c < 2) ? prow[c & 1] : (hi > lo ? (hi - lo) % bm : 0);
       const uint64_t has = __ballot(rows > 0);
       int rank = npart + __popcll(has & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-      if (WRITE && sort) {  // rows descending, then expert order, over both chunks
+      if (sort) {  // rows descending, then expert order, over both chunks
         rank = 0;
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)
@@ -185,10 +181,10 @@ __device__ int plan_one_pass(const PackParams &p, const int *s_off, int E, int k
             rank += (r2 > rows || (r2 == rows && e2 < e)) ? 1 : 0;
           }
       }
-      if (WRITE && rows > 0) {
-        int32_t *d = plan + 1 + 3 * (base + nfull + rank);
+      if (rows > 0) {
+        int32_t *d = plan + 1 + 3 * (nfull + rank);
         d[0] = e;
-        d[1] = roff + lo - pb + (hi - lo) / bm * bm;
+        d[1] = lo - pb + (hi - lo) / bm * bm;
         d[2] = rows;
       }
       npart += __popcll(has);
@@ -198,41 +194,21 @@ __device__ int plan_one_pass(const PackParams &p, const int *s_off, int E, int k
   return total;
 }
 
-// Plans of every launch unit of p.group > 1 passes when the passes' tile
-// counts fit `cnt` (ncnt ints of LDS, free): every wave first counts the
-// tiles of its passes, then writes them after the earlier passes of their
-// unit, so all waves plan in parallel. Same plan as plan_units.
-__device__ void plan_units_parallel(const PackParams &p, const int *s_off, int E, int kept,
-                                    int w, int nw, int lane, int *cnt) {
-  const int G = p.group;
-  for (int pass = w; pass < p.passes; pass += nw) {
-    const int n = plan_one_pass<false>(p, s_off, E, kept, pass, lane, nullptr, 0, 0);
-    if (lane == 0) cnt[pass] = n;
-  }
-  __syncthreads();
-  for (int pass = w; pass < p.passes; pass += nw) {
-    const int u = pass / G, j = pass - u * G;
-    int32_t *plan = p.plan + (int64_t)u * (1 + 3 * (int64_t)G * p.slots);
-    int base = 0, n = 0;
-    for (int j2 = 0; j2 < G && u * G + j2 < p.passes; ++j2) {
-      base += (j2 < j) ? cnt[u * G + j2] : 0;
-      n += cnt[u * G + j2];
-    }
-    plan_one_pass(p, s_off, E, kept, pass, lane, plan, base, j * p.capacity);
-    if (j == 0 && lane == 0) plan[0] = n;
-  }
-}
-
 // Plans of every launch unit (p.group consecutive passes), one wave per unit.
+// A unit's passes are consecutive position ranges, and every pass but the
+// last holds exactly `capacity` positions, so the unit's rows are one
+// contiguous range of its buffers: its tiles are planned over the whole
+// range, and an expert span that a pass boundary cuts inside the unit still
+// gives one run of tiles (each row's result does not depend on its tile).
 __device__ void plan_units(const PackParams &p, const int *s_off, int E, int kept, int w,
                            int nw, int lane) {
   const int G = max(p.group, 1);
   const int units = (p.passes + G - 1) / G;
   for (int u = w; u < units; u += nw) {
     int32_t *plan = p.plan + (int64_t)u * (1 + 3 * (int64_t)G * p.slots);
-    int n = 0;
-    for (int j = 0; j < G && u * G + j < p.passes; ++j)
-      n += plan_one_pass(p, s_off, E, kept, u * G + j, lane, plan, n, j * p.capacity);
+    const int64_t ub = (int64_t)u * G * p.capacity;
+    const int ue = (int)min(ub + (int64_t)G * p.capacity, (int64_t)kept);
+    const int n = plan_range(p, s_off, E, (int)ub, ue, lane, plan);
     if (lane == 0) plan[0] = n;
   }
 }
@@ -339,10 +315,8 @@ __device__ __forceinline__ void zero_unrouted_rows(const PackParams &p, int r0, 
 }
 
 // a4 and the clears of the call: the plan of every launch unit, ctrl[1..2]
-// and the completion counts. One workgroup of kPackThreads; s_wc is free
-// LDS for the parallel planner.
-__device__ __forceinline__ void plan_and_clear(const PackParams &p, const int *s_off, int *s_wc,
-                                               int tid) {
+// and the completion counts. One workgroup of kPackThreads.
+__device__ __forceinline__ void plan_and_clear(const PackParams &p, const int *s_off, int tid) {
   const int E = p.E, w = tid >> 6, lane = tid & 63;
   if (tid == 0 && p.ctrl) {
     p.ctrl[1] = 0;  // bad stage entries
@@ -350,12 +324,7 @@ __device__ __forceinline__ void plan_and_clear(const PackParams &p, const int *s
   }
   for (int i = tid; i < p.nzero; i += kPackThreads) p.zero[i] = 0;
   const int kept = s_off[E];
-  if (p.group > 1 && p.passes <= kPackWaves * kMaxE) {
-    __syncthreads();  // s_wc is free
-    plan_units_parallel(p, s_off, E, kept, w, kPackWaves, lane, s_wc);
-  } else {
-    plan_units(p, s_off, E, kept, w, kPackWaves, lane);
-  }
+  plan_units(p, s_off, E, kept, w, kPackWaves, lane);
 }
 
 __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
@@ -436,7 +405,7 @@ __global__ void __launch_bounds__(kPackThreads) pack_plan_kernel(PackParams p) {
   }
 
   if (!p.do_plan) return;
-  plan_and_clear(p, s_off, &s_wc[0][0], tid);
+  plan_and_clear(p, s_off, tid);
 
   // rows whose pairs were all dropped produce zeros (rare). A pack that
   // dropped nothing has no such row.
@@ -536,7 +505,7 @@ __global__ void __launch_bounds__(kPackThreads) pack_scatter_kernel(PackParams p
   for (int e = tid; e <= E; e += kPackThreads) s_off[e] = p.offset[e];
   if (b == p.nblk) {  // the planner
     __syncthreads();
-    if (p.do_plan) plan_and_clear(p, s_off, &s_wc[0][0], tid);
+    if (p.do_plan) plan_and_clear(p, s_off, tid);
     return;
   }
   int *wc = s_wc[w];
