@@ -42,16 +42,18 @@ __device__ __forceinline__ void rotate_block_t(const RotParams &p, int item, int
                                                int e, int i) {
   const int64_t col = blk * 128 + 32 * i;
   const u32x4 *xp = (const u32x4 *)(p.x + (int64_t)row * p.H + col);
-  u32x4 xv[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) xv[c] = xp[c];
   const bool upper1 = (i & 1) != 0, upper2 = (i & 2) != 0;
 #pragma unroll 1
   for (int pj = 0; pj < p.nproj; ++pj) {
+    // x is loaded again for the second projection (from the cache): not
+    // keeping it live across the butterflies leaves room for 4 waves/SIMD
     const u32x4 *sp = (const u32x4 *)(p.suh[pj] + (int64_t)e * p.H + col);
-    u32x4 sv[4];
+    u32x4 xv[4], sv[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sv[c] = sp[c];
+    for (int c = 0; c < 4; ++c) {
+      xv[c] = xp[c];
+      sv[c] = sp[c];
+    }
     // x stays packed: each product widens its two fp16 (or bf16) operands
     // itself, which keeps 32 widened copies of x out of the registers
     double v[32];
