@@ -280,11 +280,12 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t x_dtype, int32_t rows, int3
  *   expert_of_pos int32[P]
  *   Passes are grouped into launch units of G = plan_group passes when the
  *   call runs several passes on 128-row tiles (rows * topk >= 64 *
- *   num_experts): G = 4 from 8 passes, 2 from 4 passes, else 1. A unit
- *   covers packed positions [u G C, (u + 1) G C); spans are still cut every
- *   C positions. The scratch for such calls is therefore 2 G C rows of xt,
- *   at and d (about 1 GB for 3072 rows x top-8, hidden 6144, intermediate
- *   2048 at C = 2048).
+ *   num_experts): G = min(8, ceil(passes / 2)), else 1. A unit covers
+ *   packed positions [u G C, (u + 1) G C) and is planned as one range, so
+ *   an expert span that a pass boundary cuts inside a unit is tiled as one
+ *   run. The scratch for such calls is therefore 2 G C rows of xt, at and d
+ *   (1.38 GB in all for 3072 rows x top-8, hidden 6144, intermediate 2048
+ *   at C = 2048, where G = 6).
  *   plan        per unit: int32 ntiles + tiles of {expert, start, len}
  *               (start relative to the unit; slots: G * plan_slots)
  *   xt          fp16 [G C][2][hidden]  rotated gate/up inputs of the unit
