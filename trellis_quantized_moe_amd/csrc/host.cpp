@@ -117,7 +117,7 @@ struct MoeLayout {
   int passes, slots, cap, ncnt_ints;
   // A launch unit is `group` consecutive passes (on the pipelined path
   // about half the passes, at most 8; else 1): one plan, one buffer set of
-  // gcap = group * cap rows. Spans are still cut every `cap` pairs.
+  // gcap = group * cap rows, planned as one position range.
   int group, units, gcap;
   // fused: a single pass on 16-row tiles runs its GEMMs and combine in one
   // launch (experts_narrow_kernel), with separate sums and counts for the
