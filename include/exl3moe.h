@@ -276,7 +276,8 @@ int32_t exl3_moe_additive(const uint16_t *x, int32_t x_dtype, int32_t rows, int3
  *               A caller reads them after the call's stream work completes;
  *               the library itself never waits for them.
  *   meta        forward only: count[E], offset[E+1], pair_of_pos[P],
- *               weight_of_pos[P], pos_of_pair[P], num_active[1] (P = pairs)
+ *               weight_of_pos[P], pos_of_pair[P], num_active[1] (P = pairs;
+ *               each array starts 256-byte aligned)
  *   expert_of_pos int32[P]
  *   Passes are grouped into launch units of G = plan_group passes when the
  *   call runs several passes on 128-row tiles (rows * topk >= 64 *

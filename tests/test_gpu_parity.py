@@ -506,6 +506,53 @@ def test_moe_wide_grouped_passes_additive_equals_forward(cap, group):
     assert torch.equal(add.view(torch.int32), one.view(torch.int32))
 
 
+@pytest.mark.parametrize("E,rows,cap", [(4, 300, 100), (4, 300, 7), (16, 1024, 100)])
+def test_unit_plan_tiles_each_span_once(E, rows, cap):
+    """The plan of every launch unit, read back from the workspace, tiles the
+    unit's packed positions exactly once: tiles are disjoint and cover
+    [unit start, unit end); each lies inside its expert's span; all are 128
+    rows but the last of an expert's run inside the unit, so a span that a
+    pass boundary cuts inside the unit is still one run; the count stays
+    within the launch bound min(E, positions) + positions / 128."""
+    wl = synth.moe_workload("tiny", rows=rows, topk=2, E=E, H=256, I=384, K=(3, 5, 8))
+    P = rows * wl.topk
+    assert P >= 64 * E
+    lay = exl3.moe_layout(rows, wl.topk, E, wl.hidden, wl.intermediate, cap)
+    G, C = lay.plan_group, min(cap, P)
+    assert G > 1, lay.plan_group
+    gate, up, down, x, ids, w = _moe_inputs(wl)
+    ws = torch.empty(lay.total, dtype=torch.uint8, device=DEV)
+    moe_forward(x, ids, w, gate, up, down, cap, torch.float32, ws=ws)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    o0 = lay.meta + (4 * E + 255) // 256 * 256  # offset[E + 1] follows count[E], 256-B aligned
+    offset = raw[o0:o0 + 4 * (E + 1)].view(np.int32)
+    kept = int(offset[E])
+    assert kept == P
+    units = (lay.passes + G - 1) // G
+    per_unit = 1 + 3 * G * lay.plan_slots
+    plan = raw[lay.plan:lay.plan + 4 * units * per_unit].view(np.int32).reshape(units, per_unit)
+    for u in range(units):
+        ub, ue = u * G * C, min((u + 1) * G * C, kept)
+        n = int(plan[u, 0])
+        t = plan[u, 1:1 + 3 * n].reshape(n, 3)
+        assert n <= min(E, ue - ub) + -(-(ue - ub) // 128), (u, n)
+        order = np.argsort(t[:, 1], kind="stable")
+        starts, lens = t[order, 1], t[order, 2]
+        assert starts[0] == 0 and np.all(lens > 0) and np.all(lens <= 128), u
+        assert np.array_equal(starts[1:], (starts + lens)[:-1]), u  # disjoint, no gaps
+        assert starts[-1] + lens[-1] == ue - ub, u
+        for e, st, ln in t[order]:
+            lo, hi = ub + st, ub + st + ln
+            assert offset[e] <= lo and hi <= offset[e + 1], (u, e, st, ln)
+        for e in np.unique(t[:, 0]):
+            et = t[t[:, 0] == e]
+            et = et[np.argsort(et[:, 1])]
+            assert np.all(et[:-1, 2] == 128), (u, e)  # one run: only the last is partial
+            lo, hi = max(offset[e], ub), min(offset[e + 1], ue)
+            assert et[0, 1] == lo - ub and et[-1, 1] + et[-1, 2] == hi - ub, (u, e)
+
+
 def test_linear_wide_multistage_parity():
     # 1024 rows x 8192 out selects 128-row tiles; three stages, one zero
     p, x = _linear_case(256, 8192, ((3, 1.0), (2, 0.25), (4, 0.0)), 1024, seed=9)
