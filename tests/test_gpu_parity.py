@@ -506,14 +506,18 @@ def test_moe_wide_grouped_passes_additive_equals_forward(cap, group):
     assert torch.equal(add.view(torch.int32), one.view(torch.int32))
 
 
-@pytest.mark.parametrize("E,rows,cap", [(4, 300, 100), (4, 300, 7), (16, 1024, 100)])
+@pytest.mark.parametrize("E,rows,cap", [(4, 300, 100), (4, 300, 7), (16, 1024, 100),
+                                        (300, 9600, 2400)])
 def test_unit_plan_tiles_each_span_once(E, rows, cap):
     """The plan of every launch unit, read back from the workspace, tiles the
     unit's packed positions exactly once: tiles are disjoint and cover
     [unit start, unit end); each lies inside its expert's span; all are 128
     rows but the last of an expert's run inside the unit, so a span that a
     pass boundary cuts inside the unit is still one run; the count stays
-    within the launch bound min(E, positions) + positions / 128."""
+    within the launch bound min(E, positions) + positions / 128. With 300
+    experts a unit spans more than 128 of them (the planner's unsorted
+    order for partial tiles). The output equals the one-pass output bit for
+    bit."""
     wl = synth.moe_workload("tiny", rows=rows, topk=2, E=E, H=256, I=384, K=(3, 5, 8))
     P = rows * wl.topk
     assert P >= 64 * E
@@ -522,8 +526,10 @@ def test_unit_plan_tiles_each_span_once(E, rows, cap):
     assert G > 1, lay.plan_group
     gate, up, down, x, ids, w = _moe_inputs(wl)
     ws = torch.empty(lay.total, dtype=torch.uint8, device=DEV)
-    moe_forward(x, ids, w, gate, up, down, cap, torch.float32, ws=ws)
+    y = moe_forward(x, ids, w, gate, up, down, cap, torch.float32, ws=ws)
+    one = moe_forward(x, ids, w, gate, up, down, 10 ** 6, torch.float32)
     torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), one.view(torch.int32))
     raw = ws.cpu().numpy()
     o0 = lay.meta + (4 * E + 255) // 256 * 256  # offset[E + 1] follows count[E], 256-B aligned
     offset = raw[o0:o0 + 4 * (E + 1)].view(np.int32)
